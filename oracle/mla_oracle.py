@@ -1,0 +1,284 @@
+"""CPU oracle for weight-absorbed Multi-head Latent Attention (MLA) decode.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this module: only
+the tests, the smoke check and the benchmark's CPU-baseline leg use it.  It shares
+no code with the HIP library (no kernels, headers, helpers or tables); it reads the
+same stored input bytes and decodes them itself.
+
+Everything is float64 numpy.  Each function follows one passage of the source pages,
+named by page title and section:
+
+* "Operator Notes (1): MLA — Multi-head Latent Attention at the Operator Level"
+  (section 2, the operator pseudocode and shapes; sections 1 and 3, cache sizes);
+* "multi-head latent attention" glossary entry (the paragraph on the decoupled RoPE
+  key, which also states that the up-projections can be absorbed into the query
+  and output projections);
+* "Multi-Head Latent Attention and the compression of the KV cache" dispatch (the
+  paragraph on mathematical equivalence through associativity).
+
+Readings of points the pages leave open (stated once here, used throughout):
+
+* Softmax scale: the caller passes it; the workloads use 1/sqrt(d_h + d_r), the width
+  of the concatenated [content | RoPE] key, for the whole dot product.
+* Weight layout: ``w_uk[h, j, c]`` and ``w_uv[h, c, j]`` hold the page's
+  ``W_UK[c, h*d_h + j]`` and ``W_UV[c, h*d_h + j]`` (a pure permutation;
+  ``to_page_layout`` converts).
+* The RoPE key ``k_rope[t, :]`` is one d_r-wide vector per token shared by all heads;
+  ``q_rope`` is per head.  Both arrive already rotated.
+* ``seq_lens[b]`` counts cache rows including the s_q new tokens; query i of a
+  sequence of length L sees rows t <= L - s_q + i (causal among the new tokens).
+* A query row that sees no key returns zeros and lse = -inf.
+
+Parity pins for every function live in tests/test_oracle.py.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# ---------------------------------------------------------------------------------
+# Stored-number decoding (from the formats' definitions, not from any library)
+# ---------------------------------------------------------------------------------
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 is the upper 16 bits of an IEEE-754 binary32; decoding is exact."""
+    b32 = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16))
+    with np.errstate(invalid="ignore"):  # signalling-NaN patterns stay NaN
+        return b32.view(np.float32).astype(np.float64)
+
+
+def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
+    """OCP 8-bit float E4M3 ("fn": finite, no infinities).
+
+    Bit layout S EEEE MMM, exponent bias 7.  Exponent field 0 encodes subnormals
+    (M/8) * 2^-6; other fields encode (1 + M/8) * 2^(E-7).  The two codes with
+    E = 15 and M = 7 are NaN; every other code is finite (largest 448).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    subnormal = (m / 8.0) * np.exp2(-6.0)
+    val = sign * np.where(e == 0, subnormal, normal)
+    return np.where((e == 15) & (c & 0x7 == 7), np.nan, val)
+
+
+def decode(arr: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return decode_bf16(arr)
+    if dtype == "fp8":
+        return decode_e4m3fn(arr)
+    raise ValueError(dtype)
+
+
+def dequantize_cache(codes: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """fp8 latent with one float32 scale per token: value = e4m3(code) * scale[token]."""
+    return decode_e4m3fn(codes) * np.asarray(scale, np.float64)[..., None]
+
+
+# ---------------------------------------------------------------------------------
+# Cache arithmetic ("Operator Notes (1): MLA", sections 1 and 3)
+# ---------------------------------------------------------------------------------
+
+
+def mha_cache_numbers_per_token(n_heads: int, d_head: int) -> int:
+    """Full K and V for every head are cached: two n_h*d_h-wide vectors per token."""
+    return 2 * n_heads * d_head
+
+
+def mla_cache_numbers_per_token(d_latent: int, d_rope: int = 0) -> int:
+    """Only the latent (plus, with decoupled RoPE, the shared rotary key) is cached."""
+    return d_latent + d_rope
+
+
+# ---------------------------------------------------------------------------------
+# Weight layouts
+# ---------------------------------------------------------------------------------
+
+
+def to_page_layout(w_uk: np.ndarray, w_uv: np.ndarray):
+    """Per-head stored weights -> the page's [d_c, n_h*d_h] matrices.
+
+    ``W_UK_page[c, h*d_h + j] = w_uk[h, j, c]`` and ``W_UV_page[c, h*d_h + j] = w_uv[h, c, j]``
+    ("Operator Notes (1): MLA", section 2: both up-projections map the d_c-wide latent
+    to all heads' keys / values at once).
+    """
+    n_h, d_h, d_c = w_uk.shape
+    uk = np.transpose(w_uk, (2, 0, 1)).reshape(d_c, n_h * d_h)
+    uv = np.transpose(w_uv, (1, 0, 2)).reshape(d_c, n_h * d_h)
+    return uk, uv
+
+
+# ---------------------------------------------------------------------------------
+# Masking (causal among the s_q new tokens)
+# ---------------------------------------------------------------------------------
+
+
+def visible_keys(seq_len: int, q_len: int, i: int) -> int:
+    """Number of cache rows query i sees: rows 0 .. L - s_q + i (clamped to [0, L])."""
+    return int(min(max(seq_len - q_len + i + 1, 0), seq_len))
+
+
+def _softmax_rows(s: np.ndarray, n_vis: np.ndarray):
+    """Row softmax of scores s[r, t] over the first n_vis[r] columns.
+
+    Returns (p, lse): p is zero outside the visible prefix, lse = log sum_t exp(s).
+    A row with nothing visible gets p = 0 and lse = -inf.
+    """
+    R, L = s.shape
+    vis = np.arange(L)[None, :] < n_vis[:, None]
+    s = np.where(vis, s, -np.inf)
+    m = np.max(s, axis=1, initial=-np.inf)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    e = np.where(vis, np.exp(s - m_safe[:, None]), 0.0)
+    denom = e.sum(axis=1)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        p = np.where(denom[:, None] > 0, e / denom[:, None], 0.0)
+        lse = np.where(denom > 0, m_safe + np.log(denom), -np.inf)
+    return p, lse
+
+
+# ---------------------------------------------------------------------------------
+# Explicit form: decompress K and V from the latent, then attend.
+# ("Operator Notes (1): MLA", section 2; plus the decoupled RoPE key of the glossary
+# entry's paragraph on rotary position.)  This is the authority.
+# ---------------------------------------------------------------------------------
+
+
+def mla_explicit(q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, seq_lens, scale, rows=None):
+    """Decompress-then-attend MLA decode.
+
+    q_nope [B,s_q,n_h,d_h], q_rope [B,s_q,n_h,d_r], c_kv [B,T,d_c], k_rope [B,T,d_r],
+    w_uk [n_h,d_h,d_c], w_uv [n_h,d_c,d_h] (float64).  ``rows`` optionally restricts
+    the work to a list of (b, i, h) triples.
+
+    Per head h: K_h = c_kv W_UK (the head's d_h columns), V_h = c_kv W_UV (likewise);
+    the score of token t is scale * (q_nope . K_h[t] + q_rope . k_rope[t]); softmax over
+    the visible tokens; the output is the probability-weighted sum of V_h rows.
+    Returns out[B,s_q,n_h,d_h] (NaN where not computed) and lse[B,s_q,n_h].
+    """
+    B, sq, n_h, d_h = q_nope.shape
+    uk_page, uv_page = to_page_layout(w_uk, w_uv)
+    out = np.full((B, sq, n_h, d_h), np.nan)
+    lse = np.full((B, sq, n_h), np.nan)
+    if rows is None:
+        rows = [(b, i, h) for b in range(B) for i in range(sq) for h in range(n_h)]
+    by_bh = {}
+    for (b, i, h) in rows:
+        by_bh.setdefault((b, h), []).append(i)
+    for (b, h), qs in sorted(by_bh.items()):
+        L = int(seq_lens[b])
+        cols = slice(h * d_h, (h + 1) * d_h)
+        K = c_kv[b, :L] @ uk_page[:, cols]              # [L, d_h]
+        V = c_kv[b, :L] @ uv_page[:, cols]              # [L, d_h]
+        for i in qs:
+            s = scale * (K @ q_nope[b, i, h] + k_rope[b, :L] @ q_rope[b, i, h])
+            p, l = _softmax_rows(s[None, :], np.array([visible_keys(L, sq, i)]))
+            out[b, i, h] = p[0] @ V
+            lse[b, i, h] = l[0]
+    return out, lse
+
+
+# ---------------------------------------------------------------------------------
+# Absorbed form (glossary entry, paragraph on the decoupled RoPE key: W_UK folds into
+# the query side and W_UV into the output side; the dispatch's associativity paragraph
+# states that this gives the same result).  Three stages, one per library call.
+# ---------------------------------------------------------------------------------
+
+
+def absorb_query(q_nope, w_uk):
+    """q_lat[b,i,h,c] = sum_j q_nope[b,i,h,j] * w_uk[h,j,c]: the query expressed against
+    the latent, so that q_nope . (c_kv W_UK_h)[t] = q_lat . c_kv[t]."""
+    B, sq, n_h, _ = q_nope.shape
+    q_lat = np.empty((B, sq, n_h, w_uk.shape[2]))
+    for h in range(n_h):
+        q_lat[:, :, h, :] = q_nope[:, :, h, :] @ w_uk[h]
+    return q_lat
+
+
+def latent_attention(q_lat, q_rope, c_kv, k_rope, seq_lens, scale):
+    """Attention of every head directly over the cached latent.
+
+    score[t] = scale * (q_lat . c_kv[t] + q_rope . k_rope[t]); softmax over visible t;
+    o_lat = sum_t p[t] * c_kv[t] (the latent is both key and value).
+    Returns o_lat [B,s_q,n_h,d_c] and lse [B,s_q,n_h] (natural log).
+    """
+    B, sq, n_h, d_c = q_lat.shape
+    o_lat = np.zeros((B, sq, n_h, d_c))
+    lse = np.full((B, sq, n_h), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        C = c_kv[b, :L]
+        R = k_rope[b, :L]
+        s = scale * (q_lat[b] @ C.T + q_rope[b] @ R.T)          # [s_q, n_h, L]
+        n_vis = np.repeat([visible_keys(L, sq, i) for i in range(sq)], n_h)
+        p, l = _softmax_rows(s.reshape(sq * n_h, L), n_vis)
+        o_lat[b] = (p @ C).reshape(sq, n_h, d_c)
+        lse[b] = l.reshape(sq, n_h)
+    return o_lat, lse
+
+
+def absorb_output(o_lat, w_uv):
+    """out[b,i,h,j] = sum_c o_lat[b,i,h,c] * w_uv[h,c,j]: the per-head value projection
+    applied once to the attended latent instead of to every cached token."""
+    B, sq, n_h, _ = o_lat.shape
+    out = np.empty((B, sq, n_h, w_uv.shape[2]))
+    for h in range(n_h):
+        out[:, :, h, :] = o_lat[:, :, h, :] @ w_uv[h]
+    return out
+
+
+def mla_absorbed(q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, seq_lens, scale):
+    """The whole absorbed decode. Returns dict(out, o_lat, lse, q_lat)."""
+    q_lat = absorb_query(q_nope, w_uk)
+    o_lat, lse = latent_attention(q_lat, q_rope, c_kv, k_rope, seq_lens, scale)
+    return {"q_lat": q_lat, "o_lat": o_lat, "lse": lse, "out": absorb_output(o_lat, w_uv)}
+
+
+# ---------------------------------------------------------------------------------
+# Splitting the token axis and merging (log-sum-exp combine)
+# ---------------------------------------------------------------------------------
+
+
+def merge_partials(o_parts, lse_parts):
+    """Merge attention results computed over disjoint token subsets.
+
+    o_parts [S, ..., d] are each subset's normalised outputs, lse_parts [S, ...] their
+    log-sum-exp.  Since exp(lse_s) is each subset's softmax denominator, the full output
+    is the exp(lse_s)-weighted mean of the o_s, and the full lse is log sum_s exp(lse_s).
+    Subsets with lse = -inf (nothing visible) carry zero weight.
+    """
+    o_parts = np.asarray(o_parts, np.float64)
+    lse_parts = np.asarray(lse_parts, np.float64)
+    M = np.max(lse_parts, axis=0)
+    M_safe = np.where(np.isfinite(M), M, 0.0)
+    w = np.where(np.isfinite(lse_parts), np.exp(lse_parts - M_safe), 0.0)
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        o = np.where(tot[..., None] > 0, np.einsum("s...,s...d->...d", w, o_parts) / tot[..., None], 0.0)
+        lse = np.where(tot > 0, M_safe + np.log(tot), -np.inf)
+    return o, lse
+
+
+# ---------------------------------------------------------------------------------
+# Paged cache: block-table lookup
+# ---------------------------------------------------------------------------------
+
+
+def gather_pages(pool, block_table, seq_lens, seq_len_max, fill=0.0):
+    """Rebuild contiguous per-sequence rows from a block pool.
+
+    Logical row t of sequence b lives in pool block ``block_table[b, t // bs]`` at offset
+    ``t % bs``.  Rows at or past seq_lens[b] are set to ``fill``.
+    pool [N_blk, bs, ...] -> [B, seq_len_max, ...].
+    """
+    bs = pool.shape[1]
+    B = block_table.shape[0]
+    out = np.full((B, seq_len_max) + pool.shape[2:], fill, dtype=pool.dtype)
+    for b in range(B):
+        for t in range(int(seq_lens[b])):
+            out[b, t] = pool[block_table[b, t // bs], t % bs]
+    return out

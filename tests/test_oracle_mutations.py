@@ -1,0 +1,89 @@
+"""Plant one plausible mistake at a time in the oracle and check a pin catches it.
+
+The mistakes are planted in the oracle module (on the CPU, through monkeypatch) and
+never touch the GPU path.  Each case names the pin expected to fail.
+"""
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+import test_oracle as P
+
+_orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
+
+
+def _latent_attention_no_rope(q_lat, q_rope, c_kv, k_rope, seq_lens, scale):
+    return _orig["latent_attention"](q_lat, 0 * q_rope, c_kv, k_rope, seq_lens, scale)
+
+
+def _explicit_no_rope(q_nope, q_rope, *a, **k):
+    return _orig["mla_explicit"](q_nope, 0 * q_rope, *a, **k)
+
+
+def _softmax_wrong_sign(s, n_vis):
+    return _orig["_softmax_rows"](-s, n_vis)
+
+
+def _visible_off_by_one(seq_len, q_len, i):
+    return int(min(max(seq_len - q_len + i, 0), seq_len))
+
+
+def _absorb_query_wrong_head(q_nope, w_uk):
+    return _orig["absorb_query"](q_nope, np.roll(w_uk, 1, axis=0))
+
+
+def _absorb_output_wrong_head(o_lat, w_uv):
+    return _orig["absorb_output"](o_lat, np.roll(w_uv, 1, axis=0))
+
+
+def _page_layout_transposed(w_uk, w_uv):
+    n_h, d_h, d_c = w_uk.shape
+    uk = np.transpose(w_uk, (2, 1, 0)).reshape(d_c, n_h * d_h)
+    uv = np.transpose(w_uv, (1, 2, 0)).reshape(d_c, n_h * d_h)
+    return uk, uv
+
+
+def _merge_inverted_weights(o_parts, lse_parts):
+    return _orig["merge_partials"](o_parts, -np.asarray(lse_parts))
+
+
+def _e4m3_wrong_bias(codes):
+    return _orig["decode_e4m3fn"](codes) * 2.0
+
+
+def _bf16_low_half(bits):
+    return np.asarray(bits, np.uint16).astype(np.float64)
+
+
+def _latent_attention_scale_on_latent_only(q_lat, q_rope, c_kv, k_rope, seq_lens, scale):
+    return _orig["latent_attention"](q_lat, q_rope / scale, c_kv, k_rope, seq_lens, scale)
+
+
+def _mha_count_wrong(n_heads, d_head):
+    return n_heads * d_head
+
+
+CASES = [
+    ("latent_attention", _latent_attention_no_rope, lambda: P.pin_absorbed_vs_explicit(P.small_inputs())),
+    ("latent_attention", _latent_attention_scale_on_latent_only,
+     lambda: P.pin_absorbed_vs_explicit(P.small_inputs())),
+    ("mla_explicit", _explicit_no_rope, lambda: P.pin_explicit_vs_sdpa(P.small_inputs())),
+    ("_softmax_rows", _softmax_wrong_sign, lambda: P.pin_explicit_vs_sdpa(P.small_inputs())),
+    ("_softmax_rows", _softmax_wrong_sign, P.pin_softmax_rows),
+    ("visible_keys", _visible_off_by_one, lambda: P.pin_explicit_vs_sdpa(P.small_inputs())),
+    ("absorb_query", _absorb_query_wrong_head, lambda: P.pin_absorbed_vs_explicit(P.small_inputs())),
+    ("absorb_output", _absorb_output_wrong_head, lambda: P.pin_absorbed_vs_explicit(P.small_inputs())),
+    ("to_page_layout", _page_layout_transposed, lambda: P.pin_explicit_vs_sdpa(P.small_inputs())),
+    ("merge_partials", _merge_inverted_weights, lambda: P.pin_split_merge(P.small_inputs(), 3)),
+    ("decode_e4m3fn", _e4m3_wrong_bias, P.pin_e4m3_table),
+    ("decode_bf16", _bf16_low_half, P.pin_bf16_decode),
+    ("mha_cache_numbers_per_token", _mha_count_wrong, P.pin_cache_arithmetic),
+]
+
+
+@pytest.mark.parametrize("name,mutant,pin", CASES, ids=[f"{c[0]}-{c[1].__name__}" for c in CASES])
+def test_pin_catches_planted_mistake(monkeypatch, name, mutant, pin):
+    pin()  # the unmutated oracle passes the pin
+    monkeypatch.setattr(O, name, mutant)
+    with pytest.raises((AssertionError, ValueError)):
+        pin()
