@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Benchmark of one weight-absorbed MLA decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--replicas R]
+
+A step is the whole hot path over one batch: mla_absorb_q -> mla_decode (split-K decode
+kernel + combine) -> mla_absorb_out, on synthetic inputs already resident in HBM.  The
+timed loop cycles over R copies of the cache and weights at distinct addresses so that
+the 151 MB bf16 cache of the headline workload cannot be served from the 256 MB
+last-level (Infinity) cache between steps.
+
+Prints one JSON line:
+  value        latent-cache GB/s of the whole step (cache bytes / step time)
+  roofline     the decode call (its kernels) against the 8 TB/s HBM peak, timed with HIP
+               events around each call inside the timed loop
+  cpu_baseline the CPU oracle (fp64 numpy, absorbed form) on a bounded sample of the
+               same workload, on this host's cores
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop / clk / CU
+
+
+def bytes_of(dtype: str) -> int:
+    return {"f32": 4, "bf16": 2, "fp8": 1}[dtype]
+
+
+def work_counts(cfg, seq_lens) -> dict:
+    """Algorithmic work of one step: every cache byte read once, q in / o out once."""
+    L = np.asarray(seq_lens, np.int64)
+    kvb, ab = bytes_of(cfg.kv_dtype), bytes_of(cfg.act_dtype)
+    per_token = cfg.d_latent * kvb + cfg.d_rope * ab + (4 if cfg.kv_dtype == "fp8" else 0)
+    cache = int(L.sum()) * per_token
+    rows = cfg.batch * cfg.q_len * cfg.n_heads
+    qo = rows * ((cfg.d_latent + cfg.d_rope) * ab + cfg.d_latent * ab + 4)
+    vis = sum(max(0, min(int(l) - cfg.q_len + i + 1, int(l))) for l in L for i in range(cfg.q_len))
+    attn_flops = cfg.n_heads * vis * (2 * (cfg.d_latent + cfg.d_rope) + 2 * cfg.d_latent)
+    absorb_flops = 2 * rows * cfg.d_head * cfg.d_latent
+    weight_bytes = 2 * cfg.n_heads * cfg.d_head * cfg.d_latent * ab
+    return {"cache_bytes": cache, "qo_bytes": qo, "attn_flops": attn_flops,
+            "absorb_flops_each": absorb_flops, "weight_bytes": weight_bytes,
+            "decode_bytes": cache + qo}
+
+
+def decode_sources_sha256() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mla_latent_kv_lat_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.startswith(("decode_", "device_common")):
+            h.update(open(os.path.join(csrc, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per decode call from the committed rocprofv3 counter summary, if it was
+    taken on the current decode sources (else None)."""
+    path = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"decode_sources_sha256:\s*([0-9a-f]{64})", text)
+    m_val = re.search(r"hbm_bytes_per_decode_call:\s*([0-9.eE+]+)", text)
+    if not (m_sha and m_val) or m_sha.group(1) != decode_sources_sha256():
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(inp, budget_s: float) -> dict:
+    """Time the CPU oracle's absorbed form on as many whole sequences as fit the budget."""
+    from oracle import mla_oracle as O
+    cfg = inp.cfg
+    act = cfg.act_dtype
+
+    def dec_seq(b_list):
+        q_nope = O.decode(inp.q_nope[b_list], act)
+        q_rope = O.decode(inp.q_rope[b_list], act)
+        if cfg.paged:
+            lat = O.decode(inp.c_kv, cfg.kv_dtype)
+            rope = O.decode(inp.k_rope, act)
+            lat = O.gather_pages(lat, inp.block_table[b_list], inp.seq_lens[b_list], cfg.seq_len)
+            rope = O.gather_pages(rope, inp.block_table[b_list], inp.seq_lens[b_list], cfg.seq_len)
+        elif cfg.kv_dtype == "fp8":
+            lat = O.dequantize_cache(inp.c_kv[b_list], inp.kv_scale[b_list])
+            rope = O.decode(inp.k_rope[b_list], act)
+        else:
+            lat = O.decode(inp.c_kv[b_list], cfg.kv_dtype)
+            rope = O.decode(inp.k_rope[b_list], act)
+        return q_nope, q_rope, lat, rope
+
+    w_uk, w_uv = O.decode(inp.w_uk, act), O.decode(inp.w_uv, act)
+    done, secs = [], 0.0
+    b = 0
+    while b < cfg.batch:
+        # Grow the sample in whole sequences until the time budget is spent.
+        q_nope, q_rope, lat, rope = dec_seq([b])
+        t0 = time.perf_counter()
+        O.mla_absorbed(q_nope, q_rope, lat, rope, w_uk, w_uv, inp.seq_lens[[b]], cfg.softmax_scale)
+        secs += time.perf_counter() - t0
+        done.append(b)
+        b += 1
+        if secs >= budget_s:
+            break
+    wc = work_counts(cfg, inp.seq_lens[done])
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    return {"value": wc["cache_bytes"] / secs / 1e9, "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{len(done)} of {cfg.batch} sequences of {cfg.name}, whole absorbed "
+                      f"decode (q absorption, attention, output absorption) in fp64, "
+                      f"{secs:.2f} s wall"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
+    ap.add_argument("--replicas", type=int, default=4)
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
+              "not sharded across GPUs in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    from mla_latent_kv_lat_amd import configs, synth
+    from mla_latent_kv_lat_amd.runner import DeviceWorkload
+
+    cfg = configs.BY_NAME[args.workload] if args.workload else configs.HEADLINE
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(cfg, 0)
+    wc = work_counts(cfg, inp.seq_lens)
+    w = DeviceWorkload(inp, split_tokens=args.split_tokens, replicas=args.replicas)
+    print(f"[bench] plan (splits, tokens/split) = {w.plan}; workspace {w.ws_bytes} B",
+          file=sys.stderr, flush=True)
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for _ in range(args.warmup):
+        w.step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for k in range(K):
+        c = w.caches[k % len(w.caches)]
+        w.absorb_q(c)
+        ev[k][0].record()
+        w.decode(c)
+        ev[k][1].record()
+        w.absorb_out(c)
+    stop.record()
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(stop) / K
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_avg = float(np.mean(dec_ms))
+    print(f"[bench] timed {K} steps: {ms_step * 1e3:.1f} us/step, decode call {dec_avg * 1e3:.1f} us "
+          f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})",
+          file=sys.stderr, flush=True)
+
+    achieved = wc["decode_bytes"] / (dec_avg * 1e-3) / 1e9
+    traffic = measured_traffic(cfg.name)
+    result = {
+        "metric": "MLA decode latent-cache GB/s + TFLOP/s and % roofline (bf16, B=32, T=4096)",
+        "value": round(wc["cache_bytes"] / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian latent cache, queries and random-init weights)",
+        "config": {"workload": cfg.name, "batch": cfg.batch, "q_len": cfg.q_len,
+                   "n_heads": cfg.n_heads, "d_head": cfg.d_head, "d_latent": cfg.d_latent,
+                   "d_rope": cfg.d_rope, "seq_len": cfg.seq_len, "kv_dtype": cfg.kv_dtype,
+                   "paged": cfg.paged, "splits": w.plan[0], "split_tokens": w.plan[1],
+                   "cache_replicas": len(w.caches)},
+        "tflops": round(wc["attn_flops"] / (ms_step * 1e-3) / 1e12, 2),
+        "decode_tokens_per_s": round(cfg.batch * cfg.q_len / (ms_step * 1e-3), 1),
+        "decode_call_us": round(dec_avg * 1e3, 2),
+        "decode_call_tflops": round(wc["attn_flops"] / (dec_avg * 1e-3) / 1e12, 2),
+        "decode_call_mfma_frac": round(wc["attn_flops"] / (dec_avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,182 @@
+/*
+ * mla.h -- weight-absorbed Multi-head Latent Attention (MLA) decode on AMD MI355X (gfx950).
+ *
+ * The operation.  MLA caches, per token, one d_c-wide latent c_kv instead of every head's
+ * keys and values; per-head keys and values are the latent times the up-projections
+ * W_UK and W_UV ("Operator Notes (1): MLA -- Multi-head Latent Attention at the Operator
+ * Level", section 2).  A small RoPE key k_rope, shared by all heads, is cached beside the
+ * latent, and the up-projections can be folded into the query side and the output side
+ * ("multi-head latent attention" glossary entry, paragraph on the decoupled RoPE key);
+ * by associativity the folded form gives the same attention result ("Multi-Head Latent
+ * Attention and the compression of the KV cache", paragraph on mathematical
+ * equivalence).  One decode step is three calls:
+ *
+ *   mla_absorb_q    q_lat[b,i,h,:] = q_nope[b,i,h,:] . W_UK[h]              (query side)
+ *   mla_decode      s[t] = scale * (q_lat . c_kv[b,t] + q_rope . k_rope[b,t])
+ *                   p = softmax over visible t;  o_lat = sum_t p[t] * c_kv[b,t]
+ *                   (mla_decode_paged: the same over a block-table-indexed pool)
+ *   mla_absorb_out  out[b,i,h,:] = o_lat[b,i,h,:] . W_UV[h]                  (output side)
+ *
+ * Conventions shared by every entry point.
+ *   - Tensor arguments are DEVICE pointers to dense row-major arrays, shapes listed
+ *     outermost first, aligned to 16 bytes.  Host arguments are marked "host".
+ *   - Index names: B batch, s_q query tokens per sequence, n_h heads, d_h head width,
+ *     d_c latent width, d_r RoPE-key width, T cache rows per sequence.
+ *   - Dtypes: MLA_F32 (IEEE binary32), MLA_BF16 (bfloat16), MLA_FP8_E4M3 (OCP e4m3fn,
+ *     latent cache only, with one float32 scale per token: value = e4m3(code) * scale).
+ *   - Causality: seq_lens[b] counts cache rows INCLUDING the s_q new tokens; query i of
+ *     sequence b sees rows 0 .. seq_lens[b] - s_q + i.  A query that sees no row gets
+ *     o_lat = 0 and lse = -inf.
+ *   - Ownership: the caller owns every buffer.  The library keeps no state, never
+ *     allocates or frees device memory, and never synchronises: each call validates
+ *     its arguments on the host, enqueues its kernels on `stream` (a hipStream_t passed
+ *     as void*, NULL = the null stream) and returns.  Outputs must not alias inputs.
+ *   - Errors: a status is returned; nothing is thrown or aborted across the ABI.  On any
+ *     status other than MLA_OK nothing was enqueued, except MLA_ERR_HIP (a launch
+ *     failed; mla_last_hip_error() gives the hipError_t of the calling thread).
+ *   - Contracts not checked on the host (they live in device memory): s_q <= seq_lens[b]
+ *     <= T (or <= max_seq_len when paged), and block-table entries are valid pool block
+ *     indices for every row below seq_lens[b].  Rows at or past seq_lens[b] and table
+ *     entries past the last used block are never read.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, bad scale, misaligned pointer */
+  MLA_ERR_UNSUPPORTED = 2, /* valid, but no kernel for this dtype / shape combination */
+  MLA_ERR_WORKSPACE = 3,   /* workspace missing or smaller than mla_decode_workspace_bytes */
+  MLA_ERR_HIP = 4          /* a HIP launch failed; see mla_last_hip_error() */
+} mla_status;
+
+typedef enum { MLA_F32 = 0, MLA_BF16 = 1, MLA_FP8_E4M3 = 2 } mla_dtype;
+
+typedef struct {
+  int32_t batch;         /* B   >= 1 */
+  int32_t q_len;         /* s_q in [1, 8] */
+  int32_t n_heads;       /* n_h >= 1 */
+  int32_t d_head;        /* d_h >= 1 */
+  int32_t d_latent;      /* d_c >= 1 */
+  int32_t d_rope;        /* d_r >= 0 */
+  float softmax_scale;   /* finite, > 0; multiplies the whole [latent | rope] dot product */
+  int32_t split_tokens;  /* tokens per split of the context (split-K); 0 = library's choice.
+                            Any value gives the same result up to rounding; a fixed value
+                            gives bitwise-reproducible results. */
+} mla_dims;
+
+/* Supported kernel set (anything else returns MLA_ERR_UNSUPPORTED):
+ *   - every shape with all tensors MLA_F32, and with activations / weights in MLA_BF16
+ *     and the latent cache in MLA_BF16 or MLA_FP8_E4M3 (general kernels);
+ *   - d_c = 512, d_r = 64, activations MLA_BF16, cache MLA_BF16 or MLA_FP8_E4M3,
+ *     s_q * n_h a multiple of 64: the matrix-core (MFMA) decode kernel. */
+
+/* ---- query-side absorption ---------------------------------------------------------
+ * q_lat[b,i,h,c] = sum_j q_nope[b,i,h,j] * w_uk[h,j,c]   (fp32 accumulation)
+ *   q_nope [B, s_q, n_h, d_h]   dtype q_dt
+ *   w_uk   [n_h, d_h, d_c]      dtype w_dt  (w_uk[h,j,c] is the page's W_UK[c, h*d_h + j])
+ *   q_lat  [B, s_q, n_h, d_c]   dtype out_dt (rounded to nearest-even)
+ * q_dt, w_dt, out_dt are all MLA_F32 or all MLA_BF16. */
+mla_status mla_absorb_q(const mla_dims* dims, const void* q_nope, mla_dtype q_dt,
+                        const void* w_uk, mla_dtype w_dt, void* q_lat, mla_dtype out_dt,
+                        void* stream);
+
+/* ---- latent attention (contiguous cache) -------------------------------------------
+ * For every (b, i, h): s[t] = softmax_scale * (q_lat[b,i,h,:] . c_kv[b,t,:]
+ *                                              + q_rope[b,i,h,:] . k_rope[b,t,:]),
+ * p = softmax of s over the visible rows, o_lat[b,i,h,:] = sum_t p[t] * c_kv[b,t,:],
+ * lse[b,i,h] = log sum_t exp(s[t]) (natural log).  fp32 accumulation and softmax.
+ *   q_lat   [B, s_q, n_h, d_c]  dtype q_dt
+ *   q_rope  [B, s_q, n_h, d_r]  dtype q_dt  (may be NULL when d_r == 0)
+ *   c_kv    [B, T, d_c]         dtype kv_dt
+ *   kv_scale[B, T] float32      required iff kv_dt == MLA_FP8_E4M3, else NULL
+ *   k_rope  [B, T, d_r]         dtype rope_dt (== q_dt; may be NULL when d_r == 0)
+ *   T       host, rows per sequence in the cache arrays (their second dimension)
+ *   seq_lens[B] int32           valid rows per sequence, or NULL (every sequence has T)
+ *   o_lat   [B, s_q, n_h, d_c]  dtype o_dt (== q_dt)
+ *   lse     [B, s_q, n_h] float32, or NULL
+ *   workspace / workspace_bytes: device scratch of at least
+ *           mla_decode_workspace_bytes(dims, kv_dt, T) bytes (may be NULL when that is 0);
+ *           its contents on entry are irrelevant and on return unspecified. */
+mla_status mla_decode(const mla_dims* dims, const void* q_lat, const void* q_rope, mla_dtype q_dt,
+                      const void* c_kv, mla_dtype kv_dt, const float* kv_scale,
+                      const void* k_rope, mla_dtype rope_dt, int32_t T, const int32_t* seq_lens,
+                      void* o_lat, mla_dtype o_dt, float* lse, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ---- latent attention over a paged cache -------------------------------------------
+ * Same result as mla_decode on the cache rebuilt from a block pool: logical row t of
+ * sequence b is row (t % block_size) of pool block block_table[b, t / block_size].
+ *   c_kv_pool     [n_blocks, block_size, d_c]  dtype kv_dt
+ *   kv_scale_pool [n_blocks, block_size] f32   iff kv_dt == MLA_FP8_E4M3, else NULL
+ *   k_rope_pool   [n_blocks, block_size, d_r]  dtype rope_dt
+ *   block_table   [B, max_blocks_per_seq] int32
+ *   seq_lens      [B] int32 (required)
+ *   max_seq_len   host upper bound of seq_lens; block_size * max_blocks_per_seq must be
+ *                 >= max_seq_len.  The work grid is sized from it.
+ * Other arguments as mla_decode; workspace sized by mla_decode_workspace_bytes(dims,
+ * kv_dt, max_seq_len).  With the same split_tokens the result is bitwise equal to
+ * mla_decode on the gathered cache. */
+mla_status mla_decode_paged(const mla_dims* dims, const void* q_lat, const void* q_rope,
+                            mla_dtype q_dt, const void* c_kv_pool, mla_dtype kv_dt,
+                            const float* kv_scale_pool, const void* k_rope_pool, mla_dtype rope_dt,
+                            int32_t n_blocks, int32_t block_size, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens, int32_t max_seq_len,
+                            void* o_lat, mla_dtype o_dt, float* lse, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace mla_decode / mla_decode_paged need for this shape, cache dtype
+ * and (maximum) context length; 0 when the chosen plan needs none.  Returns 0 as well for
+ * arguments that mla_decode would reject (call mla_decode_plan to tell the cases apart). */
+size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype kv_dt, int32_t max_seq_len);
+
+/* Host-only: the split-K plan mla_decode would use.  Writes the number of context splits
+ * and the tokens per split (host pointers, either may be NULL).  No HIP call. */
+mla_status mla_decode_plan(const mla_dims* dims, mla_dtype kv_dt, int32_t max_seq_len,
+                           int32_t* num_splits, int32_t* split_tokens);
+
+/* ---- output-side absorption --------------------------------------------------------
+ * out[b,i,h,j] = sum_c o_lat[b,i,h,c] * w_uv[h,c,j]   (fp32 accumulation)
+ *   o_lat [B, s_q, n_h, d_c]  dtype in_dt
+ *   w_uv  [n_h, d_c, d_h]     dtype w_dt  (w_uv[h,c,j] is the page's W_UV[c, h*d_h + j])
+ *   out   [B, s_q, n_h, d_h]  dtype out_dt
+ * in_dt, w_dt, out_dt are all MLA_F32 or all MLA_BF16. */
+mla_status mla_absorb_out(const mla_dims* dims, const void* o_lat, mla_dtype in_dt,
+                          const void* w_uv, mla_dtype w_dt, void* out, mla_dtype out_dt,
+                          void* stream);
+
+/* ---- utilities -------------------------------------------------------------------- */
+
+/* Copy rows of a block pool into a contiguous per-sequence array (the paged lookup alone):
+ * dst[b, t, :] = pool[block_table[b, t / block_size], t % block_size, :] for t < seq_lens[b];
+ * rows t >= seq_lens[b] (t < max_seq_len) are left untouched.  Rows are row_bytes wide
+ * (a multiple of 4).  pool [n_blocks, block_size, row_bytes], dst [B, max_seq_len, row_bytes]. */
+mla_status mla_gather_pages(const void* pool, int32_t n_blocks, int32_t block_size, int64_t row_bytes,
+                            const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t max_seq_len, void* dst, void* stream);
+
+/* Decode every e4m3fn code on the device exactly as the fp8 decode kernels do:
+ * out[k] = value of code k, k = 0..255 (float32 [256]). */
+mla_status mla_fp8_e4m3_table(float* out, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* mla_status_str(mla_status status);
+
+/* hipError_t of the last MLA_ERR_HIP returned on the calling thread (0 if none). */
+int mla_last_hip_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int mla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

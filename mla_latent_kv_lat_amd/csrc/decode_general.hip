@@ -1,0 +1,268 @@
+// General latent-attention decode kernel (VALU) and the split-K combine kernel.
+//
+// The general kernel serves every shape the matrix-core kernel does not (fp32 caches,
+// latent or RoPE widths other than 512 / 64, query-row counts that are not a multiple of
+// 64).  One workgroup owns 4 query rows of one sequence and one split of its context.
+// Scores follow the absorbed form: the head's query, already multiplied by W_UK, is
+// dotted directly with the cached latent, plus the RoPE term ("multi-head latent
+// attention" glossary entry, paragraph on the decoupled RoPE key).  Softmax is the
+// streaming (online) form in base-2 units; the latent itself is the value.
+#include "device_common.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kRB = 4;          // query rows per workgroup (one wave reduces each row)
+constexpr int kTT = 256;        // tokens per step (one per thread in the score phase)
+constexpr int kThreads = 256;
+constexpr int kMaxCols = 8;     // output columns per thread: d_c <= 2048
+
+template <typename QS, typename KVS, bool PAGED>
+__global__ __launch_bounds__(kThreads) void decode_general_kernel(DecodeArgs a, int num_splits,
+                                                                   int chunk) {
+  extern __shared__ float smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int split = blockIdx.x, rblk = blockIdx.y, b = blockIdx.z;
+  const int rows = a.sq * a.H;
+  const int r0 = rblk * kRB;
+  const int D = a.dc + a.dr;
+  const int L = a.seq_lens ? a.seq_lens[b] : int(a.T);
+  const int t_lo = split * chunk;
+  const int t_hi = min(L, t_lo + chunk);
+  // The combine reads only splits that start below the sequence length.
+  if (num_splits > 1 && t_lo >= L) return;
+
+  float* q_s = smem;               // [kRB][D], multiplied by softmax_scale * log2(e)
+  float* p_s = q_s + kRB * D;      // [kRB][kTT] scores, then probabilities
+  float* red_s = p_s + kRB * kTT;  // [3][kRB]: rescale factor, running max, step sum
+
+  using QR = typename QS::raw;
+  using KR = typename KVS::raw;
+  const QR* q_lat = static_cast<const QR*>(a.q_lat);
+  const QR* q_rope = static_cast<const QR*>(a.q_rope);
+  for (int idx = tid; idx < kRB * D; idx += kThreads) {
+    const int r = idx / D, d = idx - r * D, row = r0 + r;
+    float v = 0.f;
+    if (row < rows) {
+      const int64_t qrow = int64_t(b) * rows + row;
+      v = d < a.dc ? load_as_f32<QS>(q_lat, qrow * a.dc + d)
+                   : load_as_f32<QS>(q_rope, qrow * a.dr + (d - a.dc));
+    }
+    q_s[idx] = v * a.scale_log2;
+  }
+  int vis[kRB];  // query i of the sequence sees tokens t < L - s_q + i + 1
+#pragma unroll
+  for (int r = 0; r < kRB; ++r) {
+    const int row = r0 + r;
+    const int i = row / a.H;
+    vis[r] = row < rows ? min(max(L - a.sq + i + 1, 0), L) : 0;
+  }
+  float m[kRB], l[kRB], acc[kRB][kMaxCols];
+#pragma unroll
+  for (int r = 0; r < kRB; ++r) {
+    m[r] = -INFINITY;
+    l[r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kMaxCols; ++j) acc[r][j] = 0.f;
+  }
+  const KR* kv = static_cast<const KR*>(a.c_kv);
+  const QR* kr = static_cast<const QR*>(a.k_rope);
+  constexpr bool kFp8 = sizeof(KR) == 1;
+  __syncthreads();
+
+  for (int t0 = t_lo; t0 < t_hi; t0 += kTT) {
+    // Scores: thread tid owns token t0 + tid.
+    float sc[kRB];
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) sc[r] = -INFINITY;
+    const int t = t0 + tid;
+    if (t < t_hi) {
+      const int64_t crow = cache_row(PAGED, b, t, a.T, a.block_table, a.max_blocks, a.block_size);
+      float dl[kRB] = {}, dp[kRB] = {};
+      for (int d = 0; d < a.dc; ++d) {
+        const float x = load_as_f32<KVS>(kv, crow * a.dc + d);
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) dl[r] += q_s[r * D + d] * x;
+      }
+      for (int d = 0; d < a.dr; ++d) {
+        const float x = load_as_f32<QS>(kr, crow * a.dr + d);
+#pragma unroll
+        for (int r = 0; r < kRB; ++r) dp[r] += q_s[r * D + a.dc + d] * x;
+      }
+      const float ts = kFp8 ? a.kv_scale[crow] : 1.f;
+#pragma unroll
+      for (int r = 0; r < kRB; ++r)
+        if (t < vis[r]) sc[r] = dl[r] * ts + dp[r];
+    }
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) p_s[r * kTT + tid] = sc[r];
+    __syncthreads();
+    {
+      // Wave w updates the statistics of row w over this step's tokens.
+      const int r = wave;
+      float v[kTT / 64];
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < kTT / 64; ++j) {
+        v[j] = p_s[r * kTT + lane + 64 * j];
+        cmax = fmaxf(cmax, v[j]);
+      }
+      cmax = wave_max(cmax);
+      float m_old = -INFINITY;
+#pragma unroll
+      for (int rr = 0; rr < kRB; ++rr)
+        if (rr == r) m_old = m[rr];
+      const float m_new = fmaxf(m_old, cmax);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      float csum = 0.f;
+#pragma unroll
+      for (int j = 0; j < kTT / 64; ++j) {
+        const float p = exp2f(v[j] - m_use);
+        p_s[r * kTT + lane + 64 * j] = p;
+        csum += p;
+      }
+      csum = wave_sum(csum);
+      if (lane == 0) {
+        red_s[r] = exp2f(m_old - m_use);
+        red_s[kRB + r] = m_new;
+        red_s[2 * kRB + r] = csum;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int r = 0; r < kRB; ++r) {
+      const float alpha = red_s[r];
+      m[r] = red_s[kRB + r];
+      l[r] = l[r] * alpha + red_s[2 * kRB + r];
+#pragma unroll
+      for (int j = 0; j < kMaxCols; ++j) acc[r][j] *= alpha;
+    }
+    // Weighted sum of latent rows: thread tid owns columns tid, tid + 256, ...
+    const int nt = min(kTT, t_hi - t0);
+    for (int tt = 0; tt < nt; ++tt) {
+      const int64_t crow =
+          cache_row(PAGED, b, t0 + tt, a.T, a.block_table, a.max_blocks, a.block_size);
+      const float ts = kFp8 ? a.kv_scale[crow] : 1.f;
+      float pr[kRB];
+#pragma unroll
+      for (int r = 0; r < kRB; ++r) pr[r] = p_s[r * kTT + tt] * ts;
+#pragma unroll
+      for (int j = 0; j < kMaxCols; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < a.dc) {
+          const float x = load_as_f32<KVS>(kv, crow * a.dc + c);
+#pragma unroll
+          for (int r = 0; r < kRB; ++r) acc[r][j] += pr[r] * x;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  using OR = typename QS::raw;
+#pragma unroll
+  for (int r = 0; r < kRB; ++r) {
+    const int row = r0 + r;
+    if (row >= rows) continue;
+    const float inv = l[r] > 0.f ? 1.f / l[r] : 0.f;
+    const float lse2 = l[r] > 0.f ? m[r] + log2f(l[r]) : -INFINITY;
+    if (num_splits == 1) {
+      OR* o = static_cast<OR*>(a.o_lat) + (int64_t(b) * rows + row) * a.dc;
+#pragma unroll
+      for (int j = 0; j < kMaxCols; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < a.dc) store_from_f32<QS>(o, c, acc[r][j] * inv);
+      }
+      if (a.lse && tid == 0) a.lse[int64_t(b) * rows + row] = lse2 * kLn2;
+    } else {
+      const int64_t prow = (int64_t(b) * num_splits + split) * rows + row;
+      float* o = a.part_o + prow * a.dc;
+#pragma unroll
+      for (int j = 0; j < kMaxCols; ++j) {
+        const int c = tid + j * kThreads;
+        if (c < a.dc) o[c] = acc[r][j] * inv;
+      }
+      if (tid == 0) a.part_lse[prow] = lse2;
+    }
+  }
+}
+
+// Merge the splits of one (sequence, query row): weights 2^(lse_s - max) over the splits
+// that start below the sequence length; output = weighted mean of the normalised partial
+// outputs; lse = max + log2(sum of weights), returned in natural-log units.
+template <typename OS>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int chunk) {
+  extern __shared__ float w_s[];  // [S] weights, then 2 reduction slots per wave
+  const int row = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int rows = a.sq * a.H;
+  const int L = a.seq_lens ? a.seq_lens[b] : int(a.T);
+  const int nvalid = min(S, (L + chunk - 1) / chunk);
+  const float* pl = a.part_lse + int64_t(b) * S * rows + row;
+  float* red = w_s + S;
+
+  float mx = -INFINITY;
+  for (int s = tid; s < nvalid; s += 256) mx = fmaxf(mx, pl[int64_t(s) * rows]);
+  mx = wave_max(mx);
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float m_use = mx == -INFINITY ? 0.f : mx;
+  float tot = 0.f;
+  for (int s = tid; s < nvalid; s += 256) {
+    const float w = exp2f(pl[int64_t(s) * rows] - m_use);
+    w_s[s] = w;
+    tot += w;
+  }
+  tot = wave_sum(tot);
+  __syncthreads();
+  if (lane == 0) red[4 + wave] = tot;
+  __syncthreads();
+  tot = red[4] + red[5] + red[6] + red[7];
+  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  using OR = typename OS::raw;
+  OR* o = static_cast<OR*>(a.o_lat) + (int64_t(b) * rows + row) * a.dc;
+  const float* po = a.part_o + (int64_t(b) * S * rows + row) * a.dc;
+  for (int c = tid; c < a.dc; c += 256) {
+    float v = 0.f;
+    for (int s = 0; s < nvalid; ++s) v += w_s[s] * po[int64_t(s) * rows * a.dc + c];
+    store_from_f32<OS>(o, c, v * inv);
+  }
+  if (a.lse && tid == 0)
+    a.lse[int64_t(b) * rows + row] = tot > 0.f ? (m_use + log2f(tot)) * kLn2 : -INFINITY;
+}
+
+template <typename QS, typename KVS, bool PAGED>
+int launch_general_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+  const dim3 grid(p.num_splits, (p.rows + kRB - 1) / kRB, a.B);
+  const size_t lds = sizeof(float) * (kRB * (a.dc + a.dr) + kRB * kTT + 3 * kRB);
+  hipLaunchKernelGGL((decode_general_kernel<QS, KVS, PAGED>), grid, dim3(kThreads), lds, s, a,
+                     p.num_splits, p.split_tokens);
+  return int(hipGetLastError());
+}
+
+template <typename QS, typename KVS>
+int launch_general_p(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+  return a.paged ? launch_general_t<QS, KVS, true>(a, p, s) : launch_general_t<QS, KVS, false>(a, p, s);
+}
+
+}  // namespace
+
+int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+  if (a.q_dt == MLA_F32) return launch_general_p<F32, F32>(a, p, s);
+  if (a.kv_dt == MLA_FP8_E4M3) return launch_general_p<BF16, FP8>(a, p, s);
+  return launch_general_p<BF16, BF16>(a, p, s);
+}
+
+int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+  const dim3 grid(p.rows, a.B);
+  const size_t lds = sizeof(float) * (p.num_splits + 8);
+  if (a.q_dt == MLA_F32)
+    hipLaunchKernelGGL((combine_kernel<F32>), grid, dim3(256), lds, s, a, p.num_splits, p.split_tokens);
+  else
+    hipLaunchKernelGGL((combine_kernel<BF16>), grid, dim3(256), lds, s, a, p.num_splits, p.split_tokens);
+  return int(hipGetLastError());
+}
+
+}  // namespace mla

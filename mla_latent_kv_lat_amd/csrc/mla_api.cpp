@@ -1,0 +1,310 @@
+// C ABI of libmla: argument validation, split-K planning and kernel dispatch.
+//
+// Validation and planning are pure host logic and run before any HIP call, so every
+// error path can be exercised on a machine without a GPU.  Launch failures surface as
+// MLA_ERR_HIP with the hipError_t kept per thread.
+#include <cmath>
+#include <cstdint>
+
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kNumCUs = 256;          // MI355X compute units; the plan targets a fixed count
+constexpr int kMaxLatent = 2048;      // general-kernel limits (query rows are staged in LDS)
+constexpr int kMaxRope = 512;
+constexpr int kMaxQLen = 8;
+constexpr int kMaxRows = 1 << 16;
+constexpr bool kMfmaDecodeReady = false;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+size_t elem_bytes(mla_dtype t) {
+  switch (t) {
+    case MLA_F32: return 4;
+    case MLA_BF16: return 2;
+    case MLA_FP8_E4M3: return 1;
+  }
+  return 0;
+}
+
+bool valid_dtype(mla_dtype t) { return t == MLA_F32 || t == MLA_BF16 || t == MLA_FP8_E4M3; }
+
+mla_status hip_status(int err) {
+  if (err == 0) return MLA_OK;
+  g_last_hip_error = err;
+  return MLA_ERR_HIP;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shared argument checks of mla_decode and mla_decode_paged.
+mla_status check_decode_common(const mla_dims* d, const void* q_lat, const void* q_rope,
+                               mla_dtype q_dt, const void* kv, mla_dtype kv_dt,
+                               const float* kv_scale, const void* k_rope, mla_dtype rope_dt,
+                               const void* o_lat, mla_dtype o_dt, const float* lse) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!valid_dtype(q_dt) || !valid_dtype(kv_dt) || !valid_dtype(rope_dt) || !valid_dtype(o_dt))
+    return MLA_ERR_INVALID_ARG;
+  if (!q_lat || !kv || !o_lat) return MLA_ERR_INVALID_ARG;
+  if (d->d_rope > 0 && (!q_rope || !k_rope)) return MLA_ERR_INVALID_ARG;
+  if ((kv_dt == MLA_FP8_E4M3) != (kv_scale != nullptr)) return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_lat, 16) || !aligned(kv, 16) || !aligned(o_lat, 16)) return MLA_ERR_INVALID_ARG;
+  if (q_rope && !aligned(q_rope, 16)) return MLA_ERR_INVALID_ARG;
+  if (k_rope && !aligned(k_rope, 16)) return MLA_ERR_INVALID_ARG;
+  if (kv_scale && !aligned(kv_scale, 4)) return MLA_ERR_INVALID_ARG;
+  if (lse && !aligned(lse, 4)) return MLA_ERR_INVALID_ARG;
+  // Supported dtype sets.
+  if (q_dt == MLA_FP8_E4M3 || rope_dt != q_dt || o_dt != q_dt) return MLA_ERR_UNSUPPORTED;
+  if (q_dt == MLA_F32 && kv_dt != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (q_dt == MLA_BF16 && kv_dt == MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (d->d_latent > kMaxLatent || d->d_rope > kMaxRope) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+void fill_common(DecodeArgs* a, const mla_dims* d, const void* q_lat, const void* q_rope,
+                 mla_dtype q_dt, const void* kv, mla_dtype kv_dt, const float* kv_scale,
+                 const void* k_rope, void* o_lat, float* lse) {
+  a->B = d->batch;
+  a->sq = d->q_len;
+  a->H = d->n_heads;
+  a->dc = d->d_latent;
+  a->dr = d->d_rope;
+  a->scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  a->q_lat = q_lat;
+  a->q_rope = q_rope;
+  a->q_dt = q_dt;
+  a->c_kv = kv;
+  a->kv_dt = kv_dt;
+  a->kv_scale = kv_scale;
+  a->k_rope = k_rope;
+  a->o_lat = o_lat;
+  a->lse = lse;
+  a->paged = false;
+  a->block_size = 0;
+  a->block_table = nullptr;
+  a->max_blocks = 0;
+  a->part_o = nullptr;
+  a->part_lse = nullptr;
+}
+
+mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t ws_bytes) {
+  if (p.workspace == 0) return MLA_OK;
+  if (!ws || ws_bytes < p.workspace || !aligned(ws, 256)) return MLA_ERR_WORKSPACE;
+  const size_t o_bytes = align_up(size_t(a->B) * p.num_splits * p.rows * a->dc * 4, 256);
+  a->part_o = static_cast<float*>(ws);
+  a->part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+  return MLA_OK;
+}
+
+mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+  int err = p.kernel == DecodeKernel::kMfma ? launch_decode_mfma(a, p, s)
+                                            : launch_decode_general(a, p, s);
+  if (err) return hip_status(err);
+  if (p.num_splits > 1) return hip_status(launch_combine(a, p, s));
+  return MLA_OK;
+}
+
+}  // namespace
+
+mla_status check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->q_len < 1 || d->q_len > kMaxQLen || d->n_heads < 1 || d->d_head < 1 ||
+      d->d_latent < 1 || d->d_rope < 0 || d->split_tokens < 0)
+    return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (int64_t(d->q_len) * d->n_heads > kMaxRows) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt) {
+  return kMfmaDecodeReady && q_dt == MLA_BF16 && (kv_dt == MLA_BF16 || kv_dt == MLA_FP8_E4M3) && d->d_latent == 512 &&
+         d->d_rope == 64 && (d->q_len * d->n_heads) % 64 == 0;
+}
+
+mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
+                       DecodePlan* plan) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (max_seq_len < 1) return MLA_ERR_INVALID_ARG;
+  DecodePlan p{};
+  p.rows = d->q_len * d->n_heads;
+  int tile, min_chunk;
+  if (mfma_decode_eligible(d, q_dt, kv_dt)) {
+    p.kernel = DecodeKernel::kMfma;
+    p.row_block = 64;
+    tile = 64;
+    min_chunk = 512;
+  } else {
+    p.kernel = DecodeKernel::kGeneral;
+    p.row_block = 4;
+    tile = 256;
+    min_chunk = 256;
+  }
+  const int64_t units = int64_t(d->batch) * ceil_div(p.rows, p.row_block);
+  int64_t chunk;
+  if (d->split_tokens > 0) {
+    chunk = ceil_div(d->split_tokens, tile) * tile;
+  } else {
+    // Enough workgroups to give every compute unit at least one, without making a split
+    // so short that its partial result costs more traffic than its share of the cache.
+    const int64_t want_splits = ceil_div(kNumCUs, units);
+    chunk = ceil_div(ceil_div(max_seq_len, want_splits), tile) * tile;
+    if (chunk < min_chunk) chunk = min_chunk;
+  }
+  const int64_t splits = ceil_div(max_seq_len, chunk);
+  if (splits > 8192 || chunk > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  p.num_splits = int32_t(splits);
+  p.split_tokens = int32_t(chunk);
+  if (p.num_splits > 1) {
+    p.workspace = align_up(size_t(d->batch) * splits * p.rows * d->d_latent * 4, 256) +
+                  align_up(size_t(d->batch) * splits * p.rows * 4, 256);
+  }
+  *plan = p;
+  return MLA_OK;
+}
+
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+mla_status mla_absorb_q(const mla_dims* d, const void* q_nope, mla_dtype q_dt, const void* w_uk,
+                        mla_dtype w_dt, void* q_lat, mla_dtype out_dt, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!valid_dtype(q_dt) || !valid_dtype(w_dt) || !valid_dtype(out_dt)) return MLA_ERR_INVALID_ARG;
+  if (!q_nope || !w_uk || !q_lat) return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_nope, 16) || !aligned(w_uk, 16) || !aligned(q_lat, 16)) return MLA_ERR_INVALID_ARG;
+  if (q_dt != w_dt || q_dt != out_dt || q_dt == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  return hip_status(launch_absorb(q_nope, w_uk, q_lat, q_dt, d->batch * d->q_len, d->n_heads,
+                                  d->d_head, d->d_latent, static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_absorb_out(const mla_dims* d, const void* o_lat, mla_dtype in_dt, const void* w_uv,
+                          mla_dtype w_dt, void* out, mla_dtype out_dt, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!valid_dtype(in_dt) || !valid_dtype(w_dt) || !valid_dtype(out_dt)) return MLA_ERR_INVALID_ARG;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (!aligned(o_lat, 16) || !aligned(w_uv, 16) || !aligned(out, 16)) return MLA_ERR_INVALID_ARG;
+  if (in_dt != w_dt || in_dt != out_dt || in_dt == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  return hip_status(launch_absorb(o_lat, w_uv, out, in_dt, d->batch * d->q_len, d->n_heads,
+                                  d->d_latent, d->d_head, static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* d, mla_dtype kv_dt, int32_t max_seq_len) {
+  DecodePlan p;
+  mla_dtype q_dt = kv_dt == MLA_F32 ? MLA_F32 : MLA_BF16;
+  if (plan_decode(d, q_dt, kv_dt, max_seq_len, &p) != MLA_OK) return 0;
+  return p.workspace;
+}
+
+mla_status mla_decode_plan(const mla_dims* d, mla_dtype kv_dt, int32_t max_seq_len,
+                           int32_t* num_splits, int32_t* split_tokens) {
+  if (!valid_dtype(kv_dt)) return MLA_ERR_INVALID_ARG;
+  DecodePlan p;
+  mla_dtype q_dt = kv_dt == MLA_F32 ? MLA_F32 : MLA_BF16;
+  mla_status st = plan_decode(d, q_dt, kv_dt, max_seq_len, &p);
+  if (st != MLA_OK) return st;
+  if (num_splits) *num_splits = p.num_splits;
+  if (split_tokens) *split_tokens = p.split_tokens;
+  return MLA_OK;
+}
+
+mla_status mla_decode(const mla_dims* d, const void* q_lat, const void* q_rope, mla_dtype q_dt,
+                      const void* c_kv, mla_dtype kv_dt, const float* kv_scale, const void* k_rope,
+                      mla_dtype rope_dt, int32_t T, const int32_t* seq_lens, void* o_lat,
+                      mla_dtype o_dt, float* lse, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  mla_status st = check_decode_common(d, q_lat, q_rope, q_dt, c_kv, kv_dt, kv_scale, k_rope,
+                                       rope_dt, o_lat, o_dt, lse);
+  if (st != MLA_OK) return st;
+  if (T < 1) return MLA_ERR_INVALID_ARG;
+  if (seq_lens && !aligned(seq_lens, 4)) return MLA_ERR_INVALID_ARG;
+  DecodePlan p;
+  st = plan_decode(d, q_dt, kv_dt, T, &p);
+  if (st != MLA_OK) return st;
+  DecodeArgs a;
+  fill_common(&a, d, q_lat, q_rope, q_dt, c_kv, kv_dt, kv_scale, k_rope, o_lat, lse);
+  a.T = T;
+  a.seq_lens = seq_lens;
+  st = attach_workspace(&a, p, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  return run_decode(a, p, static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_decode_paged(const mla_dims* d, const void* q_lat, const void* q_rope,
+                            mla_dtype q_dt, const void* c_kv_pool, mla_dtype kv_dt,
+                            const float* kv_scale_pool, const void* k_rope_pool, mla_dtype rope_dt,
+                            int32_t n_blocks, int32_t block_size, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens,
+                            int32_t max_seq_len, void* o_lat, mla_dtype o_dt, float* lse,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_decode_common(d, q_lat, q_rope, q_dt, c_kv_pool, kv_dt, kv_scale_pool,
+                                       k_rope_pool, rope_dt, o_lat, o_dt, lse);
+  if (st != MLA_OK) return st;
+  if (n_blocks < 1 || block_size < 1 || max_blocks_per_seq < 1 || max_seq_len < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!block_table || !seq_lens || !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (int64_t(block_size) * max_blocks_per_seq < max_seq_len) return MLA_ERR_INVALID_ARG;
+  DecodePlan p;
+  st = plan_decode(d, q_dt, kv_dt, max_seq_len, &p);
+  if (st != MLA_OK) return st;
+  DecodeArgs a;
+  fill_common(&a, d, q_lat, q_rope, q_dt, c_kv_pool, kv_dt, kv_scale_pool, k_rope_pool, o_lat, lse);
+  a.T = max_seq_len;
+  a.seq_lens = seq_lens;
+  a.paged = true;
+  a.block_size = block_size;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  st = attach_workspace(&a, p, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  return run_decode(a, p, static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_gather_pages(const void* pool, int32_t n_blocks, int32_t block_size, int64_t row_bytes,
+                            const int32_t* block_table, int32_t batch, int32_t max_blocks_per_seq,
+                            const int32_t* seq_lens, int32_t max_seq_len, void* dst, void* stream) {
+  if (!pool || !block_table || !seq_lens || !dst) return MLA_ERR_INVALID_ARG;
+  if (n_blocks < 1 || block_size < 1 || row_bytes < 4 || row_bytes % 4 || batch < 1 ||
+      max_blocks_per_seq < 1 || max_seq_len < 1)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(pool, 4) || !aligned(dst, 4) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (int64_t(block_size) * max_blocks_per_seq < max_seq_len) return MLA_ERR_INVALID_ARG;
+  return hip_status(launch_gather_pages(pool, block_size, row_bytes, block_table, batch,
+                                        max_blocks_per_seq, seq_lens, max_seq_len, dst,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_fp8_e4m3_table(float* out, void* stream) {
+  if (!out || !aligned(out, 4)) return MLA_ERR_INVALID_ARG;
+  return hip_status(launch_fp8_table(out, static_cast<hipStream_t>(stream)));
+}
+
+const char* mla_status_str(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG: invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED: no kernel for this dtype/shape";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE: workspace missing or too small";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP: a HIP launch failed";
+  }
+  return "unknown mla_status";
+}
+
+int mla_last_hip_error(void) { return g_last_hip_error; }
+
+int mla_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal host-side interface between the C ABI (mla_api.cpp) and the kernel launchers.
+// No device code here, so the validation and planning logic builds as plain C++ too.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "mla.h"
+
+typedef struct ihipStream_t* hipStream_t;
+
+namespace mla {
+
+// Which decode kernel family runs a call.
+enum class DecodeKernel : int {
+  kGeneral = 0,  // VALU kernel for any supported shape (one workgroup per 4 query rows)
+  kMfma = 1,     // matrix-core kernel for d_c = 512, d_r = 64, bf16 queries, bf16/fp8 cache
+};
+
+// Split-K plan of one decode call.
+struct DecodePlan {
+  DecodeKernel kernel;
+  int32_t rows;          // s_q * n_h query rows per sequence
+  int32_t row_block;     // query rows per workgroup
+  int32_t num_splits;    // context splits per sequence (grid dimension)
+  int32_t split_tokens;  // tokens per split (multiple of the token tile)
+  size_t workspace;      // bytes of partial results (0 when num_splits == 1)
+};
+
+// Everything a decode kernel reads or writes.  Pointers are device pointers.
+struct DecodeArgs {
+  int32_t B, sq, H, dc, dr;
+  float scale_log2;      // softmax_scale * log2(e): scores are kept in base-2 units
+  const void* q_lat;     // [B, sq, H, dc]
+  const void* q_rope;    // [B, sq, H, dr]
+  mla_dtype q_dt;
+  const void* c_kv;      // [B, T, dc] or pool [n_blocks, block_size, dc]
+  mla_dtype kv_dt;
+  const float* kv_scale; // [B, T] or pool [n_blocks, block_size] (fp8 only)
+  const void* k_rope;    // [B, T, dr] or pool
+  int64_t T;             // rows per sequence of a contiguous cache
+  const int32_t* seq_lens;  // [B] or nullptr (every sequence has T rows)
+  bool paged;
+  int32_t block_size;
+  const int32_t* block_table;  // [B, max_blocks]
+  int32_t max_blocks;
+  void* o_lat;           // [B, sq, H, dc], dtype q_dt
+  float* lse;            // [B, sq, H] or nullptr
+  float* part_o;         // [B, S, rows, dc] normalised partial outputs (S > 1)
+  float* part_lse;       // [B, S, rows] base-2 log-sum-exp of each split (S > 1)
+};
+
+// Host-only validation and planning (mla_api.cpp).
+mla_status check_dims(const mla_dims* d);
+mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
+                       DecodePlan* plan);
+bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt);
+
+// Launchers (one per kernel file).  Return the hipError_t of the launch as int.
+int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+int launch_absorb(const void* x, const void* w, void* y, mla_dtype dt, int32_t M, int32_t H,
+                  int32_t K, int32_t N, hipStream_t s);
+int launch_gather_pages(const void* pool, int32_t block_size, int64_t row_bytes,
+                        const int32_t* table, int32_t B, int32_t max_blocks, const int32_t* seq_lens,
+                        int32_t max_seq_len, void* dst, hipStream_t s);
+int launch_fp8_table(float* out, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,201 @@
+"""Host-side checks of the C ABI: no GPU needed, no kernel is ever launched.
+
+Every call below fails validation (or is host-only planning), so it returns before the
+library makes any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from mla_latent_kv_lat_amd import build, capi as L, configs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+A = 1 << 20  # a fake, 16-byte aligned "device address": never dereferenced on these paths
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        build.build()
+    return L.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTED)
+
+
+def test_status_strings_and_version():
+    for s in range(5):
+        assert L.mla_status_str(s).startswith("MLA_")
+    assert "unknown" in L.mla_status_str(99)
+    assert L.mla_version() >= 100
+    assert L.mla_last_hip_error() == 0
+
+
+def v2(**kw):
+    c = configs.V2_DECODE
+    base = dict(batch=c.batch, q_len=c.q_len, n_heads=c.n_heads, d_head=c.d_head,
+                d_latent=c.d_latent, d_rope=c.d_rope, softmax_scale=c.softmax_scale)
+    base.update(kw)
+    return L.dims(**base)
+
+
+BAD_DIMS = [dict(batch=0), dict(q_len=0), dict(q_len=9), dict(n_heads=0), dict(d_head=0),
+            dict(d_latent=0), dict(d_rope=-1), dict(softmax_scale=0.0),
+            dict(softmax_scale=float("nan")), dict(softmax_scale=float("inf")),
+            dict(softmax_scale=-1.0), dict(split_tokens=-5)]
+
+
+@pytest.mark.parametrize("bad", BAD_DIMS)
+def test_bad_dims_rejected_everywhere(bad):
+    d = v2(**bad)
+    bf = "bf16"
+    assert L.mla_absorb_q(d, A, A, A, dtype=bf, check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_absorb_out(d, A, A, A, dtype=bf, check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_decode(d, A, A, A, A, 4096, None, A, None, A, 1 << 30, q_dtype=bf, kv_dtype=bf,
+                        check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_paged(d, A, A, A, A, A, A, 4096, A, None, A, 1 << 30, block_size=64,
+                              n_blocks=64, max_blocks_per_seq=64, q_dtype=bf, kv_dtype=bf,
+                              check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_workspace_bytes(d, "bf16", 4096) == 0
+    assert L.mla_decode_plan(d, "bf16", 4096, check=False)[0] == L.MLA_ERR_INVALID_ARG
+
+
+def test_null_dims_pointer(lib):
+    f = lib.mla_absorb_q
+    assert f(None, A, 1, A, 1, A, 1, None) == L.MLA_ERR_INVALID_ARG
+    assert lib.mla_decode_workspace_bytes(None, 1, 4096) == 0
+
+
+def test_absorb_argument_errors():
+    d = v2()
+    assert L.mla_absorb_q(d, 0, A, A, dtype="bf16", check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_absorb_q(d, A, 0, A, dtype="bf16", check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_absorb_q(d, A, A, 0, dtype="bf16", check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_absorb_q(d, A + 2, A, A, dtype="bf16", check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_absorb_out(d, A, A + 8, A, dtype="bf16", check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_absorb_q(d, A, A, A, dtype="fp8", check=False) == L.MLA_ERR_UNSUPPORTED
+    assert L.mla_absorb_q(d, A, A, A, dtype=7, check=False) == L.MLA_ERR_INVALID_ARG
+    # mixed dtypes
+    lib = L.library()
+    st = lib.mla_absorb_q(ctypes.byref(d), ctypes.c_void_p(A), L.MLA_BF16, ctypes.c_void_p(A),
+                          L.MLA_F32, ctypes.c_void_p(A), L.MLA_BF16, None)
+    assert st == L.MLA_ERR_UNSUPPORTED
+
+
+def _decode(d, **kw):
+    args = dict(q_lat=A, q_rope=A, c_kv=A, k_rope=A, T=4096, seq_lens=None, o_lat=A, lse=None,
+                workspace=A, workspace_bytes=1 << 30, q_dtype="bf16", kv_dtype="bf16")
+    args.update(kw)
+    return L.mla_decode(d, args.pop("q_lat"), args.pop("q_rope"), args.pop("c_kv"), args.pop("k_rope"),
+                        args.pop("T"), args.pop("seq_lens"), args.pop("o_lat"), args.pop("lse"),
+                        args.pop("workspace"), args.pop("workspace_bytes"), check=False, **args)
+
+
+def test_decode_argument_errors():
+    d = v2(split_tokens=512)
+    E, U, W = L.MLA_ERR_INVALID_ARG, L.MLA_ERR_UNSUPPORTED, L.MLA_ERR_WORKSPACE
+    assert _decode(d, q_lat=0) == E
+    assert _decode(d, c_kv=0) == E
+    assert _decode(d, o_lat=0) == E
+    assert _decode(d, q_rope=0) == E          # d_r > 0 needs the RoPE query
+    assert _decode(d, k_rope=0) == E
+    assert _decode(d, T=0) == E
+    assert _decode(d, c_kv=A + 4) == E        # misaligned
+    assert _decode(d, lse=A + 2) == E
+    assert _decode(d, seq_lens=A + 1) == E
+    assert _decode(d, kv_dtype="fp8") == E    # fp8 cache without its scale
+    assert _decode(d, kv_scale=A) == E        # scale given for a bf16 cache
+    assert _decode(d, q_dtype="fp8", kv_dtype="fp8", kv_scale=A) == U
+    assert _decode(d, q_dtype="f32", kv_dtype="bf16") == U
+    assert _decode(d, q_dtype="bf16", kv_dtype="f32") == U
+    assert _decode(v2(d_latent=4096)) == U
+    need = L.mla_decode_workspace_bytes(d, "bf16", 4096)
+    assert need > 0
+    assert _decode(d, workspace=None, workspace_bytes=0) == W
+    assert _decode(d, workspace_bytes=need - 1) == W
+    assert _decode(d, workspace=A + 16, workspace_bytes=need) == W   # not 256-byte aligned
+
+
+def test_decode_without_rope_needs_no_rope_pointers():
+    d = v2(d_rope=0, split_tokens=512)
+    # Passes validation up to the workspace check, which fails on purpose (a split plan
+    # needs a workspace), so nothing is launched.
+    assert L.mla_decode_workspace_bytes(d, "bf16", 4096) > 0
+    assert _decode(d, q_rope=0, k_rope=0, workspace=None, workspace_bytes=0) == L.MLA_ERR_WORKSPACE
+
+
+def test_paged_argument_errors():
+    d = v2(split_tokens=1024)
+    need = L.mla_decode_workspace_bytes(d, "bf16", 16384)
+
+    def call(**kw):
+        a = dict(block_table=A, seq_lens=A, max_seq_len=16384, block_size=64, n_blocks=100,
+                 max_blocks_per_seq=256, workspace=A, workspace_bytes=need)
+        a.update(kw)
+        return L.mla_decode_paged(d, A, A, A, A, a.pop("block_table"), a.pop("seq_lens"),
+                                  a.pop("max_seq_len"), A, None, a.pop("workspace"),
+                                  a.pop("workspace_bytes"), q_dtype="bf16", kv_dtype="bf16",
+                                  check=False, **a)
+
+    E = L.MLA_ERR_INVALID_ARG
+    assert call(block_table=0) == E
+    assert call(seq_lens=0) == E
+    assert call(block_size=0) == E
+    assert call(n_blocks=0) == E
+    assert call(max_blocks_per_seq=0) == E
+    assert call(max_seq_len=0) == E
+    assert call(max_blocks_per_seq=255) == E  # 64 * 255 < 16384
+    assert call(block_table=A + 2) == E
+    assert call(workspace_bytes=need - 256) == L.MLA_ERR_WORKSPACE
+
+
+def test_utility_argument_errors():
+    E = L.MLA_ERR_INVALID_ARG
+    g = L.mla_gather_pages
+    kw = dict(block_size=64, n_blocks=10, row_bytes=1152, batch=2, max_blocks_per_seq=4, check=False)
+    assert g(0, A, A, 256, A, **kw) == E
+    assert g(A, A, A, 256, 0, **kw) == E
+    assert g(A, A, A, 256, A, **{**kw, "row_bytes": 6}) == E
+    assert g(A, A, A, 300, A, **kw) == E      # 64 * 4 < 300
+    assert L.mla_fp8_e4m3_table(0, check=False) == E
+
+
+@pytest.mark.parametrize("cfg", configs.ALL, ids=lambda c: c.name)
+def test_plan_covers_the_context(cfg):
+    d = L.dims_from_config(cfg)
+    n, tok = L.mla_decode_plan(d, cfg.kv_dtype, cfg.seq_len)
+    assert n >= 1 and tok >= 1
+    assert (n - 1) * tok < cfg.seq_len <= n * tok
+    ws = L.mla_decode_workspace_bytes(d, cfg.kv_dtype, cfg.seq_len)
+    rows = cfg.q_len * cfg.n_heads
+    if n == 1:
+        assert ws == 0
+    else:
+        po = cfg.batch * n * rows * cfg.d_latent * 4
+        pl = cfg.batch * n * rows * 4
+        r = lambda x: (x + 255) // 256 * 256
+        assert ws == r(po) + r(pl)
+
+
+def test_plan_honours_split_tokens():
+    cfg = configs.LONG_CONTEXT
+    for st in (1, 100, 4096, 200000):
+        d = L.dims_from_config(cfg, split_tokens=st)
+        n, tok = L.mla_decode_plan(d, "bf16", cfg.seq_len)
+        assert tok >= st and (n - 1) * tok < cfg.seq_len <= n * tok

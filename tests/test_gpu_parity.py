@@ -1,0 +1,289 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars (max |gpu - ref| / max |ref| per output tensor):
+  fp32 workloads 1e-4; bf16 2e-2; fp8 cache 2e-2 against the oracle on the dequantized
+  cache and 6e-2 against the oracle on the latent before quantization.
+Integer work (block-table lookup, fp8 code table) is bit-exact.
+
+Every case prints its name, seed and shape before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from mla_latent_kv_lat_amd import capi, configs, synth
+from mla_latent_kv_lat_amd.runner import DeviceWorkload, to_device, to_host_f64
+from conftest import decoded, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 2e-2}
+TOL_FP8_PREQUANT = 6e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    capi.library()  # fails loudly when libmla.so is missing
+    return "cuda"
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+
+
+def run(inp, split_tokens=0, stages=True):
+    """Run the three calls; return host float64 arrays of every output."""
+    w = DeviceWorkload(inp, split_tokens=split_tokens)
+    w.step()
+    torch.cuda.synchronize()
+    res = {"q_lat": to_host_f64(w.q_lat), "o_lat": to_host_f64(w.o_lat),
+           "lse": to_host_f64(w.lse), "out": to_host_f64(w.out), "plan": w.plan}
+    return res, w
+
+
+def oracle_full(d, batches=None):
+    sl = slice(None) if batches is None else batches
+    return O.mla_absorbed(d["q_nope"][sl], d["q_rope"][sl], d["c_kv"][sl], d["k_rope"][sl],
+                          d["w_uk"], d["w_uv"], d["seq_lens"][sl], d["scale"])
+
+
+def check_all(res, ref, tol, batches=None, what=""):
+    sl = slice(None) if batches is None else batches
+    errs = {k: max_rel_err(res[k][sl], ref[k]) for k in ("q_lat", "o_lat", "out")}
+    fin = np.isfinite(ref["lse"])
+    assert np.array_equal(np.isneginf(res["lse"][sl]), np.isneginf(ref["lse"])), what
+    errs["lse"] = max_rel_err(res["lse"][sl][fin], ref["lse"][fin]) if fin.any() else 0.0
+    print(f"  {what} max rel err: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= tol, (what, k, v)
+    return errs
+
+
+# ------------------------------------------------------------------ utilities ----
+
+def test_fp8_code_table_matches_format_definition():
+    say("fp8 table")
+    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    capi.mla_fp8_e4m3_table(out)
+    got = out.cpu().numpy().astype(np.float64)
+    ref = O.decode_e4m3fn(np.arange(256, dtype=np.uint8))
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(got[ok], ref[ok])
+
+
+@pytest.mark.parametrize("block_size", [64, 16, 7])
+def test_gather_pages_bit_exact(block_size):
+    cfg = configs.PAGED_VARLEN.with_(batch=5, seq_len=700, len_min=1, block_size=block_size, cfg_id=20)
+    say("gather", block_size, cfg)
+    inp = synth.make_inputs(cfg, 3)
+    pool = to_device(inp.c_kv, "bf16", "cuda")
+    table = to_device(inp.block_table, "i32", "cuda")
+    lens = to_device(inp.seq_lens, "i32", "cuda")
+    dst = torch.zeros(cfg.batch, cfg.seq_len, cfg.d_latent, dtype=torch.bfloat16, device="cuda")
+    capi.mla_gather_pages(pool, table, lens, cfg.seq_len, dst)
+    torch.cuda.synchronize()
+    got = dst.cpu().view(torch.int16).numpy().view(np.uint16)
+    ref = O.gather_pages(inp.c_kv, inp.block_table, inp.seq_lens, cfg.seq_len, fill=0)
+    assert np.array_equal(got, ref)
+
+
+# ------------------------------------------------------------- tiny (fp32) ----
+
+def test_tiny_config_end_to_end():
+    cfg = configs.TINY
+    say("tiny", cfg)
+    inp = synth.make_inputs(cfg, 0)
+    d = decoded(inp)
+    res, _ = run(inp)
+    ref = oracle_full(d)
+    check_all(res, ref, TOL["f32"], what="tiny")
+    ex, _ = O.mla_explicit(d["q_nope"], d["q_rope"], d["c_kv"], d["k_rope"], d["w_uk"], d["w_uv"],
+                           d["seq_lens"], d["scale"])
+    assert max_rel_err(res["out"], ex) <= TOL["f32"]
+
+
+@pytest.mark.parametrize("split_tokens", [0, 32, 100])
+def test_tiny_config_splits_and_ragged(split_tokens):
+    cfg = configs.TINY.with_(batch=3, q_len=2, cfg_id=21)
+    say("tiny ragged", split_tokens, cfg)
+    inp = synth.make_inputs(cfg, 1, lengths=np.array([128, 37, 2], np.int32), poison_tail=True)
+    d = decoded(inp)
+    res, _ = run(inp, split_tokens=split_tokens)
+    check_all(res, oracle_full(d), TOL["f32"], what=f"tiny split={split_tokens}")
+
+
+# ------------------------------------------------------- stage-by-stage bf16 ----
+
+def test_absorb_q_and_out_v2_shapes():
+    cfg = configs.V2_DECODE
+    say("absorb stages", cfg)
+    inp = synth.make_inputs(cfg.with_(seq_len=64), 0)
+    d = decoded(inp)
+    w = DeviceWorkload(inp)
+    w.absorb_q()
+    # Output side on its own: a latent output drawn as a stand-alone stored input.
+    o_lat_bits = synth.make_stage_input(cfg, 0, "o_lat", (cfg.batch, 1, cfg.n_heads, cfg.d_latent), 0.1)
+    o_lat = to_device(o_lat_bits, "bf16", "cuda")
+    w.absorb_out(o_lat=o_lat)
+    torch.cuda.synchronize()
+    ref_q = O.absorb_query(d["q_nope"], d["w_uk"])
+    e_q = max_rel_err(to_host_f64(w.q_lat), ref_q)
+    ref_o = O.absorb_output(O.decode_bf16(o_lat_bits), d["w_uv"])
+    e_o = max_rel_err(to_host_f64(w.out), ref_o)
+    print(f"  absorb_q {e_q:.2e} absorb_out {e_o:.2e}")
+    assert e_q <= TOL["bf16"] and e_o <= TOL["bf16"]
+
+
+def decode_stage_case(cfg, seed, lengths, split_tokens, poison=True, q_gain=1.0):
+    """mla_decode alone: both sides read the same stored q_lat (the oracle's q_lat rounded
+    to the stored dtype), so only the attention stage is compared."""
+    inp = synth.make_inputs(cfg, seed, lengths=np.array(lengths, np.int32), poison_tail=poison,
+                            q_gain=q_gain)
+    d = decoded(inp)
+    q_lat = O.absorb_query(d["q_nope"], d["w_uk"])
+    q_bits = synth.store(q_lat.astype(np.float32), cfg.act_dtype)
+    q_dec = O.decode(q_bits, cfg.act_dtype)
+    w = DeviceWorkload(inp, split_tokens=split_tokens)
+    w.decode(q_lat=to_device(q_bits, cfg.act_dtype, "cuda"))
+    torch.cuda.synchronize()
+    o_ref, lse_ref = O.latent_attention(q_dec, d["q_rope"], d["c_kv"], d["k_rope"], d["seq_lens"],
+                                        d["scale"])
+    o_got, lse_got = to_host_f64(w.o_lat), to_host_f64(w.lse)
+    return o_got, lse_got, o_ref, lse_ref, inp, d, w
+
+
+@pytest.mark.parametrize("split_tokens", [0, 64, 192, 512])
+def test_decode_stage_bf16_ragged(split_tokens):
+    cfg = configs.V2_DECODE.with_(batch=3, seq_len=1000, cfg_id=22)
+    say("decode bf16 ragged", split_tokens, cfg)
+    o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [1000, 77, 1], split_tokens)
+    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
+    print(f"  o_lat {e_o:.2e} lse {e_l:.2e}")
+    assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
+
+
+def test_decode_stage_peaked_scores():
+    cfg = configs.V2_DECODE.with_(batch=2, seq_len=700, cfg_id=23)
+    say("decode peaked", cfg)
+    o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [700, 333], 128, q_gain=4.0)
+    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
+    print(f"  o_lat {e_o:.2e} lse {e_l:.2e}")
+    assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("split_tokens", [0, 128])
+def test_decode_stage_fp8_causal(split_tokens):
+    cfg = configs.SPEC_FP8.with_(batch=3, seq_len=700, cfg_id=24)
+    say("decode fp8 causal", split_tokens, cfg)
+    o, l, o_ref, l_ref, inp, d, _ = decode_stage_case(cfg, 0, [700, 130, 4], split_tokens)
+    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
+    print(f"  o_lat {e_o:.2e} lse {e_l:.2e} (dequantized cache)")
+    assert e_o <= TOL["fp8"] and e_l <= TOL["fp8"]
+    # Against the latent before quantization (kernel + quantization error).
+    pre = np.where(np.isfinite(inp.c_kv_prequant), inp.c_kv_prequant, 0).astype(np.float64)
+    q_dec = O.decode(synth.store(O.absorb_query(d["q_nope"], d["w_uk"]).astype(np.float32), "bf16"), "bf16")
+    o_pre, _ = O.latent_attention(q_dec, d["q_rope"], pre, d["k_rope"], d["seq_lens"], d["scale"])
+    e_pre = max_rel_err(o, o_pre)
+    print(f"  o_lat vs pre-quantization latent {e_pre:.2e}")
+    assert e_pre <= TOL_FP8_PREQUANT
+
+
+def test_causal_equals_independent_single_query_decodes():
+    cfg = configs.SPEC_FP8.with_(batch=2, seq_len=300, cfg_id=25)
+    say("causal vs single", cfg)
+    lengths = np.array([300, 41], np.int32)
+    inp = synth.make_inputs(cfg, 0, lengths=lengths)
+    res, _ = run(inp, split_tokens=64)
+    for i in range(cfg.q_len):
+        one = synth.make_inputs(cfg.with_(q_len=1), 0, lengths=lengths - cfg.q_len + 1 + i)
+        # Same cache and weights; the single query is query i of the causal block.
+        one.q_nope = np.ascontiguousarray(inp.q_nope[:, i:i + 1])
+        one.q_rope = np.ascontiguousarray(inp.q_rope[:, i:i + 1])
+        one.c_kv, one.k_rope, one.kv_scale = inp.c_kv, inp.k_rope, inp.kv_scale
+        one.w_uk, one.w_uv = inp.w_uk, inp.w_uv
+        r1, _ = run(one, split_tokens=64)
+        e = max_rel_err(r1["out"][:, 0], res["out"][:, i])
+        print(f"  query {i}: {e:.2e}")
+        assert e <= 1e-2
+
+
+# -------------------------------------------------------------- paged cache ----
+
+def test_paged_equals_contiguous_bitwise():
+    cfg = configs.PAGED_VARLEN.with_(batch=6, seq_len=1500, len_min=1, cfg_id=26)
+    say("paged vs contiguous", cfg)
+    inp = synth.make_inputs(cfg, 0, poison_tail=True)
+    res_p, wp = run(inp, split_tokens=256)
+    # Contiguous copy of the same rows (gathered on the host from the stored pool).
+    flat = synth.Inputs(**{**inp.__dict__})
+    flat.cfg = cfg.with_(paged=False)
+    flat.c_kv = O.gather_pages(inp.c_kv, inp.block_table, inp.seq_lens, cfg.seq_len, fill=synth.BF16_NAN_BITS)
+    flat.k_rope = O.gather_pages(inp.k_rope, inp.block_table, inp.seq_lens, cfg.seq_len, fill=synth.BF16_NAN_BITS)
+    flat.block_table = None
+    res_c, _ = run(flat, split_tokens=256)
+    for k in ("o_lat", "lse", "out"):
+        assert np.array_equal(res_p[k], res_c[k], equal_nan=True), k
+    d = decoded(inp)
+    check_all(res_p, oracle_full(d), TOL["bf16"], what="paged")
+
+
+# ------------------------------------------------ full-size, sampled oracle ----
+
+FULL = [configs.TINY, configs.V2_DECODE, configs.PAGED_VARLEN, configs.LONG_CONTEXT, configs.SPEC_FP8]
+SAMPLE = {configs.V2_DECODE.name: [0, 17, 31], configs.PAGED_VARLEN.name: [0, 33, 63],
+          configs.LONG_CONTEXT.name: [2], configs.SPEC_FP8.name: [5, 127]}
+
+
+@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
+def test_full_size_sampled(cfg):
+    say("full size", cfg.name)
+    inp = synth.make_inputs(cfg, 0)
+    res, w = run(inp)
+    print(f"  plan (splits, tokens) = {res['plan']}", flush=True)
+    for k in ("o_lat", "out", "lse"):
+        assert np.all(np.isfinite(res[k])), k
+    batches = SAMPLE.get(cfg.name)
+    d = decoded_batches(inp, batches)
+    ref = oracle_full(d)
+    sl = slice(None) if batches is None else batches
+    errs = check_all(res, ref, TOL[cfg.kv_dtype], batches=sl, what=cfg.name)
+    del w
+
+
+def decoded_batches(inp, batches):
+    """Decode only the sampled sequences (keeps the oracle's work and memory small)."""
+    if batches is None:
+        return decoded(inp)
+    sub = synth.Inputs(**{**inp.__dict__})
+    sub.q_nope, sub.q_rope = inp.q_nope[batches], inp.q_rope[batches]
+    sub.seq_lens = inp.seq_lens[batches]
+    if inp.cfg.paged:
+        sub.block_table = inp.block_table[batches]
+    else:
+        sub.c_kv, sub.k_rope = inp.c_kv[batches], inp.k_rope[batches]
+        if inp.kv_scale is not None:
+            sub.kv_scale = inp.kv_scale[batches]
+    return decoded(sub)
+
+
+def test_run_to_run_bitwise_deterministic():
+    cfg = configs.V2_DECODE.with_(batch=4, seq_len=2048, cfg_id=27)
+    say("determinism", cfg)
+    inp = synth.make_inputs(cfg, 0)
+    r1, w = run(inp, split_tokens=256)
+    w.step()
+    torch.cuda.synchronize()
+    for k, t in (("o_lat", w.o_lat), ("lse", w.lse), ("out", w.out)):
+        assert np.array_equal(r1[k], to_host_f64(t)), k
+
+
+def test_empty_and_short_sequences():
+    cfg = configs.V2_DECODE.with_(batch=3, seq_len=256, cfg_id=28)
+    say("empty sequence", cfg)
+    o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [0, 1, 256], 64)
+    assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
+    assert max_rel_err(o, o_ref) <= TOL["bf16"]
