@@ -163,7 +163,8 @@ mla_status mla_gather_pages(const void* pool, int32_t n_blocks, int32_t block_si
                             const int32_t* seq_lens, int32_t max_seq_len, void* dst, void* stream);
 
 /* Decode every e4m3fn code on the device exactly as the fp8 decode kernels do:
- * out[k] = value of code k, k = 0..255 (float32 [256]). */
+ * out[k] = value of code k as the general kernels convert it, out[256 + k] as the
+ * matrix-core kernels convert it (to bf16), k = 0..255 (float32 [512]). */
 mla_status mla_fp8_e4m3_table(float* out, void* stream);
 
 /* Static description of a status code (never NULL). */

@@ -18,7 +18,6 @@ constexpr int kMaxLatent = 2048;      // general-kernel limits (query rows are s
 constexpr int kMaxRope = 512;
 constexpr int kMaxQLen = 8;
 constexpr int kMaxRows = 1 << 16;
-constexpr bool kMfmaDecodeReady = false;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -124,7 +123,7 @@ mla_status check_dims(const mla_dims* d) {
 }
 
 bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt) {
-  return kMfmaDecodeReady && q_dt == MLA_BF16 && (kv_dt == MLA_BF16 || kv_dt == MLA_FP8_E4M3) && d->d_latent == 512 &&
+  return q_dt == MLA_BF16 && (kv_dt == MLA_BF16 || kv_dt == MLA_FP8_E4M3) && d->d_latent == 512 &&
          d->d_rope == 64 && (d->q_len * d->n_heads) % 64 == 0;
 }
 

@@ -66,5 +66,6 @@ int launch_gather_pages(const void* pool, int32_t block_size, int64_t row_bytes,
                         const int32_t* table, int32_t B, int32_t max_blocks, const int32_t* seq_lens,
                         int32_t max_seq_len, void* dst, hipStream_t s);
 int launch_fp8_table(float* out, hipStream_t s);
+int launch_fp8_bf16_table(float* out, hipStream_t s);
 
 }  // namespace mla

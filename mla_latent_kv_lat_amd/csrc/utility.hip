@@ -34,7 +34,8 @@ int launch_gather_pages(const void* pool, int32_t block_size, int64_t row_bytes,
 
 int launch_fp8_table(float* out, hipStream_t s) {
   hipLaunchKernelGGL(fp8_table_kernel, dim3(1), dim3(256), 0, s, out);
-  return int(hipGetLastError());
+  const int err = int(hipGetLastError());
+  return err ? err : launch_fp8_bf16_table(out + 256, s);
 }
 
 }  // namespace mla

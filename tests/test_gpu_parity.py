@@ -65,14 +65,17 @@ def check_all(res, ref, tol, batches=None, what=""):
 # ------------------------------------------------------------------ utilities ----
 
 def test_fp8_code_table_matches_format_definition():
+    """Both device conversions (general kernels: to fp32; matrix-core kernels: to bf16)
+    decode every e4m3fn code exactly as the format defines it."""
     say("fp8 table")
-    out = torch.empty(256, dtype=torch.float32, device="cuda")
+    out = torch.empty(512, dtype=torch.float32, device="cuda")
     capi.mla_fp8_e4m3_table(out)
-    got = out.cpu().numpy().astype(np.float64)
     ref = O.decode_e4m3fn(np.arange(256, dtype=np.uint8))
-    assert np.array_equal(np.isnan(got), np.isnan(ref))
-    ok = ~np.isnan(ref)
-    assert np.array_equal(got[ok], ref[ok])
+    for half in (0, 1):
+        got = out[256 * half:256 * (half + 1)].cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), half
+        ok = ~np.isnan(ref)
+        assert np.array_equal(got[ok], ref[ok]), half
 
 
 @pytest.mark.parametrize("block_size", [64, 16, 7])
@@ -156,9 +159,10 @@ def decode_stage_case(cfg, seed, lengths, split_tokens, poison=True, q_gain=1.0)
     return o_got, lse_got, o_ref, lse_ref, inp, d, w
 
 
+@pytest.mark.parametrize("n_heads", [128, 8], ids=["mfma", "general"])
 @pytest.mark.parametrize("split_tokens", [0, 64, 192, 512])
-def test_decode_stage_bf16_ragged(split_tokens):
-    cfg = configs.V2_DECODE.with_(batch=3, seq_len=1000, cfg_id=22)
+def test_decode_stage_bf16_ragged(split_tokens, n_heads):
+    cfg = configs.V2_DECODE.with_(batch=3, seq_len=1000, cfg_id=22, n_heads=n_heads)
     say("decode bf16 ragged", split_tokens, cfg)
     o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [1000, 77, 1], split_tokens)
     e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
@@ -175,9 +179,10 @@ def test_decode_stage_peaked_scores():
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("n_heads", [128, 8], ids=["mfma", "general"])
 @pytest.mark.parametrize("split_tokens", [0, 128])
-def test_decode_stage_fp8_causal(split_tokens):
-    cfg = configs.SPEC_FP8.with_(batch=3, seq_len=700, cfg_id=24)
+def test_decode_stage_fp8_causal(split_tokens, n_heads):
+    cfg = configs.SPEC_FP8.with_(batch=3, seq_len=700, cfg_id=24, n_heads=n_heads)
     say("decode fp8 causal", split_tokens, cfg)
     o, l, o_ref, l_ref, inp, d, _ = decode_stage_case(cfg, 0, [700, 130, 4], split_tokens)
     e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
