@@ -1,0 +1,129 @@
+// Vector types and LDS helpers shared by the matrix-core (MFMA) kernels.
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 used throughout (lane l, g = l / 16):
+//   A[m][k]: lane holds A[l % 16][8g .. 8g + 7];  B[k][n]: lane holds B[8g .. 8g + 7][l % 16];
+//   D[m][n]: lane holds D[4g .. 4g + 3][l % 16].
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4r + q supplies the address of
+// four consecutive 16-bit elements (row r, columns 4q .. 4q + 3 of a 4 x 16 block) and
+// lane j receives column j (rows 0 .. 3).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace mla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Chunk swizzle for LDS tiles whose rows are 128 bytes (8 chunks of 16 bytes, two rows
+// per 64-bank cycle).  Applied as chunk ^ swz128(row): the 16 consecutive rows written by
+// one 16-byte-per-lane store, and the 8 rows of each half of a transposed read (rows
+// 8g + r and 8g + 4 + r), fall in distinct banks.
+__device__ __forceinline__ int swz128(int row) {
+  return (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2) | ((row >> 2) & 1);
+}
+
+// Chunk swizzle for LDS tiles whose rows are 256 bytes (16 chunks of 16 bytes, one row
+// per 64-bank cycle).  Applied as chunk ^ swz256(row): bijective on the low 4 row bits, so
+// the 16 rows of one 16-byte-per-lane store hit distinct banks; and (swz256 >> 1) is
+// distinct on each half of a transposed read (rows 8g + r and 8g + 4 + r, g in {0, 1} or
+// {2, 3}), so those 8 rows' 32-byte column pairs hit distinct banks as well.
+__device__ __forceinline__ int swz256(int row) {
+  return ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
+}
+
+// Transposed read of 4 bf16 (see the layout note above) from LDS.
+__device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                       (__attribute__((address_space(3))) s16x4*)(p)));
+}
+
+// A 16 x 32 (k x 16 columns) bf16 MFMA operand read transposed from a row-major LDS tile
+// with 128-byte rows (64 columns, swizzled by swz128): rows k0 .. k0 + 31, columns
+// c0 .. c0 + 15 (c0 a multiple of 16).  Lane l receives column c0 + l % 16, rows
+// k0 + 8g .. k0 + 8g + 7.
+__device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* tile, int k0, int c0, int lane) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int col = c0 + 4 * q;
+  const int k_lo = k0 + 8 * g + r, k_hi = k_lo + 4;
+  const u32x2 lo = lds_read_tr4(tile + k_lo * 64 + 8 * ((col >> 3) ^ swz128(k_lo)) + (col & 7));
+  const u32x2 hi = lds_read_tr4(tile + k_hi * 64 + 8 * ((col >> 3) ^ swz128(k_hi)) + (col & 7));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// As lds_operand_tr, for a tile with 256-byte rows (128 columns, swizzled by swz256).
+__device__ __forceinline__ bf16x8 lds_operand_tr256(const uint16_t* tile, int k0, int c0, int lane) {
+  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int col = c0 + 4 * q;
+  const int k_lo = k0 + 8 * g + r, k_hi = k_lo + 4;
+  const u32x2 lo = lds_read_tr4(tile + k_lo * 128 + 8 * ((col >> 3) ^ swz256(k_lo)) + (col & 7));
+  const u32x2 hi = lds_read_tr4(tile + k_hi * 128 + 8 * ((col >> 3) ^ swz256(k_hi)) + (col & 7));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// Two e4m3fn codes (low or high half-word of `w`) -> two bf16, exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+}
+
+// 8 codes (two dwords) -> 8 bf16 (four dwords).
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  u32x4 r;
+  r[0] = e4m3x2_to_bf16x2<false>(lo);
+  r[1] = e4m3x2_to_bf16x2<true>(lo);
+  r[2] = e4m3x2_to_bf16x2<false>(hi);
+  r[3] = e4m3x2_to_bf16x2<true>(hi);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
+         (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+}
+
+// Cross-lane swaps of gfx950, written as single inline instructions (register operands
+// only, no memory access).  v_permlane16_swap_b32 a, b exchanges the odd 16-lane rows of
+// a with the even rows of b, so with a = b = x every lane ends up holding {x, x from
+// lane ^ 16} in (a, b); v_permlane32_swap_b32 does the same for lane ^ 32.  The builtin
+// forms are not used: the compiler folds max(first result, second result) down to the
+// first result, dropping the partner lane.  The leading s_nop covers the two wait
+// states the instruction needs after a VALU write of its operands.
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+
+// Reductions over lanes {l, l ^ 16, l ^ 32, l ^ 48}.
+__device__ __forceinline__ float max_xor16_32(float x) {
+  float a = x, b = x;
+  permlane16_swap(a, b);
+  x = fmaxf(a, b);
+  a = x;
+  b = x;
+  permlane32_swap(a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float sum_xor16_32(float x) {
+  float a = x, b = x;
+  permlane16_swap(a, b);
+  x = a + b;
+  a = x;
+  b = x;
+  permlane32_swap(a, b);
+  return a + b;
+}
+
+}  // namespace mla
