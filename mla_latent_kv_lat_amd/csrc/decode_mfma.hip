@@ -12,7 +12,9 @@
 //
 // Work split.  A workgroup owns 64 query rows of one sequence and one split of its
 // context, walked in tiles of 32 tokens, with eight waves in two roles (one of each per
-// SIMD, so the matrix cores stay busy while the other role does LDS / VALU work):
+// SIMD, so the matrix cores stay busy while the other role does LDS / VALU work).  All
+// products use the 32 x 32 x 16 bf16 matrix instruction (tokens or output columns on one
+// side, 32 query rows on the other).
 //   * score waves 0-3: wave p owns latent columns [128p, 128p + 128) and RoPE dims
 //     [16p, 16p + 16).  It streams exactly that slice of every cache row from HBM into
 //     registers, two tiles ahead; computes partial scores (MFMA, cache slice as the A
@@ -27,10 +29,13 @@
 // tile n while output waves finish PV of tile n - 1.  Slices and probabilities are double
 // buffered in LDS.  The cache is read from HBM once per workgroup.
 //
-// Softmax runs in base-2 units (scores times softmax_scale * log2(e)); output waves skip
-// the accumulator rescale when no row's running max moved.  fp8 (OCP e4m3fn) caches are
+// Softmax runs in base-2 units (scores times softmax_scale * log2(e), exponentials by the
+// hardware base-2 exponential; results that would be denormal flush to 0) against a per-row
+// reference max that only moves when a tile exceeds it by more than kTau; output waves
+// skip the accumulator rescale whenever no row's reference moved.  fp8 (OCP e4m3fn) caches are
 // converted exactly to bf16 in registers; the per-token scale multiplies the latent part
-// of the score and the probability used in the PV product.
+// of the score and the probability used in the PV product (each score lane loads its
+// token's scale once per tile and shares it through LDS).
 #include "device_common.h"
 #include "mfma_common.h"
 #include "mla_internal.h"
@@ -40,57 +45,60 @@ namespace {
 
 constexpr int kDC = 512;
 constexpr int kDR = 64;
-constexpr int kRows = 64;               // query rows per workgroup
+constexpr int kRows = 64;               // query rows per workgroup (two 32-row blocks)
 constexpr int kTile = 32;               // tokens per tile
 constexpr int kThreads = 512;           // 4 score waves + 4 output waves
 constexpr int kCols = 128;              // latent columns per score wave / output wave
 constexpr int kRopeW = 16;              // RoPE dims per score wave
 constexpr int kSPitch = kTile + 4;      // floats per row of a partial-score tile
 constexpr int kPPitch = kTile + 8;      // bf16 per row of the probability tile
-constexpr int kSplitA = 3;              // output column blocks done in half A (of 8)
+constexpr int kSplitA = 1;              // output column blocks (of 4) done in half A
+// A row's reference max (the value its probabilities are taken relative to) only moves
+// when a tile's max exceeds it by more than this many base-2 units, so probabilities stay
+// below 2^kTau and the output waves almost never have to rescale their accumulators.
+// The result is the same up to rounding: numerator and denominator share the reference.
+constexpr float kTau = 8.f;
 
 struct alignas(16) Smem {
   float spart[4][kRows][kSPitch];       // partial S^T of each score wave, [row][tok]
-  uint16_t v[2][4][kTile][kCols];       // cache slices (double buffered), swz256 chunks
+  uint16_t v[2][4][kTile][kCols];       // cache slices (double buffered), swz32 chunks
   uint16_t p[2][kRows][kPPitch];        // probabilities (double buffered), [row][tok]
+  float ts[2][4][kTile];                // fp8 per-token scales, one copy per score wave
   float alpha[2][kRows];                // per-row rescale factor of each buffered tile
   float lsum[kRows];
 };
 
-// Column layout of one score lane's k-slices: for k-step s (0..3) of its 128 latent
-// columns, lane group g (= lane / 16) holds 8 consecutive columns starting here.  The A
+// Column layout of one score lane's k-slices: for k-step s (0..7) of its 128 latent
+// columns, lane half h (= lane / 32) holds 8 consecutive columns starting here.  The A
 // (cache) and B (query) operands use the same map; each lane gets 16 contiguous columns
 // per pair of k-steps (one 16-byte load of fp8 codes).
-__device__ __forceinline__ int kcol(int s, int g) { return 64 * (s >> 1) + 16 * g + 8 * (s & 1); }
+__device__ __forceinline__ int kcol(int s, int h) { return 32 * (s >> 1) + 16 * h + 8 * (s & 1); }
 
 template <bool FP8>
 struct TileRegs;
 
 template <>
 struct TileRegs<false> {
-  u32x4 lat[2][4];   // [token block][k-step]: 8 bf16 of one token
-  u32x2 rope[2];     // [token block]: 4 bf16 of one token
+  u32x4 lat[8];      // [k-step]: 8 bf16 of this lane's token
+  u32x4 rope;        // 8 bf16 of this lane's token
 };
 
 template <>
 struct TileRegs<true> {
-  u32x4 lat[2][2];   // [token block][pair of k-steps]: 16 fp8 codes of one token
-  u32x2 rope[2];
-  float ts1[2][4];   // scales of tokens 16 blk + 4g + i (phase-1 output layout)
-  float ts2[8];      // scales of tokens 8g + e (softmax layout)
+  u32x4 lat[4];      // [pair of k-steps]: 16 fp8 codes of this lane's token
+  u32x4 rope;
+  float ts;          // this lane's token scale
 };
 
-__device__ __forceinline__ u32x4 a_operand(const TileRegs<false>& t, int blk, int s) {
-  return t.lat[blk][s];
-}
+__device__ __forceinline__ u32x4 a_operand(const TileRegs<false>& t, int s) { return t.lat[s]; }
 
-__device__ __forceinline__ u32x4 a_operand(const TileRegs<true>& t, int blk, int s) {
-  const u32x4 w = t.lat[blk][s >> 1];
+__device__ __forceinline__ u32x4 a_operand(const TileRegs<true>& t, int s) {
+  const u32x4 w = t.lat[s >> 1];
   return (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
 }
 
 struct Ctx {
-  int b, lane, g, m, w;
+  int b, lane, n, h, w;
   int t_hi;
   const int32_t* table;
   int max_blocks, bs;
@@ -101,61 +109,87 @@ struct Ctx {
 // (block_size a multiple of 32: one wave-uniform table entry per tile); paged general.
 enum : int { kContig = 0, kPagedTile = 1, kPagedAny = 2 };
 
-// Cache rows of the tokens of one tile.  Token indices are first clamped to the split's
-// last valid token, so every lane always issues the same loads from valid rows: tokens
-// past the split end get that row's (finite) data, and the softmax gives them weight 0.
-// Issuing the same loads on every path keeps the compiler's wait counts exact, so the
-// loads of the next tiles stay in flight while this one is computed.
-template <int PK>
-struct TileRows {
-  int64_t base;
-  int blk_t0;
-  __device__ __forceinline__ TileRows(const Ctx& c, int t0) {
-    if constexpr (PK == kContig) {
-      base = int64_t(c.b) * c.T;
-      blk_t0 = 0;
-    } else if constexpr (PK == kPagedTile) {
-      const int blk = min(t0, c.t_hi - 1) / c.bs;
-      base = int64_t(c.table[int64_t(c.b) * c.max_blocks + blk]) * c.bs;
-      blk_t0 = blk * c.bs;
-    } else {
-      base = 0;
-      blk_t0 = 0;
-    }
-  }
-  __device__ __forceinline__ int64_t row(const Ctx& c, int t) const {
-    const int tc = min(t, c.t_hi - 1);
-    if constexpr (PK == kContig) return base + tc;
-    if constexpr (PK == kPagedTile) return base + (tc - blk_t0);
-    return int64_t(c.table[int64_t(c.b) * c.max_blocks + tc / c.bs]) * c.bs + tc % c.bs;
-  }
-};
+// Buffer resource (gfx9 raw buffer: stride 0, range-checked in bytes) over `bytes` bytes.
+// A load whose offset is past the range returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
 
-// Issue the global loads of one tile (tokens t0 .. t0 + 31) for this score lane.
+__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ float buf_ld4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+// Cache row of a token (general paged layout).  Token indices are first clamped to the
+// split's last valid token, so every lane always issues the same loads from valid rows.
+__device__ __forceinline__ int64_t any_row(const Ctx& c, int t) {
+  const int tc = min(t, c.t_hi - 1);
+  return int64_t(c.table[int64_t(c.b) * c.max_blocks + tc / c.bs]) * c.bs + tc % c.bs;
+}
+
+// Issue the loads of one tile (tokens t0 .. t0 + 31; this lane's token is t0 + n).  Every
+// lane issues the same loads on every path (tokens past the split end read zeros, or the
+// split's last row in the general paged layout; the softmax gives them weight 0), which
+// keeps the compiler's wait counts exact, so the loads of the next tiles stay in flight
+// while this one is computed.  Contiguous and block-aligned paged caches use buffer
+// resources whose range ends at the last valid row of the sequence (or of the tile's
+// block), so rows past the end are never read.
 template <bool FP8, int PK>
 __device__ __forceinline__ void load_tile(TileRegs<FP8>& r, const Ctx& c, const DecodeArgs& a, int t0) {
-  const TileRows<PK> rows(c, t0);
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    const int64_t row = rows.row(c, t0 + 16 * blk + c.m);
+  constexpr uint32_t kLatBytes = kDC * (FP8 ? 1 : 2);
+  constexpr uint32_t kRopeBytes = kDR * 2;
+  const char* lat_base;
+  const char* rope_base;
+  const char* sc_base = nullptr;
+  uint32_t nrows, row0;  // rows addressable from the bases; row of token t0 (may be >= nrows)
+  if constexpr (PK == kContig) {
+    const int64_t seq_row = int64_t(c.b) * c.T;
+    lat_base = static_cast<const char*>(a.c_kv) + seq_row * kLatBytes;
+    rope_base = static_cast<const char*>(a.k_rope) + seq_row * kRopeBytes;
+    if constexpr (FP8) sc_base = reinterpret_cast<const char*>(a.kv_scale + seq_row);
+    nrows = uint32_t(c.t_hi);
+    row0 = uint32_t(t0);
+  } else if constexpr (PK == kPagedTile) {
+    const int blk = min(t0, c.t_hi - 1) / c.bs;  // the tile lies inside this block
+    const int blk_t0 = blk * c.bs;
+    const int64_t pool_row = int64_t(c.table[int64_t(c.b) * c.max_blocks + blk]) * c.bs;
+    lat_base = static_cast<const char*>(a.c_kv) + pool_row * kLatBytes;
+    rope_base = static_cast<const char*>(a.k_rope) + pool_row * kRopeBytes;
+    if constexpr (FP8) sc_base = reinterpret_cast<const char*>(a.kv_scale + pool_row);
+    nrows = uint32_t(min(c.bs, c.t_hi - blk_t0));
+    row0 = uint32_t(t0 - blk_t0);
+  }
+  if constexpr (PK == kContig || PK == kPagedTile) {
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lat_base, nrows * kLatBytes);
+    const __amdgpu_buffer_rsrc_t rr = make_rsrc(rope_base, nrows * kRopeBytes);
+    const uint32_t row = row0 + uint32_t(c.n);
     if constexpr (FP8) {
-      const uint8_t* base = static_cast<const uint8_t*>(a.c_kv) + row * kDC + kCols * c.w + 16 * c.g;
+      const uint32_t off = row * kLatBytes + kCols * c.w + 16 * c.h;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) r.lat[blk][h] = ld16(base + 64 * h);
+      for (int t = 0; t < 4; ++t) r.lat[t] = buf_ld16(rl, off + 32 * t);
+      r.ts = buf_ld4f(make_rsrc(sc_base, nrows * 4), row * 4);
+    } else {
+      const uint32_t off = row * kLatBytes + 2 * kCols * c.w;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) r.lat[s] = buf_ld16(rl, off + 2 * kcol(s, c.h));
+    }
+    r.rope = buf_ld16(rr, row * kRopeBytes + 2 * (kRopeW * c.w + 8 * c.h));
+  } else {
+    const int64_t row = any_row(c, t0 + c.n);
+    if constexpr (FP8) {
+      const uint8_t* base = static_cast<const uint8_t*>(a.c_kv) + row * kDC + kCols * c.w + 16 * c.h;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r.lat[t] = ld16(base + 32 * t);
+      r.ts = a.kv_scale[row];
     } else {
       const uint16_t* base = static_cast<const uint16_t*>(a.c_kv) + row * kDC + kCols * c.w;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) r.lat[blk][s] = ld16(base + kcol(s, c.g));
+      for (int s = 0; s < 8; ++s) r.lat[s] = ld16(base + kcol(s, c.h));
     }
-    r.rope[blk] = ld8(static_cast<const uint16_t*>(a.k_rope) + row * kDR + kRopeW * c.w + 4 * c.g);
-  }
-  if constexpr (FP8) {
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r.ts1[blk][i] = a.kv_scale[rows.row(c, t0 + 16 * blk + 4 * c.g + i)];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) r.ts2[e] = a.kv_scale[rows.row(c, t0 + 8 * c.g + e)];
+    r.rope = ld16(static_cast<const uint16_t*>(a.k_rope) + row * kDR + kRopeW * c.w + 8 * c.h);
   }
 }
 
@@ -176,9 +210,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
   Ctx c;
   c.b = b;
   c.lane = threadIdx.x & 63;
+  c.n = c.lane & 31;
+  c.h = c.lane >> 5;
   c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  c.g = c.lane >> 4;
-  c.m = c.lane & 15;
   c.table = a.block_table;
   c.max_blocks = a.max_blocks;
   c.bs = a.block_size;
@@ -196,102 +230,121 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
 
   if (c.w < 4) {
     // ================================ score waves ===================================
-    bf16x8 qb[4][4];
-    bf16x4 qrb[4];
+    // Query operands (B of phase 1): rows r0 + 32 rb2 + n, this wave's column slice.
+    bf16x8 qb[2][8];
+    bf16x8 qrb[2];
     {
       const uint16_t* ql = static_cast<const uint16_t*>(a.q_lat);
       const uint16_t* qr = static_cast<const uint16_t*>(a.q_rope);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t row = int64_t(b) * rows + r0 + 16 * j + c.m;
+      for (int rb2 = 0; rb2 < 2; ++rb2) {
+        const int64_t row = int64_t(b) * rows + r0 + 32 * rb2 + c.n;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-          qb[j][s] = __builtin_bit_cast(bf16x8, ld16(ql + row * kDC + kCols * c.w + kcol(s, c.g)));
-        qrb[j] = __builtin_bit_cast(bf16x4, ld8(qr + row * kDR + kRopeW * c.w + 4 * c.g));
+        for (int s = 0; s < 8; ++s)
+          qb[rb2][s] = __builtin_bit_cast(bf16x8, ld16(ql + row * kDC + kCols * c.w + kcol(s, c.h)));
+        qrb[rb2] = __builtin_bit_cast(bf16x8, ld16(qr + row * kDR + kRopeW * c.w + 8 * c.h));
       }
     }
-    // Softmax ownership: row 16w + m, tokens 8g .. 8g + 7 of each tile.
-    const int srow = 16 * c.w + c.m;
+    // Softmax ownership: row 16w + (lane % 16), tokens 8g .. 8g + 7 (g = lane / 16).
+    const int g = c.lane >> 4;
+    const int srow = 16 * c.w + (c.lane & 15);
     const int iq = (r0 + srow) / a.H;
     const int vis = min(max(L - a.sq + iq + 1, 0), L);  // tokens this query row may see
     const int lim = min(vis, c.t_hi);
+    // Smallest limit over this wave's rows (its first row has the smallest query index):
+    // tiles entirely below it need no masking.
+    const int iq_w = (r0 + 16 * c.w) / a.H;
+    const int lim_w = min(min(max(L - a.sq + iq_w + 1, 0), L), c.t_hi);
     float m_run = -INFINITY, l_run = 0.f;
 
     // Half A (phase 1 of tile n into buffer n % 2) and half B (its softmax).
     auto step = [&](TileRegs<FP8>& tr, int n) {
       const int t0 = t_lo + n * kTile;
       const int buf = n & 1;
+      f32x16 sacc[2];
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        f32x4 sacc[4];
+      for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) sacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int tok = 16 * blk + c.m;
+        for (int e = 0; e < 16; ++e) sacc[rb2][e] = 0.f;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const u32x4 araw = a_operand(tr, blk, s);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, araw);
+      for (int s = 0; s < 8; ++s) {
+        const u32x4 araw = a_operand(tr, s);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, araw);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            sacc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, qb[j][s], sacc[j], 0, 0, 0);
-          const int ch = (kcol(s, c.g) >> 3) ^ swz256(tok);
-          *reinterpret_cast<u32x4*>(&sm.v[buf][c.w][tok][8 * ch]) = araw;
-        }
-        if constexpr (FP8) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sacc[j][i] *= tr.ts1[blk][i];
-        }
-        const s16x4 ar = __builtin_bit_cast(s16x4, tr.rope[blk]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          sacc[j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ar, __builtin_bit_cast(s16x4, qrb[j]),
-                                                             sacc[j], 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          *reinterpret_cast<f32x4*>(&sm.spart[c.w][16 * j + c.m][16 * blk + 4 * c.g]) = sacc[j];
+        for (int rb2 = 0; rb2 < 2; ++rb2)
+          sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[rb2][s], sacc[rb2], 0, 0, 0);
+        // Keep the (bf16) slice for the output waves: 16 bytes of token n.
+        const int ch = (kcol(s, c.h) >> 3) ^ swz32(c.n);
+        *reinterpret_cast<u32x4*>(&sm.v[buf][c.w][c.n][8 * ch]) = araw;
       }
-      float ts2[8];
       if constexpr (FP8) {
+        // Share the token scales within the wave (LDS operations of one wave complete in
+        // order), then scale the latent part of tokens 8i + 4h + r.
+        if (c.h == 0) sm.ts[buf][c.w][c.n] = tr.ts;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ts2[e] = tr.ts2[e];
+        for (int i = 0; i < 4; ++i) {
+          const f32x4 tsv = *reinterpret_cast<const f32x4*>(&sm.ts[buf][c.w][8 * i + 4 * c.h]);
+#pragma unroll
+          for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sacc[rb2][4 * i + r] *= tsv[r];
+        }
       }
+      const bf16x8 ar = __builtin_bit_cast(bf16x8, tr.rope);
+#pragma unroll
+      for (int rb2 = 0; rb2 < 2; ++rb2)
+        sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qrb[rb2], sacc[rb2], 0, 0, 0);
+#pragma unroll
+      for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<f32x4*>(&sm.spart[c.w][32 * rb2 + c.n][8 * i + 4 * c.h]) =
+              f32x4{sacc[rb2][4 * i], sacc[rb2][4 * i + 1], sacc[rb2][4 * i + 2], sacc[rb2][4 * i + 3]};
       load_tile<FP8, PK>(tr, c, a, t0 + 2 * kTile);  // refill: two tiles ahead
       __syncthreads();
 
       // Online softmax of row srow over tokens 8g .. 8g + 7.
-      f32x4 s0 = *reinterpret_cast<const f32x4*>(&sm.spart[0][srow][8 * c.g]);
-      f32x4 s1 = *reinterpret_cast<const f32x4*>(&sm.spart[0][srow][8 * c.g + 4]);
+      f32x4 s0 = *reinterpret_cast<const f32x4*>(&sm.spart[0][srow][8 * g]);
+      f32x4 s1 = *reinterpret_cast<const f32x4*>(&sm.spart[0][srow][8 * g + 4]);
 #pragma unroll
       for (int q = 1; q < 4; ++q) {
-        s0 += *reinterpret_cast<const f32x4*>(&sm.spart[q][srow][8 * c.g]);
-        s1 += *reinterpret_cast<const f32x4*>(&sm.spart[q][srow][8 * c.g + 4]);
+        s0 += *reinterpret_cast<const f32x4*>(&sm.spart[q][srow][8 * g]);
+        s1 += *reinterpret_cast<const f32x4*>(&sm.spart[q][srow][8 * g + 4]);
       }
       float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      float tmax = -INFINITY;
+      if (t0 + kTile > lim_w) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sv[e] = t0 + 8 * c.g + e < lim ? sv[e] * a.scale_log2 : -INFINITY;
-        tmax = fmaxf(tmax, sv[e]);
+        for (int e = 0; e < 8; ++e)
+          if (t0 + 8 * g + e >= lim) sv[e] = -INFINITY;
       }
-      tmax = max_xor16_32(tmax);
-      const float m_new = fmaxf(m_run, tmax);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2f(m_run - m_use);
+      float tmax = sv[0];
+#pragma unroll
+      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
+      tmax = max_xor16_32(tmax) * a.scale_log2;  // scale > 0: max commutes with it
+      const bool grow = tmax > m_run + kTau;      // false while nothing is visible
+      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.f;
+      if (grow) m_run = tmax;
+      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
       float pr[8], psum = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        pr[e] = exp2f(sv[e] - m_use);
+        pr[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], a.scale_log2, neg_m));
         psum += pr[e];
-        if constexpr (FP8) pr[e] *= ts2[e];
+      }
+      if constexpr (FP8) {
+        const f32x4 t_lo4 = *reinterpret_cast<const f32x4*>(&sm.ts[buf][c.w][8 * g]);
+        const f32x4 t_hi4 = *reinterpret_cast<const f32x4*>(&sm.ts[buf][c.w][8 * g + 4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pr[e] *= t_lo4[e];
+          pr[4 + e] *= t_hi4[e];
+        }
       }
       l_run = l_run * alpha + psum;
-      m_run = m_new;
-      *reinterpret_cast<u32x4*>(&sm.p[buf][srow][8 * c.g]) =
+      *reinterpret_cast<u32x4*>(&sm.p[buf][srow][8 * g]) =
           u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
                 pack_bf16x2(pr[6], pr[7])};
-      if (c.g == 0) sm.alpha[buf][srow] = alpha;
+      if (g == 0) sm.alpha[buf][srow] = alpha;
       __syncthreads();
     };
 
@@ -312,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
     }
 
     const float l_tot = sum_xor16_32(l_run);
-    if (c.g == 0) {
+    if (g == 0) {
       sm.lsum[srow] = l_tot;
       const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
       if (single) {
@@ -325,70 +378,75 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
   } else {
     // ================================ output waves ==================================
     const int q = c.w - 4;
-    f32x4 oacc[8][4];  // O^T: cols 128q + 16cb + 4g + i, rows 16j + m
+    f32x16 oacc[4][2];  // O^T: cols 128q + 32cb + 8i + 4h + r, rows 32 rb2 + n
 #pragma unroll
-    for (int cb = 0; cb < 8; ++cb)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) oacc[cb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bf16x8 pb[4];
+      for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[cb][rb2][e] = 0.f;
+    bf16x8 pb[2][2];  // [row block][token half]
+
+    auto pv = [&](const uint16_t* vt, int cb) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 av = lds_operand_tr32(vt, 16 * ks, 32 * cb, c.lane);
+#pragma unroll
+        for (int rb2 = 0; rb2 < 2; ++rb2)
+          oacc[cb][rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rb2][ks], oacc[cb][rb2], 0, 0, 0);
+      }
+    };
 
     for (int n = 0; n < steps; ++n) {
       const int buf = (n - 1) & 1;
+      const uint16_t* vt = &sm.v[buf][q][0][0];
       if (n > 0) {
-        float al[4];
+        float al[2];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) al[j] = sm.alpha[buf][16 * j + c.m];
-        const bool moved = (al[0] != 1.f) | (al[1] != 1.f) | (al[2] != 1.f) | (al[3] != 1.f);
-        if (__any(moved)) {
+        for (int rb2 = 0; rb2 < 2; ++rb2) al[rb2] = sm.alpha[buf][32 * rb2 + c.n];
+        if (__any((al[0] != 1.f) | (al[1] != 1.f))) {
 #pragma unroll
-          for (int cb = 0; cb < 8; ++cb)
+          for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) oacc[cb][j] *= al[j];
+            for (int rb2 = 0; rb2 < 2; ++rb2) oacc[cb][rb2] *= al[rb2];
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          pb[j] = *reinterpret_cast<const bf16x8*>(&sm.p[buf][16 * j + c.m][8 * c.g]);
-        const uint16_t* vt = &sm.v[buf][q][0][0];
+        for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
-        for (int cb = 0; cb < kSplitA; ++cb) {
-          const bf16x8 av = lds_operand_tr256(vt, 0, 16 * cb, c.lane);
+          for (int ks = 0; ks < 2; ++ks)
+            pb[rb2][ks] = *reinterpret_cast<const bf16x8*>(&sm.p[buf][32 * rb2 + c.n][16 * ks + 8 * c.h]);
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            oacc[cb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[j], oacc[cb][j], 0, 0, 0);
-        }
+        for (int cb = 0; cb < kSplitA; ++cb) pv(vt, cb);
       }
       __syncthreads();
       if (n > 0) {
-        const uint16_t* vt = &sm.v[buf][q][0][0];
 #pragma unroll
-        for (int cb = kSplitA; cb < 8; ++cb) {
-          const bf16x8 av = lds_operand_tr256(vt, 0, 16 * cb, c.lane);
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            oacc[cb][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[j], oacc[cb][j], 0, 0, 0);
-        }
+        for (int cb = kSplitA; cb < 4; ++cb) pv(vt, cb);
       }
       __syncthreads();
     }
     __syncthreads();  // row sums published by the score waves
 
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lt = sm.lsum[16 * j + c.m];
+    for (int rb2 = 0; rb2 < 2; ++rb2) {
+      const float lt = sm.lsum[32 * rb2 + c.n];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int row = r0 + 16 * j + c.m;
-      if (single) {
-        uint16_t* o = static_cast<uint16_t*>(a.o_lat) + (int64_t(b) * rows + row) * kDC + kCols * q + 4 * c.g;
+      const int row = r0 + 32 * rb2 + c.n;
 #pragma unroll
-        for (int cb = 0; cb < 8; ++cb) {
-          const f32x4 v = oacc[cb][j] * inv;
-          *reinterpret_cast<u32x2*>(o + 16 * cb) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int col = kCols * q + 32 * cb + 8 * i + 4 * c.h;
+          const f32x4 v = f32x4{oacc[cb][rb2][4 * i], oacc[cb][rb2][4 * i + 1], oacc[cb][rb2][4 * i + 2],
+                                oacc[cb][rb2][4 * i + 3]} * inv;
+          if (single) {
+            uint16_t* o = static_cast<uint16_t*>(a.o_lat) + (int64_t(b) * rows + row) * kDC + col;
+            *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          } else {
+            float* o = a.part_o + ((int64_t(b) * num_splits + split) * rows + row) * kDC + col;
+            *reinterpret_cast<f32x4*>(o) = v;
+          }
         }
-      } else {
-        float* o = a.part_o + ((int64_t(b) * num_splits + split) * rows + row) * kDC + kCols * q + 4 * c.g;
-#pragma unroll
-        for (int cb = 0; cb < 8; ++cb) *reinterpret_cast<f32x4*>(o + 16 * cb) = oacc[cb][j] * inv;
-      }
     }
   }
 }

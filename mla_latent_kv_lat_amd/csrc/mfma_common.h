@@ -1,8 +1,14 @@
 // Vector types and LDS helpers shared by the matrix-core (MFMA) kernels.
 //
-// Operand layouts of v_mfma_f32_16x16x32_bf16 used throughout (lane l, g = l / 16):
-//   A[m][k]: lane holds A[l % 16][8g .. 8g + 7];  B[k][n]: lane holds B[8g .. 8g + 7][l % 16];
-//   D[m][n]: lane holds D[4g .. 4g + 3][l % 16].
+// Operand layouts (lane l):
+//   v_mfma_f32_16x16x32_bf16 (g = l / 16):
+//     A[m][k]: lane holds A[l % 16][8g .. 8g + 7];  B[k][n]: B[8g .. 8g + 7][l % 16];
+//     D[m][n]: lane holds D[4g .. 4g + 3][l % 16].
+//   v_mfma_f32_32x32x16_bf16 (h = l / 32):
+//     A[m][k]: lane holds A[l % 32][8h .. 8h + 7];  B[k][n]: B[8h .. 8h + 7][l % 32];
+//     D[m][n]: element 4i + r of lane l is D[8i + 4h + r][l % 32]   (i, r in 0..3).
+// On gfx950 the 32x32x16 form runs at twice the 16x16x32 form's throughput (the latter
+// takes as long per instruction for half the work), so dense loops use 32x32x16.
 // ds_read_b64_tr_b16: within each 16-lane group, lane 4r + q supplies the address of
 // four consecutive 16-bit elements (row r, columns 4q .. 4q + 3 of a 4 x 16 block) and
 // lane j receives column j (rows 0 .. 3).
@@ -17,6 +23,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -39,6 +46,12 @@ __device__ __forceinline__ int swz128(int row) {
 __device__ __forceinline__ int swz256(int row) {
   return ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
 }
+
+// Chunk swizzle for 256-byte-row tiles read with 32-column transposed reads (see
+// lds_operand_tr32): chunk ^ swz32(row).  Bijective on the low 4 row bits (16 rows of a
+// 16-byte-per-lane store hit distinct banks), and the 4 rows of each transposed-read pass
+// put their 64-byte column groups on distinct banks.
+__device__ __forceinline__ int swz32(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 
 // Transposed read of 4 bf16 (see the layout note above) from LDS.
 __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
@@ -66,6 +79,20 @@ __device__ __forceinline__ bf16x8 lds_operand_tr256(const uint16_t* tile, int k0
   const int k_lo = k0 + 8 * g + r, k_hi = k_lo + 4;
   const u32x2 lo = lds_read_tr4(tile + k_lo * 128 + 8 * ((col >> 3) ^ swz256(k_lo)) + (col & 7));
   const u32x2 hi = lds_read_tr4(tile + k_hi * 128 + 8 * ((col >> 3) ^ swz256(k_hi)) + (col & 7));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// A 32 x 16 (m = 32 columns, k = 16 rows) bf16 A operand of v_mfma_f32_32x32x16_bf16,
+// read transposed from a row-major LDS tile with 256-byte rows (128 columns) swizzled by
+// swz32: rows k0 .. k0 + 15, columns c0 .. c0 + 31 (c0 a multiple of 32).  Lane l receives
+// column c0 + l % 32 and rows k0 + 8h .. k0 + 8h + 7 (h = l / 32): 16-lane group G reads
+// columns c0 + 16 (G & 1) + (0..15) of rows k0 + 8 (G >> 1) + (0..7).
+__device__ __forceinline__ bf16x8 lds_operand_tr32(const uint16_t* tile, int k0, int c0, int lane) {
+  const int G = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int col = c0 + 16 * (G & 1) + 4 * q;
+  const int k_lo = k0 + 8 * (G >> 1) + r, k_hi = k_lo + 4;
+  const u32x2 lo = lds_read_tr4(tile + k_lo * 128 + 8 * ((col >> 3) ^ swz32(k_lo)) + (col & 7));
+  const u32x2 hi = lds_read_tr4(tile + k_hi * 128 + 8 * ((col >> 3) ^ swz32(k_hi)) + (col & 7));
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 

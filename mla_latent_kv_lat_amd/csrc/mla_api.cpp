@@ -122,9 +122,11 @@ mla_status check_dims(const mla_dims* d) {
   return MLA_OK;
 }
 
-bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt) {
+bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len) {
+  // The matrix-core kernel addresses one sequence's cache rows with 32-bit byte offsets.
+  const int64_t seq_bytes = int64_t(max_seq_len) * 512 * (kv_dt == MLA_FP8_E4M3 ? 1 : 2);
   return q_dt == MLA_BF16 && (kv_dt == MLA_BF16 || kv_dt == MLA_FP8_E4M3) && d->d_latent == 512 &&
-         d->d_rope == 64 && (d->q_len * d->n_heads) % 64 == 0;
+         d->d_rope == 64 && (d->q_len * d->n_heads) % 64 == 0 && seq_bytes < (int64_t(1) << 31);
 }
 
 mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
@@ -135,7 +137,7 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
   DecodePlan p{};
   p.rows = d->q_len * d->n_heads;
   int tile, min_chunk;
-  if (mfma_decode_eligible(d, q_dt, kv_dt)) {
+  if (mfma_decode_eligible(d, q_dt, kv_dt, max_seq_len)) {
     p.kernel = DecodeKernel::kMfma;
     p.row_block = 64;
     tile = 64;

@@ -54,7 +54,7 @@ struct DecodeArgs {
 mla_status check_dims(const mla_dims* d);
 mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
                        DecodePlan* plan);
-bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt);
+bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len);
 
 // Launchers (one per kernel file).  Return the hipError_t of the launch as int.
 int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
