@@ -50,7 +50,7 @@ __global__ __launch_bounds__(256) void absorb_general_kernel(const typename S::r
 
 int launch_absorb(const void* x, const void* w, void* y, mla_dtype dt, int32_t M, int32_t H,
                   int32_t K, int32_t N, hipStream_t s) {
-  if (absorb_mfma_supported(dt, K, N)) return launch_absorb_mfma(x, w, y, M, H, K, N, s);
+  if (absorb_mfma_supported(dt, M, K, N)) return launch_absorb_mfma(x, w, y, M, H, K, N, s);
   const dim3 grid((N + 255) / 256, H, (M + kMB - 1) / kMB);
   if (dt == MLA_F32)
     hipLaunchKernelGGL(absorb_general_kernel<F32>, grid, dim3(256), 0, s,

@@ -3,8 +3,8 @@
 // query, with W = W_UV it applies the value up-projection once to the attended latent
 // ("multi-head latent attention" glossary entry, paragraph on the decoupled RoPE key).
 //
-// A workgroup owns one head and 64 output columns; it stages that K x 64 slice of W[h] in
-// LDS once and then walks all M rows.  The product is formed transposed,
+// A workgroup owns one head, 64 output columns and a group of 16 or 32 rows; it stages that
+// K x 64 slice of W[h] in LDS and multiplies its rows by it.  The product is formed transposed,
 // y^T[n, m] = W^T[n, :] . x^T[:, m], so that the staged weights are the A operand (read
 // transposed from LDS), the activation rows are the B operand straight from global
 // memory, and each lane stores 4 consecutive output columns.
@@ -18,40 +18,59 @@ namespace {
 constexpr int kBN = 64;      // output columns per workgroup (one 16-column block per wave)
 constexpr int kThreads = 256;
 
+// Rows m .. m + 15 of head h as the B operand chunks of one 16-row block.  A row past M
+// loads row M - 1 instead (always in range): row m of the product depends on x row m only,
+// and rows past M are never stored, so the stand-in needs no masking.
 template <int K>
+__device__ __forceinline__ void load_x_block(bf16x8 (&bv)[K / 32], const uint16_t* __restrict__ x,
+                                             int m, int M, int H, int h, int g) {
+  const uint16_t* xr = x + (int64_t(min(m, M - 1)) * H + h) * K + 8 * g;
+#pragma unroll
+  for (int s = 0; s < K / 32; ++s) bv[s] = __builtin_bit_cast(bf16x8, ld16(xr + 32 * s));
+}
+
+// Grid (N / 64, H, ceil(M / MG)): one workgroup per (64-column tile, head, MG-row group).
+// Every load of the workgroup (its MG activation rows and the K x 64 weight slice) is issued
+// before the first wait, so a workgroup costs one memory latency; the weight slice of a
+// (tile, head) is shared by the row groups through L2.
+template <int K, int MG>
 __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ w,
                                                                uint16_t* __restrict__ y, int M,
                                                                int H, int N) {
+  constexpr int kBlocks = MG / 16;
   __shared__ __attribute__((aligned(16))) uint16_t wt[K * kBN];  // [k][64], chunks swizzled
-  const int n0 = blockIdx.x * kBN, h = blockIdx.y;
+  const int n0 = blockIdx.x * kBN, h = blockIdx.y, m0 = blockIdx.z * MG;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, mm = lane & 15;
 
-  const uint16_t* wh = w + int64_t(h) * K * N + n0;
+  bf16x8 bv[kBlocks][K / 32];
 #pragma unroll
-  for (int idx = tid; idx < K * 8; idx += kThreads) {
-    const int k = idx >> 3, ch = idx & 7;
-    *reinterpret_cast<u32x4*>(&wt[k * kBN + 8 * (ch ^ swz128(k))]) = ld16(wh + int64_t(k) * N + 8 * ch);
+  for (int i = 0; i < kBlocks; ++i) load_x_block<K>(bv[i], x, m0 + 16 * i + mm, M, H, h, g);
+  constexpr int kPer = K * 8 / kThreads;  // 16-byte weight chunks per thread
+  const uint16_t* wh = w + int64_t(h) * K * N + n0;
+  u32x4 wr[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = tid + i * kThreads, k = idx >> 3, ch = idx & 7;
+    wr[i] = ld16(wh + int64_t(k) * N + 8 * ch);
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int idx = tid + i * kThreads, k = idx >> 3, ch = idx & 7;
+    *reinterpret_cast<u32x4*>(&wt[k * kBN + 8 * (ch ^ swz128(k))]) = wr[i];
   }
   __syncthreads();
 
-  bf16x8 a[K / 32];
 #pragma unroll
-  for (int s = 0; s < K / 32; ++s) a[s] = lds_operand_tr(wt, 32 * s, 16 * wv, lane);
-
-  for (int m0 = 0; m0 < M; m0 += 16) {
-    const int m = m0 + mm;
-    const bool ok = m < M;
-    const uint16_t* xr = x + (int64_t(m) * H + h) * K + 8 * g;
-    bf16x8 bv[K / 32];
-#pragma unroll
-    for (int s = 0; s < K / 32; ++s)
-      bv[s] = __builtin_bit_cast(bf16x8, ok ? ld16(xr + 32 * s) : u32x4{0, 0, 0, 0});
+  for (int i = 0; i < kBlocks; ++i) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < K / 32; ++s) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[s], bv[s], acc, 0, 0, 0);
-    if (ok) {
+    for (int s = 0; s < K / 32; ++s)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_operand_tr(wt, 32 * s, 16 * wv, lane), bv[i][s],
+                                                    acc, 0, 0, 0);
+    const int m = m0 + 16 * i + mm;
+    if (m < M) {
       const uint32_t w0 = uint32_t(f32_to_bf16_bits(acc[0])) | (uint32_t(f32_to_bf16_bits(acc[1])) << 16);
       const uint32_t w1 = uint32_t(f32_to_bf16_bits(acc[2])) | (uint32_t(f32_to_bf16_bits(acc[3])) << 16);
       *reinterpret_cast<u32x2*>(y + (int64_t(m) * H + h) * N + n0 + 16 * wv + 4 * g) = u32x2{w0, w1};
@@ -61,20 +80,22 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
 
 }  // namespace
 
-bool absorb_mfma_supported(mla_dtype dt, int32_t K, int32_t N) {
-  return dt == MLA_BF16 && (K == 128 || K == 512) && N % kBN == 0;
+bool absorb_mfma_supported(mla_dtype dt, int32_t M, int32_t K, int32_t N) {
+  // The row groups are the grid's z dimension (at most 65535 groups of 16 rows).
+  return dt == MLA_BF16 && (K == 128 || K == 512) && N % kBN == 0 && M <= 16 * 65535;
 }
 
 int launch_absorb_mfma(const void* x, const void* w, void* y, int32_t M, int32_t H, int32_t K,
                        int32_t N, hipStream_t s) {
-  const dim3 grid(N / kBN, H);
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint16_t*>(w);
   auto* yp = static_cast<uint16_t*>(y);
   if (K == 128)
-    hipLaunchKernelGGL(absorb_mfma_kernel<128>, grid, dim3(kThreads), 0, s, xp, wp, yp, M, H, N);
+    hipLaunchKernelGGL((absorb_mfma_kernel<128, 32>), dim3(N / kBN, H, (M + 31) / 32), dim3(kThreads), 0, s,
+                       xp, wp, yp, M, H, N);
   else
-    hipLaunchKernelGGL(absorb_mfma_kernel<512>, grid, dim3(kThreads), 0, s, xp, wp, yp, M, H, N);
+    hipLaunchKernelGGL((absorb_mfma_kernel<512, 16>), dim3(N / kBN, H, (M + 15) / 16), dim3(kThreads), 0, s,
+                       xp, wp, yp, M, H, N);
   return int(hipGetLastError());
 }
 

@@ -190,47 +190,89 @@ __global__ __launch_bounds__(kThreads) void decode_general_kernel(DecodeArgs a, 
 
 // Merge the splits of one (sequence, query row): weights 2^(lse_s - max) over the splits
 // that start below the sequence length; output = weighted mean of the normalised partial
-// outputs; lse = max + log2(sum of weights), returned in natural-log units.
-template <typename OS>
+// outputs; lse = max + log2(sum of weights), returned in natural-log units.  One wave per
+// row, 8 consecutive columns per lane; the splits are read in batches whose loads are all
+// in flight together, merged with a running maximum so no separate max pass is needed.
+constexpr int kCombRows = 4;   // query rows (one per wave) per workgroup
+constexpr int kCombBatch = 8;  // splits per batch
+
+template <bool VEC>
+__device__ __forceinline__ void load8_f32(float (&v)[8], const float* p, int c, int dc) {
+  if (VEC) {  // dc % 8 == 0: the 8 columns are all in range or all out
+    const bool ok = c < dc;
+    const float4 x0 = ok ? *reinterpret_cast<const float4*>(p) : float4{0.f, 0.f, 0.f, 0.f};
+    const float4 x1 = ok ? *reinterpret_cast<const float4*>(p + 4) : float4{0.f, 0.f, 0.f, 0.f};
+    v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
+    v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = c + k < dc ? p[k] : 0.f;
+  }
+}
+
+template <typename OS, bool VEC>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int chunk) {
-  extern __shared__ float w_s[];  // [S] weights, then 2 reduction slots per wave
-  const int row = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rows = a.sq * a.H;
+  const int row = blockIdx.x * kCombRows + wave, b = blockIdx.y;
+  if (row >= rows) return;
   const int L = a.seq_lens ? a.seq_lens[b] : int(a.T);
   const int nvalid = min(S, (L + chunk - 1) / chunk);
   const float* pl = a.part_lse + int64_t(b) * S * rows + row;
-  float* red = w_s + S;
-
-  float mx = -INFINITY;
-  for (int s = tid; s < nvalid; s += 256) mx = fmaxf(mx, pl[int64_t(s) * rows]);
-  mx = wave_max(mx);
-  if (lane == 0) red[wave] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  const float m_use = mx == -INFINITY ? 0.f : mx;
-  float tot = 0.f;
-  for (int s = tid; s < nvalid; s += 256) {
-    const float w = exp2f(pl[int64_t(s) * rows] - m_use);
-    w_s[s] = w;
-    tot += w;
-  }
-  tot = wave_sum(tot);
-  __syncthreads();
-  if (lane == 0) red[4 + wave] = tot;
-  __syncthreads();
-  tot = red[4] + red[5] + red[6] + red[7];
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
+  const int64_t sstride = int64_t(rows) * a.dc;
+  const float* po = a.part_o + (int64_t(b) * S * rows + row) * a.dc;
   using OR = typename OS::raw;
   OR* o = static_cast<OR*>(a.o_lat) + (int64_t(b) * rows + row) * a.dc;
-  const float* po = a.part_o + (int64_t(b) * S * rows + row) * a.dc;
-  for (int c = tid; c < a.dc; c += 256) {
-    float v = 0.f;
-    for (int s = 0; s < nvalid; ++s) v += w_s[s] * po[int64_t(s) * rows * a.dc + c];
-    store_from_f32<OS>(o, c, v * inv);
+
+  for (int c0 = 0; c0 < a.dc; c0 += 512) {
+    const int c = c0 + 8 * lane;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float M = -INFINITY, tot = 0.f;
+    for (int s0 = 0; s0 < nvalid; s0 += kCombBatch) {
+      float ls[kCombBatch], v[kCombBatch][8];
+#pragma unroll
+      for (int j = 0; j < kCombBatch; ++j) {
+        const int sj = min(s0 + j, nvalid - 1);  // in range; surplus entries get weight 0
+        const float lj = pl[int64_t(sj) * rows];
+        ls[j] = s0 + j < nvalid ? lj : -INFINITY;
+        load8_f32<VEC>(v[j], po + sj * sstride + c, c, a.dc);
+      }
+      float bm = ls[0];
+#pragma unroll
+      for (int j = 1; j < kCombBatch; ++j) bm = fmaxf(bm, ls[j]);
+      const float Mn = fmaxf(M, bm);
+      if (Mn == -INFINITY) continue;  // nothing visible yet (uniform over the wave)
+      const float r = exp2f(M - Mn);  // 0 while M is still -inf
+      tot *= r;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] *= r;
+#pragma unroll
+      for (int j = 0; j < kCombBatch; ++j) {
+        const float w = exp2f(ls[j] - Mn);
+        tot += w;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) acc[k] = fmaf(w, v[j][k], acc[k]);
+      }
+      M = Mn;
+    }
+    const float inv = tot > 0.f ? 1.f / tot : 0.f;
+    if constexpr (VEC && sizeof(OR) == 2) {
+      if (c < a.dc) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          pk[k] = uint32_t(f32_to_bf16_bits(acc[2 * k] * inv)) |
+                  (uint32_t(f32_to_bf16_bits(acc[2 * k + 1] * inv)) << 16);
+        *reinterpret_cast<uint4*>(o + c) = uint4{pk[0], pk[1], pk[2], pk[3]};
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (c + k < a.dc) store_from_f32<OS>(o, c + k, acc[k] * inv);
+    }
+    if (c0 == 0 && lane == 0 && a.lse)
+      a.lse[int64_t(b) * rows + row] = tot > 0.f ? (M + log2f(tot)) * kLn2 : -INFINITY;
   }
-  if (a.lse && tid == 0)
-    a.lse[int64_t(b) * rows + row] = tot > 0.f ? (m_use + log2f(tot)) * kLn2 : -INFINITY;
 }
 
 template <typename QS, typename KVS, bool PAGED>
@@ -256,12 +298,15 @@ int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t 
 }
 
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
-  const dim3 grid(p.rows, a.B);
-  const size_t lds = sizeof(float) * (p.num_splits + 8);
-  if (a.q_dt == MLA_F32)
-    hipLaunchKernelGGL((combine_kernel<F32>), grid, dim3(256), lds, s, a, p.num_splits, p.split_tokens);
-  else
-    hipLaunchKernelGGL((combine_kernel<BF16>), grid, dim3(256), lds, s, a, p.num_splits, p.split_tokens);
+  const dim3 grid((p.rows + kCombRows - 1) / kCombRows, a.B);
+  const bool vec = a.dc % 8 == 0;
+  if (a.q_dt == MLA_F32) {
+    if (vec) hipLaunchKernelGGL((combine_kernel<F32, true>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+    else hipLaunchKernelGGL((combine_kernel<F32, false>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+  } else {
+    if (vec) hipLaunchKernelGGL((combine_kernel<BF16, true>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+    else hipLaunchKernelGGL((combine_kernel<BF16, false>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+  }
   return int(hipGetLastError());
 }
 

@@ -18,16 +18,17 @@
 //   * score waves 0-3: wave p owns latent columns [128p, 128p + 128) and RoPE dims
 //     [16p, 16p + 16).  It streams exactly that slice of every cache row from HBM into
 //     registers, two tiles ahead; computes partial scores (MFMA, cache slice as the A
-//     operand, query slice as the B operand); sums the four partial score tiles
-//     through LDS; runs the online softmax of rows [16p, 16p + 16); and publishes the
-//     tile's cache slice (in LDS, for the transposed reads) and the bf16 probabilities.
+//     operand, query slice as the B operand) into LDS; and publishes the tile's cache
+//     slice (in LDS, for the transposed reads).
 //   * output waves 4-7: wave 4 + q owns output columns [128q, 128q + 128) for all 64
 //     rows and accumulates O^T += V^T P^T for the previous tile (MFMA, cache slice read
 //     transposed from LDS as the A operand, probabilities as the B operand).
+//   * all eight waves share the online softmax: wave w sums the four partial scores of
+//     rows [8w, 8w + 8) and publishes their bf16 probabilities.
 // Each step has two barriers.  Half A: score waves run phase 1 of tile n while output
-// waves rescale and start PV of tile n - 1.  Half B: score waves run the softmax of
-// tile n while output waves finish PV of tile n - 1.  Slices and probabilities are double
-// buffered in LDS.  The cache is read from HBM once per workgroup.
+// waves rescale and start PV of tile n - 1.  Half B: every wave runs its rows' softmax
+// of tile n while output waves also finish PV of tile n - 1.  Slices and probabilities
+// are double buffered in LDS.  The cache is read from HBM once per workgroup.
 //
 // Softmax runs in base-2 units (scores times softmax_scale * log2(e), exponentials by the
 // hardware base-2 exponential; results that would be denormal flush to 0) against a per-row
@@ -50,9 +51,8 @@ constexpr int kTile = 32;               // tokens per tile
 constexpr int kThreads = 512;           // 4 score waves + 4 output waves
 constexpr int kCols = 128;              // latent columns per score wave / output wave
 constexpr int kRopeW = 16;              // RoPE dims per score wave
-constexpr int kSPitch = kTile + 4;      // floats per row of a partial-score tile
 constexpr int kPPitch = kTile + 8;      // bf16 per row of the probability tile
-constexpr int kSplitA = 1;              // output column blocks (of 4) done in half A
+constexpr int kSplitA = 3;              // output column blocks (of 4) done in half A
 // A row's reference max (the value its probabilities are taken relative to) only moves
 // when a tile's max exceeds it by more than this many base-2 units, so probabilities stay
 // below 2^kTau and the output waves almost never have to rescale their accumulators.
@@ -60,13 +60,65 @@ constexpr int kSplitA = 1;              // output column blocks (of 4) done in h
 constexpr float kTau = 8.f;
 
 struct alignas(16) Smem {
-  float spart[4][kRows][kSPitch];       // partial S^T of each score wave, [row][tok]
+  float spart[4][kRows][kTile];         // partial S of each score wave, [row][tok], swizzled
   uint16_t v[2][4][kTile][kCols];       // cache slices (double buffered), swz32 chunks
   uint16_t p[2][kRows][kPPitch];        // probabilities (double buffered), [row][tok]
   float ts[2][4][kTile];                // fp8 per-token scales, one copy per score wave
   float alpha[2][kRows];                // per-row rescale factor of each buffered tile
   float lsum[kRows];
 };
+
+// Partial-score rows hold 8 chunks of 4 tokens; chunk c of row r is stored at c ^ sp_swz(r),
+// which keeps both the score waves' writes (16 rows, one chunk) and the softmax reads
+// (2 rows, 8 chunks) on distinct LDS banks.
+__device__ __forceinline__ int sp_swz(int row) { return (row >> 1) & 7; }
+
+// Softmax state of one lane: row `row` of the workgroup, tokens 4 tg .. 4 tg + 3 of each tile.
+struct SoftmaxLane {
+  int row, tg;
+  int lim;    // tokens below this index are visible to the row (and inside the split)
+  int lim_w;  // smallest lim over the wave's 8 rows: tiles below it need no masking
+  float m_run, l_run;
+};
+
+// Online softmax of one tile for this lane's row and 4 tokens: sums the four partial
+// scores, masks invisible tokens (only in tiles that reach past lim_w), moves the row's
+// reference max when the tile exceeds it by more than kTau, and publishes the bf16
+// probabilities and the row's rescale factor.  Rows are spread over all eight waves
+// (8 rows per wave, 8 lanes per row), so the 8-lane reductions are DPP steps.
+template <bool FP8>
+__device__ __forceinline__ void softmax_tile(Smem& sm, SoftmaxLane& st, int buf, int t0, float scale_log2) {
+  const int ch = 4 * (st.tg ^ sp_swz(st.row));
+  f32x4 sv4 = *reinterpret_cast<const f32x4*>(&sm.spart[0][st.row][ch]);
+#pragma unroll
+  for (int q = 1; q < 4; ++q) sv4 += *reinterpret_cast<const f32x4*>(&sm.spart[q][st.row][ch]);
+  float sv[4] = {sv4[0], sv4[1], sv4[2], sv4[3]};
+  if (t0 + kTile > st.lim_w) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (t0 + 4 * st.tg + e >= st.lim) sv[e] = -INFINITY;
+  }
+  float tmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  tmax = max8(tmax) * scale_log2;  // scale > 0: max commutes with it
+  const bool grow = tmax > st.m_run + kTau;  // false while nothing is visible
+  const float alpha = grow ? __builtin_amdgcn_exp2f(st.m_run - tmax) : 1.f;
+  if (grow) st.m_run = tmax;
+  const float neg_m = st.m_run == -INFINITY ? 0.f : -st.m_run;
+  float pr[4], psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    pr[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, neg_m));
+    psum += pr[e];
+  }
+  if constexpr (FP8) {
+    const f32x4 t4 = *reinterpret_cast<const f32x4*>(&sm.ts[buf][0][4 * st.tg]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pr[e] *= t4[e];
+  }
+  st.l_run = st.l_run * alpha + psum;
+  *reinterpret_cast<u32x2*>(&sm.p[buf][st.row][4 * st.tg]) = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+  if (st.tg == 0) sm.alpha[buf][st.row] = alpha;
+}
 
 // Column layout of one score lane's k-slices: for k-step s (0..7) of its 128 latent
 // columns, lane half h (= lane / 32) holds 8 consecutive columns starting here.  The A
@@ -228,6 +280,34 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
   const int steps = ntiles > 0 ? ntiles + 1 : 0;
   const bool single = num_splits == 1;
 
+  // Softmax ownership (all eight waves): row 8w + lane / 8, tokens 4 (lane % 8) + (0..3).
+  SoftmaxLane st;
+  st.row = 8 * c.w + (c.lane >> 3);
+  st.tg = c.lane & 7;
+  {
+    const int iq = (r0 + st.row) / a.H;  // query token of the row
+    st.lim = min(min(max(L - a.sq + iq + 1, 0), L), c.t_hi);
+    // The wave's first row has the smallest query index, hence the smallest limit.
+    const int iq_w = (r0 + 8 * c.w) / a.H;
+    st.lim_w = min(min(max(L - a.sq + iq_w + 1, 0), L), c.t_hi);
+  }
+  st.m_run = -INFINITY;
+  st.l_run = 0.f;
+
+  // Row sums and log-sum-exp of this lane's row, once its last tile is done.
+  auto finish_rows = [&](const SoftmaxLane& sl) {
+    const float l_tot = sum8(sl.l_run);
+    if (sl.tg == 0) {
+      sm.lsum[sl.row] = l_tot;
+      const float lse2 = l_tot > 0.f ? sl.m_run + log2f(l_tot) : -INFINITY;
+      if (single) {
+        if (a.lse) a.lse[int64_t(b) * rows + r0 + sl.row] = lse2 * kLn2;
+      } else {
+        a.part_lse[(int64_t(b) * num_splits + split) * rows + r0 + sl.row] = lse2;
+      }
+    }
+  };
+
   if (c.w < 4) {
     // ================================ score waves ===================================
     // Query operands (B of phase 1): rows r0 + 32 rb2 + n, this wave's column slice.
@@ -245,18 +325,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
         qrb[rb2] = __builtin_bit_cast(bf16x8, ld16(qr + row * kDR + kRopeW * c.w + 8 * c.h));
       }
     }
-    // Softmax ownership: row 16w + (lane % 16), tokens 8g .. 8g + 7 (g = lane / 16).
-    const int g = c.lane >> 4;
-    const int srow = 16 * c.w + (c.lane & 15);
-    const int iq = (r0 + srow) / a.H;
-    const int vis = min(max(L - a.sq + iq + 1, 0), L);  // tokens this query row may see
-    const int lim = min(vis, c.t_hi);
-    // Smallest limit over this wave's rows (its first row has the smallest query index):
-    // tiles entirely below it need no masking.
-    const int iq_w = (r0 + 16 * c.w) / a.H;
-    const int lim_w = min(min(max(L - a.sq + iq_w + 1, 0), L), c.t_hi);
-    float m_run = -INFINITY, l_run = 0.f;
-
     // Half A (phase 1 of tile n into buffer n % 2) and half B (its softmax).
     auto step = [&](TileRegs<FP8>& tr, int n) {
       const int t0 = t_lo + n * kTile;
@@ -295,56 +363,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
       for (int rb2 = 0; rb2 < 2; ++rb2)
         sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qrb[rb2], sacc[rb2], 0, 0, 0);
 #pragma unroll
-      for (int rb2 = 0; rb2 < 2; ++rb2)
+      for (int rb2 = 0; rb2 < 2; ++rb2) {
+        const int row = 32 * rb2 + c.n;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          *reinterpret_cast<f32x4*>(&sm.spart[c.w][32 * rb2 + c.n][8 * i + 4 * c.h]) =
+        for (int i = 0; i < 4; ++i)  // tokens 8i + 4h + (0..3) = chunk 2i + h
+          *reinterpret_cast<f32x4*>(&sm.spart[c.w][row][4 * ((2 * i + c.h) ^ sp_swz(row))]) =
               f32x4{sacc[rb2][4 * i], sacc[rb2][4 * i + 1], sacc[rb2][4 * i + 2], sacc[rb2][4 * i + 3]};
+      }
       load_tile<FP8, PK>(tr, c, a, t0 + 2 * kTile);  // refill: two tiles ahead
       __syncthreads();
 
-      // Online softmax of row srow over tokens 8g .. 8g + 7.
-      f32x4 s0 = *reinterpret_cast<const f32x4*>(&sm.spart[0][srow][8 * g]);
-      f32x4 s1 = *reinterpret_cast<const f32x4*>(&sm.spart[0][srow][8 * g + 4]);
-#pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        s0 += *reinterpret_cast<const f32x4*>(&sm.spart[q][srow][8 * g]);
-        s1 += *reinterpret_cast<const f32x4*>(&sm.spart[q][srow][8 * g + 4]);
-      }
-      float sv[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
-      if (t0 + kTile > lim_w) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (t0 + 8 * g + e >= lim) sv[e] = -INFINITY;
-      }
-      float tmax = sv[0];
-#pragma unroll
-      for (int e = 1; e < 8; ++e) tmax = fmaxf(tmax, sv[e]);
-      tmax = max_xor16_32(tmax) * a.scale_log2;  // scale > 0: max commutes with it
-      const bool grow = tmax > m_run + kTau;      // false while nothing is visible
-      const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - tmax) : 1.f;
-      if (grow) m_run = tmax;
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
-      float pr[8], psum = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pr[e] = __builtin_amdgcn_exp2f(fmaf(sv[e], a.scale_log2, neg_m));
-        psum += pr[e];
-      }
-      if constexpr (FP8) {
-        const f32x4 t_lo4 = *reinterpret_cast<const f32x4*>(&sm.ts[buf][c.w][8 * g]);
-        const f32x4 t_hi4 = *reinterpret_cast<const f32x4*>(&sm.ts[buf][c.w][8 * g + 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pr[e] *= t_lo4[e];
-          pr[4 + e] *= t_hi4[e];
-        }
-      }
-      l_run = l_run * alpha + psum;
-      *reinterpret_cast<u32x4*>(&sm.p[buf][srow][8 * g]) =
-          u32x4{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3]), pack_bf16x2(pr[4], pr[5]),
-                pack_bf16x2(pr[6], pr[7])};
-      if (g == 0) sm.alpha[buf][srow] = alpha;
+      softmax_tile<FP8>(sm, st, buf, t0, a.scale_log2);
       __syncthreads();
     };
 
@@ -364,16 +393,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
       __syncthreads();
     }
 
-    const float l_tot = sum_xor16_32(l_run);
-    if (g == 0) {
-      sm.lsum[srow] = l_tot;
-      const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
-      if (single) {
-        if (a.lse) a.lse[int64_t(b) * rows + r0 + srow] = lse2 * kLn2;
-      } else {
-        a.part_lse[(int64_t(b) * num_splits + split) * rows + r0 + srow] = lse2;
-      }
-    }
+    finish_rows(st);
     __syncthreads();
   } else {
     // ================================ output waves ==================================
@@ -423,9 +443,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
 #pragma unroll
         for (int cb = kSplitA; cb < 4; ++cb) pv(vt, cb);
       }
+      if (n < ntiles) softmax_tile<FP8>(sm, st, n & 1, t_lo + n * kTile, a.scale_log2);
       __syncthreads();
     }
-    __syncthreads();  // row sums published by the score waves
+    finish_rows(st);
+    __syncthreads();  // every row sum published
 
 #pragma unroll
     for (int rb2 = 0; rb2 < 2; ++rb2) {

@@ -153,4 +153,30 @@ __device__ __forceinline__ float sum_xor16_32(float x) {
   return a + b;
 }
 
+// Data-parallel-primitive (DPP) lane permutations of a float, applied to the source
+// operand of a register move: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1]
+// (lane ^ 2) and row_half_mirror (lane j of each 8-lane group reads lane 7 - j).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+
+// Reductions over the 8-lane group of a lane (lanes 8j .. 8j + 7): after the two quad
+// steps every lane holds its quad's result, and the half mirror pairs each lane of one
+// quad with a lane of the other.
+__device__ __forceinline__ float max8(float x) {
+  x = fmaxf(x, dpp_f32<kDppXor1>(x));
+  x = fmaxf(x, dpp_f32<kDppXor2>(x));
+  return fmaxf(x, dpp_f32<kDppHalfMirror>(x));
+}
+
+__device__ __forceinline__ float sum8(float x) {
+  x += dpp_f32<kDppXor1>(x);
+  x += dpp_f32<kDppXor2>(x);
+  return x + dpp_f32<kDppHalfMirror>(x);
+}
+
 }  // namespace mla

@@ -18,6 +18,7 @@ constexpr int kMaxLatent = 2048;      // general-kernel limits (query rows are s
 constexpr int kMaxRope = 512;
 constexpr int kMaxQLen = 8;
 constexpr int kMaxRows = 1 << 16;
+constexpr int kMaxGridDim = 65535;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -119,6 +120,8 @@ mla_status check_dims(const mla_dims* d) {
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if (int64_t(d->q_len) * d->n_heads > kMaxRows) return MLA_ERR_UNSUPPORTED;
+  // Batch and heads index grid dimensions that hold at most 65535 workgroups.
+  if (d->batch > kMaxGridDim || d->n_heads > kMaxGridDim) return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 

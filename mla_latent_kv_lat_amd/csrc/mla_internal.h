@@ -62,7 +62,7 @@ int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_absorb(const void* x, const void* w, void* y, mla_dtype dt, int32_t M, int32_t H,
                   int32_t K, int32_t N, hipStream_t s);
-bool absorb_mfma_supported(mla_dtype dt, int32_t K, int32_t N);
+bool absorb_mfma_supported(mla_dtype dt, int32_t M, int32_t K, int32_t N);
 int launch_absorb_mfma(const void* x, const void* w, void* y, int32_t M, int32_t H, int32_t K,
                        int32_t N, hipStream_t s);
 int launch_gather_pages(const void* pool, int32_t block_size, int64_t row_bytes,
