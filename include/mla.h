@@ -76,7 +76,11 @@ typedef struct {
  *   - every shape with all tensors MLA_F32, and with activations / weights in MLA_BF16
  *     and the latent cache in MLA_BF16 or MLA_FP8_E4M3 (general kernels);
  *   - d_c = 512, d_r = 64, activations MLA_BF16, cache MLA_BF16 or MLA_FP8_E4M3,
- *     s_q * n_h a multiple of 64: the matrix-core (MFMA) decode kernel. */
+ *     s_q * n_h a multiple of 64, and one sequence's cache rows spanning less than 2 GiB
+ *     (max_seq_len * 512 * bytes per code < 2^31): the matrix-core (MFMA) decode kernel.
+ * Limits of every kernel: d_c <= 2048, d_r <= 512, s_q * n_h <= 65536, batch <= 65535,
+ * n_heads <= 65535; a decode call uses at most 8192 context splits (an explicit
+ * split_tokens that would need more returns MLA_ERR_UNSUPPORTED). */
 
 /* ---- query-side absorption ---------------------------------------------------------
  * q_lat[b,i,h,c] = sum_j q_nope[b,i,h,j] * w_uk[h,j,c]   (fp32 accumulation)
