@@ -17,9 +17,10 @@
 // side, 32 query rows on the other).
 //   * score waves 0-3: wave p owns latent columns [128p, 128p + 128) and RoPE dims
 //     [16p, 16p + 16).  It streams exactly that slice of every cache row from HBM into
-//     registers, two tiles ahead; computes partial scores (MFMA, cache slice as the A
-//     operand, query slice as the B operand) into LDS; and publishes the tile's cache
-//     slice (in LDS, for the transposed reads).
+//     registers, two tiles ahead, with coalesced loads (whole row slices per load); stages
+//     the tile's slice in LDS (swizzled; the output waves read it there too) and refills
+//     the registers at once; computes partial scores (MFMA, cache slice read back from LDS
+//     as the A operand, query slice as the B operand) into LDS.
 //   * output waves 4-7: wave 4 + q owns output columns [128q, 128q + 128) for all 64
 //     rows and accumulates O^T += V^T P^T for the previous tile (MFMA, cache slice read
 //     transposed from LDS as the A operand, probabilities as the B operand).
@@ -129,25 +130,26 @@ __device__ __forceinline__ int kcol(int s, int h) { return 32 * (s >> 1) + 16 * 
 template <bool FP8>
 struct TileRegs;
 
+// A score wave's tile registers.  The latent slice is loaded coalesced: load k covers
+// whole 256-byte (bf16) or 128-byte (fp8) row slices of consecutive tokens, 16 bytes per
+// lane, so each load instruction touches few cache lines; the slice then goes through LDS,
+// where the score product reads it back in operand layout.  The RoPE slice is loaded in
+// operand layout directly (token n = lane % 32, dims 8h .. 8h + 7 of the wave's 16).
 template <>
 struct TileRegs<false> {
-  u32x4 lat[8];      // [k-step]: 8 bf16 of this lane's token
-  u32x4 rope;        // 8 bf16 of this lane's token
+  u32x4 lat[8];      // load k: token 4k + lane / 16, columns 8 (lane % 16) + (0..7)
+  u32x4 rope;
 };
 
 template <>
 struct TileRegs<true> {
-  u32x4 lat[4];      // [pair of k-steps]: 16 fp8 codes of this lane's token
+  u32x4 lat[4];      // load k: token 8k + lane / 8, columns 16 (lane % 8) + (0..15), fp8 codes
   u32x4 rope;
-  float ts;          // this lane's token scale
+  float ts;          // scale of token lane % 32
 };
 
-__device__ __forceinline__ u32x4 a_operand(const TileRegs<false>& t, int s) { return t.lat[s]; }
-
-__device__ __forceinline__ u32x4 a_operand(const TileRegs<true>& t, int s) {
-  const u32x4 w = t.lat[s >> 1];
-  return (s & 1) ? e4m3x8_to_bf16x8(w[2], w[3]) : e4m3x8_to_bf16x8(w[0], w[1]);
-}
+// Token held by load k of this lane.
+__device__ __forceinline__ int lat_token(bool fp8, int k, int lane) { return fp8 ? 8 * k + (lane >> 3) : 4 * k + (lane >> 4); }
 
 struct Ctx {
   int b, lane, n, h, w;
@@ -218,29 +220,20 @@ __device__ __forceinline__ void load_tile(TileRegs<FP8>& r, const Ctx& c, const 
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(lat_base, nrows * kLatBytes);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(rope_base, nrows * kRopeBytes);
     const uint32_t row = row0 + uint32_t(c.n);
-    if constexpr (FP8) {
-      const uint32_t off = row * kLatBytes + kCols * c.w + 16 * c.h;
+    const uint32_t col_off = (kLatBytes / 4) * c.w + 16 * (FP8 ? (c.lane & 7) : (c.lane & 15));
 #pragma unroll
-      for (int t = 0; t < 4; ++t) r.lat[t] = buf_ld16(rl, off + 32 * t);
-      r.ts = buf_ld4f(make_rsrc(sc_base, nrows * 4), row * 4);
-    } else {
-      const uint32_t off = row * kLatBytes + 2 * kCols * c.w;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) r.lat[s] = buf_ld16(rl, off + 2 * kcol(s, c.h));
-    }
+    for (int k = 0; k < (FP8 ? 4 : 8); ++k)
+      r.lat[k] = buf_ld16(rl, (row0 + uint32_t(lat_token(FP8, k, c.lane))) * kLatBytes + col_off);
+    if constexpr (FP8) r.ts = buf_ld4f(make_rsrc(sc_base, nrows * 4), row * 4);
     r.rope = buf_ld16(rr, row * kRopeBytes + 2 * (kRopeW * c.w + 8 * c.h));
   } else {
+    const char* lat = static_cast<const char*>(a.c_kv);
+    const int64_t col_off = (kLatBytes / 4) * c.w + 16 * (FP8 ? (c.lane & 7) : (c.lane & 15));
+#pragma unroll
+    for (int k = 0; k < (FP8 ? 4 : 8); ++k)
+      r.lat[k] = ld16(lat + any_row(c, t0 + lat_token(FP8, k, c.lane)) * kLatBytes + col_off);
     const int64_t row = any_row(c, t0 + c.n);
-    if constexpr (FP8) {
-      const uint8_t* base = static_cast<const uint8_t*>(a.c_kv) + row * kDC + kCols * c.w + 16 * c.h;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) r.lat[t] = ld16(base + 32 * t);
-      r.ts = a.kv_scale[row];
-    } else {
-      const uint16_t* base = static_cast<const uint16_t*>(a.c_kv) + row * kDC + kCols * c.w;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) r.lat[s] = ld16(base + kcol(s, c.h));
-    }
+    if constexpr (FP8) r.ts = a.kv_scale[row];
     r.rope = ld16(static_cast<const uint16_t*>(a.k_rope) + row * kDR + kRopeW * c.w + 8 * c.h);
   }
 }
@@ -334,21 +327,37 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
       for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[rb2][e] = 0.f;
+      // Stage the tile's latent slice in LDS (bf16; also the output waves' V), keep the
+      // RoPE operand and token scale, and refill the registers at once.  LDS operations of
+      // one wave complete in order, so the wave reads its own slice back without a barrier.
+      uint16_t* vs = &sm.v[buf][c.w][0][0];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int tok = lat_token(true, k, c.lane), c16 = c.lane & 7;
+          const u32x4 w = tr.lat[k];
+          *reinterpret_cast<u32x4*>(vs + tok * kCols + 8 * ((2 * c16) ^ swz32(tok))) = e4m3x8_to_bf16x8(w[0], w[1]);
+          *reinterpret_cast<u32x4*>(vs + tok * kCols + 8 * ((2 * c16 + 1) ^ swz32(tok))) = e4m3x8_to_bf16x8(w[2], w[3]);
+        }
+        if (c.h == 0) sm.ts[buf][c.w][c.n] = tr.ts;
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int tok = lat_token(false, k, c.lane);
+          *reinterpret_cast<u32x4*>(vs + tok * kCols + 8 * ((c.lane & 15) ^ swz32(tok))) = tr.lat[k];
+        }
+      }
+      const bf16x8 ar = __builtin_bit_cast(bf16x8, tr.rope);
+      load_tile<FP8, PK>(tr, c, a, t0 + 2 * kTile);  // refill: two tiles ahead
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        const u32x4 araw = a_operand(tr, s);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, araw);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + c.n * kCols + 8 * ((kcol(s, c.h) >> 3) ^ swz32(c.n)));
 #pragma unroll
         for (int rb2 = 0; rb2 < 2; ++rb2)
           sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[rb2][s], sacc[rb2], 0, 0, 0);
-        // Keep the (bf16) slice for the output waves: 16 bytes of token n.
-        const int ch = (kcol(s, c.h) >> 3) ^ swz32(c.n);
-        *reinterpret_cast<u32x4*>(&sm.v[buf][c.w][c.n][8 * ch]) = araw;
       }
       if constexpr (FP8) {
-        // Share the token scales within the wave (LDS operations of one wave complete in
-        // order), then scale the latent part of tokens 8i + 4h + r.
-        if (c.h == 0) sm.ts[buf][c.w][c.n] = tr.ts;
+        // Scale the latent part of tokens 8i + 4h + r by their per-token scales.
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x4 tsv = *reinterpret_cast<const f32x4*>(&sm.ts[buf][c.w][8 * i + 4 * c.h]);
@@ -358,7 +367,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
             for (int r = 0; r < 4; ++r) sacc[rb2][4 * i + r] *= tsv[r];
         }
       }
-      const bf16x8 ar = __builtin_bit_cast(bf16x8, tr.rope);
 #pragma unroll
       for (int rb2 = 0; rb2 < 2; ++rb2)
         sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qrb[rb2], sacc[rb2], 0, 0, 0);
@@ -370,7 +378,6 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
           *reinterpret_cast<f32x4*>(&sm.spart[c.w][row][4 * ((2 * i + c.h) ^ sp_swz(row))]) =
               f32x4{sacc[rb2][4 * i], sacc[rb2][4 * i + 1], sacc[rb2][4 * i + 2], sacc[rb2][4 * i + 3]};
       }
-      load_tile<FP8, PK>(tr, c, a, t0 + 2 * kTile);  // refill: two tiles ahead
       __syncthreads();
 
       softmax_tile<FP8>(sm, st, buf, t0, a.scale_log2);

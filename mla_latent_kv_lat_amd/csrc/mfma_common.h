@@ -22,6 +22,7 @@ namespace mla {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -155,7 +156,8 @@ __device__ __forceinline__ float sum_xor16_32(float x) {
 
 // Data-parallel-primitive (DPP) lane permutations of a float, applied to the source
 // operand of a register move: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1]
-// (lane ^ 2) and row_half_mirror (lane j of each 8-lane group reads lane 7 - j).
+// (lane ^ 2), row_half_mirror (lane j of each 8-lane group reads lane 7 - j) and
+// row_mirror (lane j of each 16-lane row reads lane 15 - j).
 template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
@@ -163,6 +165,7 @@ __device__ __forceinline__ float dpp_f32(float v) {
 constexpr int kDppXor1 = 0xB1;
 constexpr int kDppXor2 = 0x4E;
 constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
 
 // Reductions over the 8-lane group of a lane (lanes 8j .. 8j + 7): after the two quad
 // steps every lane holds its quad's result, and the half mirror pairs each lane of one
@@ -177,6 +180,18 @@ __device__ __forceinline__ float sum8(float x) {
   x += dpp_f32<kDppXor1>(x);
   x += dpp_f32<kDppXor2>(x);
   return x + dpp_f32<kDppHalfMirror>(x);
+}
+
+// Reductions over the 16-lane row of a lane: the 8-lane result, then row_mirror (lane j
+// reads lane 15 - j) pairs the two halves.
+__device__ __forceinline__ float max16(float x) {
+  x = max8(x);
+  return fmaxf(x, dpp_f32<kDppRowMirror>(x));
+}
+
+__device__ __forceinline__ float sum16(float x) {
+  x = sum8(x);
+  return x + dpp_f32<kDppRowMirror>(x);
 }
 
 }  // namespace mla
