@@ -53,7 +53,7 @@ constexpr int kThreads = 512;           // 4 score waves + 4 output waves
 constexpr int kCols = 128;              // latent columns per score wave / output wave
 constexpr int kRopeW = 16;              // RoPE dims per score wave
 constexpr int kPPitch = kTile + 8;      // bf16 per row of the probability tile
-constexpr int kSplitA = 3;              // output column blocks (of 4) done in half A
+constexpr int kSplitA = 4;              // output column blocks (of 4) done in half A
 // A row's reference max (the value its probabilities are taken relative to) only moves
 // when a tile's max exceeds it by more than this many base-2 units, so probabilities stay
 // below 2^kTau and the output waves almost never have to rescale their accumulators.
