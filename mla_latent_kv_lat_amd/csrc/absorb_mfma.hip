@@ -29,10 +29,12 @@ __device__ __forceinline__ void load_x_block(bf16x8 (&bv)[K / 32], const uint16_
   for (int s = 0; s < K / 32; ++s) bv[s] = __builtin_bit_cast(bf16x8, ld16(xr + 32 * s));
 }
 
-// Grid (N / 64, H, ceil(M / MG)): one workgroup per (64-column tile, head, MG-row group).
+// Grid (H, N / 64, ceil(M / MG)): one workgroup per (head, 64-column tile, MG-row group).
 // Every load of the workgroup (its MG activation rows and the K x 64 weight slice) is issued
-// before the first wait, so a workgroup costs one memory latency; the weight slice of a
-// (tile, head) is shared by the row groups through L2.
+// before the first wait, so a workgroup costs one memory latency.  Workgroup ids are dealt
+// to the 8 XCDs round-robin, and the head is the fastest grid dimension: with H a multiple
+// of 8, all column tiles (and row groups) of one head run on one XCD and share its
+// activation rows (and weight slice) through that XCD's L2.
 template <int K, int MG>
 __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ w,
@@ -40,7 +42,7 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
                                                                int H, int N) {
   constexpr int kBlocks = MG / 16;
   __shared__ __attribute__((aligned(16))) uint16_t wt[K * kBN];  // [k][64], chunks swizzled
-  const int n0 = blockIdx.x * kBN, h = blockIdx.y, m0 = blockIdx.z * MG;
+  const int h = blockIdx.x, n0 = blockIdx.y * kBN, m0 = blockIdx.z * MG;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, mm = lane & 15;
 
@@ -81,8 +83,8 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
 }  // namespace
 
 bool absorb_mfma_supported(mla_dtype dt, int32_t M, int32_t K, int32_t N) {
-  // The row groups are the grid's z dimension (at most 65535 groups of 16 rows).
-  return dt == MLA_BF16 && (K == 128 || K == 512) && N % kBN == 0 && M <= 16 * 65535;
+  // The row groups are the grid's z dimension (at most 65535 groups of 32 rows).
+  return dt == MLA_BF16 && (K == 128 || K == 512) && N % kBN == 0 && M <= 32 * 65535;
 }
 
 int launch_absorb_mfma(const void* x, const void* w, void* y, int32_t M, int32_t H, int32_t K,
@@ -91,10 +93,10 @@ int launch_absorb_mfma(const void* x, const void* w, void* y, int32_t M, int32_t
   const auto* wp = static_cast<const uint16_t*>(w);
   auto* yp = static_cast<uint16_t*>(y);
   if (K == 128)
-    hipLaunchKernelGGL((absorb_mfma_kernel<128, 32>), dim3(N / kBN, H, (M + 31) / 32), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((absorb_mfma_kernel<128, 32>), dim3(H, N / kBN, (M + 31) / 32), dim3(kThreads), 0, s,
                        xp, wp, yp, M, H, N);
   else
-    hipLaunchKernelGGL((absorb_mfma_kernel<512, 16>), dim3(N / kBN, H, (M + 15) / 16), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((absorb_mfma_kernel<512, 32>), dim3(H, N / kBN, (M + 31) / 32), dim3(kThreads), 0, s,
                        xp, wp, yp, M, H, N);
   return int(hipGetLastError());
 }

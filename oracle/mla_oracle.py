@@ -282,3 +282,91 @@ def gather_pages(pool, block_table, seq_lens, seq_len_max, fill=0.0):
         for t in range(int(seq_lens[b])):
             out[b, t] = pool[block_table[b, t // bs], t % bs]
     return out
+
+
+# ---------------------------------------------------------------------------------
+# Cache write of the new tokens ("Operator Notes (1): MLA", section 2: the latent is the
+# only KV state cached; "multi-head latent attention" glossary entry, paragraph on the
+# decoupled RoPE key: a small separate rotated key is cached next to the latent)
+# ---------------------------------------------------------------------------------
+#
+# Readings (the pages name these steps but print no formula):
+# * the decoupled key is projected from the same hidden state by its own matrix W_KR
+#   [d_model, d_r] and rotated by its position;
+# * the rotation is the standard rotary position embedding: dims are paired, pair j is
+#   rotated by the angle  position * base^(-2j / d_r);  the pairing is a parameter,
+#   "interleaved" (2j, 2j + 1) or "half" (j, j + d_r / 2);
+# * new token i of a sequence whose length (counting the new tokens) is L sits at position
+#   L - s_q + i, the same convention the decode's causal mask uses;
+# * an fp8 cache stores per token scale = max|c| / 448 (1 for an all-zero row) and the
+#   e4m3 code nearest to c / scale (ties to the even code).
+
+
+def rope_rotate(x, positions, base: float, pairing: str):
+    """Rotary position embedding of the last axis of x (even width d_r).
+
+    positions broadcasts against x.shape[:-1].  Pair j = (x_a, x_b) becomes
+    (x_a cos t - x_b sin t, x_a sin t + x_b cos t) with t = position * base^(-2j / d_r).
+    """
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    inv = np.asarray(base, np.float64) ** (-2.0 * np.arange(half) / d)
+    ang = np.asarray(positions, np.float64)[..., None] * inv
+    cos, sin = np.cos(ang), np.sin(ang)
+    out = np.empty_like(x)
+    if pairing == "interleaved":
+        a, b = x[..., 0::2], x[..., 1::2]
+        out[..., 0::2] = a * cos - b * sin
+        out[..., 1::2] = a * sin + b * cos
+    elif pairing == "half":
+        a, b = x[..., :half], x[..., half:]
+        out[..., :half] = a * cos - b * sin
+        out[..., half:] = a * sin + b * cos
+    else:
+        raise ValueError(pairing)
+    return out
+
+
+def new_token_positions(seq_lens, q_len: int):
+    """Position of new token i of sequence b: seq_lens[b] - q_len + i."""
+    return np.asarray(seq_lens, np.int64)[:, None] - q_len + np.arange(q_len)[None, :]
+
+
+def cache_append_rows(x, w_dkv, w_kr, seq_lens, q_len: int, base: float, pairing: str):
+    """Latent and rotated RoPE key of every new token.
+
+    x [B, s_q, d_model], w_dkv [d_model, d_c], w_kr [d_model, d_r] ->
+    (c [B, s_q, d_c], k_rope [B, s_q, d_r], positions [B, s_q]).
+    """
+    x = np.asarray(x, np.float64)
+    c = x @ np.asarray(w_dkv, np.float64)
+    k = x @ np.asarray(w_kr, np.float64)
+    pos = new_token_positions(seq_lens, q_len)
+    return c, rope_rotate(k, pos, base, pairing), pos
+
+
+_E4M3_MAGNITUDES = None
+
+
+def quantize_e4m3fn_rows(c):
+    """Per-row fp8 encoding: scale = max|row| / 448 (1 if the row is zero) and, for every
+    element y = c / scale, the e4m3fn code of sign(y) and of the finite magnitude nearest
+    to |y| (ties to the magnitude whose code has an even mantissa), as a sign-magnitude
+    format rounds.  Returns (codes uint8, scale float64)."""
+    global _E4M3_MAGNITUDES
+    if _E4M3_MAGNITUDES is None:
+        codes = np.arange(0x7F, dtype=np.uint8)  # 0x00 .. 0x7E: +0 .. 448 (0x7F is NaN)
+        _E4M3_MAGNITUDES = (codes, decode_e4m3fn(codes))
+    cand_codes, cand_vals = _E4M3_MAGNITUDES
+    c = np.asarray(c, np.float64)
+    amax = np.max(np.abs(c), axis=-1)
+    scale = np.where(amax > 0, amax / 448.0, 1.0)
+    y = c / scale[..., None]
+    d = np.abs(np.abs(y)[..., None] - cand_vals)              # [..., n, 127]
+    best = d.min(axis=-1, keepdims=True)
+    # among the nearest magnitudes prefer an even mantissa (code bit 0 clear)
+    pref = np.where(d <= best, (cand_codes & 1).astype(np.int64), 2)
+    mag = cand_codes[np.argmin(pref * 1e9 + d, axis=-1)]
+    sign = np.where(np.signbit(y), 0x80, 0x00).astype(np.uint8)
+    return (mag | sign).astype(np.uint8), scale

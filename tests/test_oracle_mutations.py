@@ -8,6 +8,7 @@ import pytest
 
 from oracle import mla_oracle as O
 import test_oracle as P
+import test_oracle_cache_write as PC
 
 _orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
 
@@ -63,6 +64,33 @@ def _mha_count_wrong(n_heads, d_head):
     return n_heads * d_head
 
 
+def _rope_sin_sign(x, positions, base, pairing):
+    return _orig["rope_rotate"](x, -np.asarray(positions, np.float64), base, pairing)
+
+
+def _rope_wrong_frequency(x, positions, base, pairing):
+    return _orig["rope_rotate"](x, positions, np.sqrt(base), pairing)
+
+
+def _rope_swapped_pairing(x, positions, base, pairing):
+    return _orig["rope_rotate"](x, positions, base, "half" if pairing == "interleaved" else "interleaved")
+
+
+def _positions_off_by_one(seq_lens, q_len):
+    return _orig["new_token_positions"](seq_lens, q_len) + 1
+
+
+def _quantize_half_scale(c):
+    # the stored scale is amax / 224: dequantised values come out twice too large
+    codes, scale = _orig["quantize_e4m3fn_rows"](c)
+    return codes, scale * 2.0
+
+
+def _quantize_ties_up(c):
+    codes, scale = _orig["quantize_e4m3fn_rows"](np.nextafter(np.asarray(c, np.float64), np.inf))
+    return codes, scale
+
+
 CASES = [
     ("latent_attention", _latent_attention_no_rope, lambda: P.pin_absorbed_vs_explicit(P.small_inputs())),
     ("latent_attention", _latent_attention_scale_on_latent_only,
@@ -78,6 +106,12 @@ CASES = [
     ("decode_e4m3fn", _e4m3_wrong_bias, P.pin_e4m3_table),
     ("decode_bf16", _bf16_low_half, P.pin_bf16_decode),
     ("mha_cache_numbers_per_token", _mha_count_wrong, P.pin_cache_arithmetic),
+    ("rope_rotate", _rope_sin_sign, PC.pin_rope_hand_example),
+    ("rope_rotate", _rope_wrong_frequency, PC.pin_rope_hand_example),
+    ("rope_rotate", _rope_swapped_pairing, PC.pin_rope_hand_example),
+    ("new_token_positions", _positions_off_by_one, PC.pin_cache_append_brute),
+    ("quantize_e4m3fn_rows", _quantize_half_scale, PC.pin_quantize_special),
+    ("quantize_e4m3fn_rows", _quantize_ties_up, PC.pin_quantize_special),
 ]
 
 
