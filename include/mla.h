@@ -156,6 +156,47 @@ mla_status mla_absorb_out(const mla_dims* dims, const void* o_lat, mla_dtype in_
                           const void* w_uv, mla_dtype w_dt, void* out, mla_dtype out_dt,
                           void* stream);
 
+/* ---- cache write of the new tokens (the step before decode) ------------------------
+ * The latent is the only KV state cached ("Operator Notes (1): MLA", section 2:
+ * c_kv = x . W_DKV); next to it sits the small decoupled key that carries the rotary
+ * position ("multi-head latent attention" glossary entry, paragraph on the decoupled RoPE
+ * key).  For new token i (0 <= i < s_q) of sequence b, at position p = seq_lens[b] - s_q + i
+ * (seq_lens counts the new tokens, as in decode):
+ *   c[b,i,:]  = x[b,i,:] . w_dkv                        (d_c wide, fp32 accumulation)
+ *   kr[b,i,:] = RoPE(x[b,i,:] . w_kr, p)                (d_r wide)
+ * RoPE turns pair j of the vector by the angle p * rope_base^(-2j / d_r); the pairs are
+ * (2j, 2j + 1) for MLA_ROPE_INTERLEAVED and (j, j + d_r / 2) for MLA_ROPE_HALF (the pages
+ * name the rotation but print no formula; this is the standard rotary embedding).
+ * Both are written to pool row  block_table[b, p / block_size] * block_size + p % block_size:
+ *   c_kv_pool row   <- c: kv_dt MLA_BF16 rounds to nearest-even; MLA_F32 stores as is;
+ *                      MLA_FP8_E4M3 stores the e4m3fn codes of c / s (nearest-even on the
+ *                      magnitude) with s = max|c| / 448 (1 for an all-zero row), and
+ *                      kv_scale_pool row <- s
+ *   k_rope_pool row <- kr, in dtype x_dt
+ *   x      [B, s_q, d_model]  dtype x_dt (MLA_BF16; MLA_F32 only with an MLA_F32 cache)
+ *   w_dkv  [d_model, d_c]     dtype x_dt
+ *   w_kr   [d_model, d_r]     dtype x_dt (may be NULL when d_r == 0)
+ *   pools, block_table, seq_lens as for mla_decode_paged; s_q <= seq_lens[b] and the
+ *   rows written must lie inside the pool (device-side contracts, not checked).
+ *   d_r must be even.  workspace: at least mla_cache_append_workspace_bytes(dims, d_model)
+ *   bytes of device scratch (fp32 split-K partial sums); contents irrelevant on entry.
+ * Only the rows of the new tokens are written.  Errors as for mla_decode. */
+typedef enum { MLA_ROPE_INTERLEAVED = 0, MLA_ROPE_HALF = 1 } mla_rope_pairing;
+
+size_t mla_cache_append_workspace_bytes(const mla_dims* dims, int32_t d_model);
+mla_status mla_cache_append(const mla_dims* dims, int32_t d_model, const void* x, const void* w_dkv,
+                            const void* w_kr, mla_dtype x_dt, float rope_base, mla_rope_pairing pairing,
+                            void* c_kv_pool, mla_dtype kv_dt, float* kv_scale_pool, void* k_rope_pool,
+                            int32_t n_blocks, int32_t block_size, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Rotary embedding of the query's decoupled part, in place, with the positions above:
+ *   q_rope[b,i,h,:] <- RoPE(q_rope[b,i,h,:], seq_lens[b] - s_q + i)
+ *   q_rope [B, s_q, n_h, d_r]  dtype q_dt (MLA_BF16 or MLA_F32), d_r even; seq_lens [B]. */
+mla_status mla_rope_query(const mla_dims* dims, void* q_rope, mla_dtype q_dt, const int32_t* seq_lens,
+                          float rope_base, mla_rope_pairing pairing, void* stream);
+
 /* ---- utilities -------------------------------------------------------------------- */
 
 /* Copy rows of a block pool into a contiguous per-sequence array (the paged lookup alone):

@@ -28,7 +28,8 @@ DTYPE_CODES = {"f32": MLA_F32, "bf16": MLA_BF16, "fp8": MLA_FP8_E4M3}
 EXPORTED = (
     "mla_absorb_q", "mla_decode", "mla_decode_paged", "mla_decode_workspace_bytes",
     "mla_decode_plan", "mla_absorb_out", "mla_gather_pages", "mla_fp8_e4m3_table",
-    "mla_status_str", "mla_last_hip_error", "mla_version",
+    "mla_status_str", "mla_last_hip_error", "mla_version", "mla_cache_append_workspace_bytes",
+    "mla_cache_append", "mla_rope_query",
 )
 
 
@@ -73,6 +74,10 @@ _SIGNATURES = {
     "mla_decode_plan": [_dims_p, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "mla_gather_pages": [_vp, _i32, _i32, _i64, _vp, _i32, _i32, _vp, _i32, _vp, _vp],
     "mla_fp8_e4m3_table": [_vp, _vp],
+    "mla_cache_append_workspace_bytes": [_dims_p, _i32],
+    "mla_cache_append": [_dims_p, _i32, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp, _i32, _vp, _vp,
+                         _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp],
+    "mla_rope_query": [_dims_p, _vp, _i32, _vp, ctypes.c_float, _i32, _vp],
     "mla_status_str": [_i32],
     "mla_last_hip_error": [],
     "mla_version": [],
@@ -91,6 +96,7 @@ def _lib() -> ctypes.CDLL:
             fn.argtypes = args
             fn.restype = _i32
         lib.mla_decode_workspace_bytes.restype = _sz
+        lib.mla_cache_append_workspace_bytes.restype = _sz
         lib.mla_status_str.restype = ctypes.c_char_p
         _LIB = lib
     return _LIB
@@ -219,6 +225,44 @@ def mla_gather_pages(pool, block_table, seq_lens, max_seq_len: int, dst, *, bloc
                                  max_blocks_per_seq, _ptr(seq_lens), max_seq_len, _ptr(dst),
                                  _stream(stream))
     return _done(st, "mla_gather_pages", check)
+
+
+ROPE_PAIRING = {"interleaved": 0, "half": 1}
+
+
+def mla_cache_append_workspace_bytes(d: MlaDims, d_model: int) -> int:
+    return int(_lib().mla_cache_append_workspace_bytes(ctypes.byref(d), d_model))
+
+
+def mla_cache_append(d: MlaDims, x, w_dkv, w_kr, c_kv_pool, k_rope_pool, block_table, seq_lens, workspace,
+                     *, rope_base: float = 10000.0, pairing: str = "interleaved", kv_scale_pool=None,
+                     workspace_bytes: Optional[int] = None, d_model: Optional[int] = None,
+                     block_size: Optional[int] = None, n_blocks: Optional[int] = None,
+                     max_blocks_per_seq: Optional[int] = None, x_dtype=None, kv_dtype=None,
+                     stream=None, check=True) -> int:
+    if d_model is None:
+        d_model = x.shape[-1]
+    if block_size is None:
+        block_size = c_kv_pool.shape[1]
+    if n_blocks is None:
+        n_blocks = c_kv_pool.shape[0]
+    if max_blocks_per_seq is None:
+        max_blocks_per_seq = block_table.shape[1]
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib().mla_cache_append(
+        ctypes.byref(d), d_model, _ptr(x), _ptr(w_dkv), _ptr(w_kr), _dt(x, x_dtype), rope_base,
+        ROPE_PAIRING[pairing], _ptr(c_kv_pool), _dt(c_kv_pool, kv_dtype), _ptr(kv_scale_pool),
+        _ptr(k_rope_pool), n_blocks, block_size, _ptr(block_table), max_blocks_per_seq, _ptr(seq_lens),
+        _ptr(workspace), workspace_bytes, _stream(stream))
+    return _done(st, "mla_cache_append", check)
+
+
+def mla_rope_query(d: MlaDims, q_rope, seq_lens, *, rope_base: float = 10000.0, pairing: str = "interleaved",
+                   dtype=None, stream=None, check=True) -> int:
+    st = _lib().mla_rope_query(ctypes.byref(d), _ptr(q_rope), _dt(q_rope, dtype), _ptr(seq_lens), rope_base,
+                               ROPE_PAIRING[pairing], _stream(stream))
+    return _done(st, "mla_rope_query", check)
 
 
 def mla_fp8_e4m3_table(out, *, stream=None, check=True) -> int:

@@ -204,6 +204,76 @@ mla_status mla_absorb_out(const mla_dims* d, const void* o_lat, mla_dtype in_dt,
                                   d->d_latent, d->d_head, static_cast<hipStream_t>(stream)));
 }
 
+size_t mla_cache_append_workspace_bytes(const mla_dims* d, int32_t d_model) {
+  if (check_dims(d) != MLA_OK || d_model < 1) return 0;
+  return size_t(cache_append_chunks(d_model)) * size_t(d->batch) * d->q_len *
+         (size_t(d->d_latent) + d->d_rope) * sizeof(float);
+}
+
+mla_status mla_cache_append(const mla_dims* d, int32_t d_model, const void* x, const void* w_dkv,
+                            const void* w_kr, mla_dtype x_dt, float rope_base, mla_rope_pairing pairing,
+                            void* c_kv_pool, mla_dtype kv_dt, float* kv_scale_pool, void* k_rope_pool,
+                            int32_t n_blocks, int32_t block_size, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, const int32_t* seq_lens, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (d_model < 1 || !valid_dtype(x_dt) || !valid_dtype(kv_dt)) return MLA_ERR_INVALID_ARG;
+  if (pairing != MLA_ROPE_INTERLEAVED && pairing != MLA_ROPE_HALF) return MLA_ERR_INVALID_ARG;
+  if (d->d_rope % 2 != 0) return MLA_ERR_INVALID_ARG;
+  if (d->d_rope > 0 && (!(rope_base > 1.f) || !std::isfinite(rope_base))) return MLA_ERR_INVALID_ARG;
+  if (!x || !w_dkv || !c_kv_pool || !block_table || !seq_lens) return MLA_ERR_INVALID_ARG;
+  if (d->d_rope > 0 && (!w_kr || !k_rope_pool)) return MLA_ERR_INVALID_ARG;
+  if (n_blocks < 1 || block_size < 1 || max_blocks_per_seq < 1) return MLA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w_dkv, 16) || (w_kr && !aligned(w_kr, 16)) || !aligned(c_kv_pool, 16) ||
+      (k_rope_pool && !aligned(k_rope_pool, 16)) || !aligned(block_table, 4) || !aligned(seq_lens, 4))
+    return MLA_ERR_INVALID_ARG;
+  if (x_dt == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  if (x_dt == MLA_F32 ? kv_dt != MLA_F32 : kv_dt == MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (kv_dt == MLA_FP8_E4M3 && (!kv_scale_pool || !aligned(kv_scale_pool, 4))) return MLA_ERR_INVALID_ARG;
+  const int64_t M = int64_t(d->batch) * d->q_len;
+  if ((M + 31) / 32 > kMaxGridDim || cache_append_chunks(d_model) > kMaxGridDim) return MLA_ERR_UNSUPPORTED;
+  const size_t need = mla_cache_append_workspace_bytes(d, d_model);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 16)) return MLA_ERR_WORKSPACE;
+  CacheAppendArgs a;
+  a.M = int32_t(M);
+  a.sq = d->q_len;
+  a.d_model = d_model;
+  a.dc = d->d_latent;
+  a.dr = d->d_rope;
+  a.x = x;
+  a.w_dkv = w_dkv;
+  a.w_kr = w_kr;
+  a.x_dt = x_dt;
+  a.kv_dt = kv_dt;
+  a.base = rope_base;
+  a.pairing = int32_t(pairing);
+  a.c_pool = c_kv_pool;
+  a.scale_pool = kv_scale_pool;
+  a.rope_pool = k_rope_pool;
+  a.bs = block_size;
+  a.table = block_table;
+  a.max_blocks = max_blocks_per_seq;
+  a.seq_lens = seq_lens;
+  a.part = static_cast<float*>(workspace);
+  return hip_status(launch_cache_append(a, static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_rope_query(const mla_dims* d, void* q_rope, mla_dtype q_dt, const int32_t* seq_lens,
+                          float rope_base, mla_rope_pairing pairing, void* stream) {
+  mla_status st = check_dims(d);
+  if (st != MLA_OK) return st;
+  if (!valid_dtype(q_dt) || !q_rope || !seq_lens) return MLA_ERR_INVALID_ARG;
+  if (pairing != MLA_ROPE_INTERLEAVED && pairing != MLA_ROPE_HALF) return MLA_ERR_INVALID_ARG;
+  if (d->d_rope < 2 || d->d_rope % 2 != 0 || !(rope_base > 1.f) || !std::isfinite(rope_base))
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(q_rope, 16) || !aligned(seq_lens, 4)) return MLA_ERR_INVALID_ARG;
+  if (q_dt == MLA_FP8_E4M3) return MLA_ERR_UNSUPPORTED;
+  if (int64_t(d->batch) * d->q_len * d->n_heads > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  return hip_status(launch_rope_query(q_rope, q_dt, d->batch, d->q_len, d->n_heads, d->d_rope, rope_base,
+                                      int32_t(pairing), seq_lens, static_cast<hipStream_t>(stream)));
+}
+
 size_t mla_decode_workspace_bytes(const mla_dims* d, mla_dtype kv_dt, int32_t max_seq_len) {
   DecodePlan p;
   mla_dtype q_dt = kv_dt == MLA_F32 ? MLA_F32 : MLA_BF16;

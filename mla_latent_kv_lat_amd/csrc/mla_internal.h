@@ -50,6 +50,25 @@ struct DecodeArgs {
   float* part_lse;       // [B, S, rows] base-2 log-sum-exp of each split (S > 1)
 };
 
+// Everything the cache-write kernels read or write.  Pointers are device pointers.
+struct CacheAppendArgs {
+  int32_t M, sq, d_model, dc, dr;   // M = B * s_q new tokens
+  const void* x;                    // [M, d_model]
+  const void* w_dkv;                // [d_model, dc]
+  const void* w_kr;                 // [d_model, dr]
+  mla_dtype x_dt, kv_dt;
+  float base;
+  int32_t pairing;
+  void* c_pool;                     // [n_blocks * bs, dc]
+  float* scale_pool;                // [n_blocks * bs] (fp8 only)
+  void* rope_pool;                  // [n_blocks * bs, dr]
+  int32_t bs;
+  const int32_t* table;             // [B, max_blocks]
+  int32_t max_blocks;
+  const int32_t* seq_lens;          // [B]
+  float* part;                      // workspace: [chunks, M, dc + dr] fp32
+};
+
 // Host-only validation and planning (mla_api.cpp).
 mla_status check_dims(const mla_dims* d);
 mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
@@ -69,6 +88,10 @@ int launch_gather_pages(const void* pool, int32_t block_size, int64_t row_bytes,
                         const int32_t* table, int32_t B, int32_t max_blocks, const int32_t* seq_lens,
                         int32_t max_seq_len, void* dst, hipStream_t s);
 int launch_fp8_table(float* out, hipStream_t s);
+int64_t cache_append_chunks(int32_t d_model);  // split-K chunks of the projection
+int launch_cache_append(const CacheAppendArgs& a, hipStream_t s);
+int launch_rope_query(void* q, mla_dtype dt, int32_t B, int32_t sq, int32_t H, int32_t dr, float base,
+                      int32_t pairing, const int32_t* seq_lens, hipStream_t s);
 int launch_fp8_bf16_table(float* out, hipStream_t s);
 
 }  // namespace mla

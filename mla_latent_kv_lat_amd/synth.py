@@ -37,7 +37,7 @@ from .configs import MLAConfig
 
 TENSOR_IDS = {
     "c_kv": 0, "k_rope": 1, "q_nope": 2, "q_rope": 3, "w_uk": 4, "w_uv": 5,
-    "lengths": 6, "perm": 7, "q_lat": 8, "o_lat": 9,
+    "lengths": 6, "perm": 7, "q_lat": 8, "o_lat": 9, "x": 10, "w_dkv": 11, "w_kr": 12,
 }
 
 E4M3_MAX = 448.0
@@ -122,6 +122,23 @@ def draw_lengths(cfg: MLAConfig, seed: int) -> np.ndarray:
     return r.integers(cfg.len_min, cfg.seq_len, size=cfg.batch, endpoint=True).astype(np.int32)
 
 
+def paged_layout(cfg: MLAConfig, seed: int, seq_lens: np.ndarray):
+    """Block table of a shared pool: N_blk = sum_b ceil(L_b / bs) blocks, a seeded
+    permutation of the pool dealt out in order; unused slots hold -1.  Returns (table, N_blk)."""
+    bs = cfg.block_size
+    nblk_per = (seq_lens.astype(np.int64) + bs - 1) // bs
+    n_blk = int(nblk_per.sum())
+    max_blocks = (cfg.seq_len + bs - 1) // bs
+    perm = rng_for(seed, cfg.cfg_id, "perm").permutation(n_blk).astype(np.int32)
+    table = np.full((cfg.batch, max_blocks), -1, dtype=np.int32)
+    off = 0
+    for b in range(cfg.batch):
+        n = int(nblk_per[b])
+        table[b, :n] = perm[off:off + n]
+        off += n
+    return table, n_blk
+
+
 def make_inputs(cfg: MLAConfig, seed: int = 0, *, poison_tail: bool = False,
                 q_gain: float = 1.0, lengths: Optional[np.ndarray] = None) -> Inputs:
     B, sq, H = cfg.batch, cfg.q_len, cfg.n_heads
@@ -144,16 +161,7 @@ def make_inputs(cfg: MLAConfig, seed: int = 0, *, poison_tail: bool = False,
 
     if cfg.paged:
         bs = cfg.block_size
-        nblk_per = (seq_lens.astype(np.int64) + bs - 1) // bs
-        n_blk = int(nblk_per.sum())
-        max_blocks = (T + bs - 1) // bs
-        perm = rng_for(seed, cid, "perm").permutation(n_blk).astype(np.int32)
-        table = np.full((B, max_blocks), -1, dtype=np.int32)
-        off = 0
-        for b in range(B):
-            n = int(nblk_per[b])
-            table[b, :n] = perm[off:off + n]
-            off += n
+        table, n_blk = paged_layout(cfg, seed, seq_lens)
         lat_shape, rope_shape = (n_blk, bs, dc), (n_blk, bs, dr)
     else:
         table = None
@@ -203,3 +211,33 @@ def make_stage_input(cfg: MLAConfig, seed: int, name: str, shape, std: float = 1
     """A stand-alone stored activation (e.g. a latent query or a latent output), for
     testing one entry point on its own."""
     return store(normal_f32(seed, cfg.cfg_id, name, shape, std), cfg.act_dtype)
+
+
+@dataclass
+class AppendInputs:
+    """Inputs of the cache-write step: hidden states of the s_q new tokens of every
+    sequence, the down-projection W_DKV [d_model, d_c] and the RoPE-key projection
+    W_KR [d_model, d_r] (both N(0,1) / sqrt(d_model): d_model is their fan-in), and a pool
+    layout in which the new tokens are the last s_q rows of each sequence."""
+    cfg: MLAConfig
+    d_model: int
+    x: np.ndarray          # [B, s_q, d_model] stored
+    w_dkv: np.ndarray      # [d_model, d_c] stored
+    w_kr: np.ndarray       # [d_model, d_r] stored
+    seq_lens: np.ndarray   # [B] int32, counting the new tokens
+    block_table: np.ndarray
+    n_blocks: int
+
+
+def make_append_inputs(cfg: MLAConfig, d_model: int, seed: int = 0) -> AppendInputs:
+    B, sq, dc, dr = cfg.batch, cfg.q_len, cfg.d_latent, cfg.d_rope
+    cid = cfg.cfg_id
+    w_std = 1.0 / float(d_model) ** 0.5
+    x = normal_f32(seed, cid, "x", (B, sq, d_model))
+    w_dkv = normal_f32(seed, cid, "w_dkv", (d_model, dc), w_std)
+    w_kr = normal_f32(seed, cid, "w_kr", (d_model, dr), w_std)
+    seq_lens = np.maximum(draw_lengths(cfg, seed), sq).astype(np.int32)
+    table, n_blk = paged_layout(cfg, seed, seq_lens)
+    act = cfg.act_dtype
+    return AppendInputs(cfg=cfg, d_model=d_model, x=store(x, act), w_dkv=store(w_dkv, act),
+                        w_kr=store(w_kr, act), seq_lens=seq_lens, block_table=table, n_blocks=n_blk)

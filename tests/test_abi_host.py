@@ -199,3 +199,69 @@ def test_plan_honours_split_tokens():
         d = L.dims_from_config(cfg, split_tokens=st)
         n, tok = L.mla_decode_plan(d, "bf16", cfg.seq_len)
         assert tok >= st and (n - 1) * tok < cfg.seq_len <= n * tok
+
+
+# ---- cache write and query rotation: argument checks (no launch) ----------------------
+
+def append_call(d=None, **kw):
+    """mla_cache_append with fake device addresses; every case below fails validation."""
+    args = dict(d_model=5120, x=A, w_dkv=A, w_kr=A, x_dt=L.MLA_BF16, base=10000.0, pairing=0,
+                c_pool=A, kv_dt=L.MLA_BF16, scale_pool=None, rope_pool=A, n_blocks=100, bs=64,
+                table=A, max_blocks=64, seq_lens=A, ws=None, ws_bytes=0)
+    args.update(kw)
+    d = d or v2()
+    return L.library().mla_cache_append(
+        ctypes.byref(d), args["d_model"], args["x"], args["w_dkv"], args["w_kr"], args["x_dt"],
+        args["base"], args["pairing"], args["c_pool"], args["kv_dt"], args["scale_pool"],
+        args["rope_pool"], args["n_blocks"], args["bs"], args["table"], args["max_blocks"],
+        args["seq_lens"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(d_model=0), L.MLA_ERR_INVALID_ARG),
+    (dict(pairing=2), L.MLA_ERR_INVALID_ARG),
+    (dict(base=1.0), L.MLA_ERR_INVALID_ARG),
+    (dict(base=float("nan")), L.MLA_ERR_INVALID_ARG),
+    (dict(x=None), L.MLA_ERR_INVALID_ARG),
+    (dict(w_kr=None), L.MLA_ERR_INVALID_ARG),
+    (dict(table=None), L.MLA_ERR_INVALID_ARG),
+    (dict(bs=0), L.MLA_ERR_INVALID_ARG),
+    (dict(x=A + 8), L.MLA_ERR_INVALID_ARG),
+    (dict(x_dt=L.MLA_FP8_E4M3), L.MLA_ERR_UNSUPPORTED),
+    (dict(x_dt=L.MLA_F32), L.MLA_ERR_UNSUPPORTED),          # f32 activations need an f32 cache
+    (dict(kv_dt=L.MLA_F32), L.MLA_ERR_UNSUPPORTED),         # bf16 activations, f32 cache
+    (dict(kv_dt=L.MLA_FP8_E4M3), L.MLA_ERR_INVALID_ARG),    # fp8 needs the scale pool
+    (dict(), L.MLA_ERR_WORKSPACE),                          # no workspace
+    (dict(ws=A, ws_bytes=16), L.MLA_ERR_WORKSPACE),         # too small
+])
+def test_cache_append_argument_errors(kw, status):
+    assert append_call(**kw) == status
+
+
+def test_cache_append_odd_rope_width_rejected():
+    assert append_call(d=v2(d_rope=63)) == L.MLA_ERR_INVALID_ARG
+
+
+def test_cache_append_workspace_formula():
+    d = v2()
+    # split-K chunks of 256 over d_model, fp32 partial rows of d_c + d_r per new token
+    assert L.mla_cache_append_workspace_bytes(d, 5120) == 20 * 32 * 1 * 576 * 4
+    assert L.mla_cache_append_workspace_bytes(d, 100) == 1 * 32 * 576 * 4
+    assert L.mla_cache_append_workspace_bytes(d, 0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), L.MLA_ERR_INVALID_ARG),
+    (dict(seq_lens=None), L.MLA_ERR_INVALID_ARG),
+    (dict(pairing=5), L.MLA_ERR_INVALID_ARG),
+    (dict(base=0.5), L.MLA_ERR_INVALID_ARG),
+    (dict(dt=L.MLA_FP8_E4M3), L.MLA_ERR_UNSUPPORTED),
+    (dict(q=A + 4), L.MLA_ERR_INVALID_ARG),
+])
+def test_rope_query_argument_errors(kw, status):
+    args = dict(q=A, dt=L.MLA_BF16, seq_lens=A, base=10000.0, pairing=0)
+    args.update(kw)
+    d = v2()
+    st = L.library().mla_rope_query(ctypes.byref(d), args["q"], args["dt"], args["seq_lens"], args["base"],
+                                    args["pairing"], None)
+    assert st == status
