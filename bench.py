@@ -127,6 +127,80 @@ def cpu_baseline(inp, budget_s: float) -> dict:
                       f"{secs:.2f} s wall"}
 
 
+def bench_cache_append(args, cfg) -> int:
+    """Time mla_cache_append alone: the new tokens' projection onto W_DKV / W_KR, rotation
+    and scatter into a paged pool.  HBM-bound on the two weight matrices."""
+    import torch
+    from mla_latent_kv_lat_amd import capi, synth
+    from mla_latent_kv_lat_amd.runner import to_device
+    dm = args.d_model
+    inp = synth.make_append_inputs(cfg, dm, 0)
+    act, kv = cfg.act_dtype, cfg.kv_dtype
+    dc, dr, bs, M = cfg.d_latent, cfg.d_rope, cfg.block_size, cfg.batch * cfg.q_len
+    ab = 4 if act == "f32" else 2
+    kb = {"f32": 4, "bf16": 2, "fp8": 1}[kv]
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}
+    x = to_device(inp.x, act, "cuda")
+    reps = []
+    for _ in range(max(1, args.replicas)):  # weight replicas, cycled: streamed from HBM each call
+        reps.append((to_device(inp.w_dkv, act, "cuda"), to_device(inp.w_kr, act, "cuda")))
+    c_pool = torch.zeros((inp.n_blocks, bs, dc), dtype=tdt[kv], device="cuda")
+    r_pool = torch.zeros((inp.n_blocks, bs, dr), dtype=tdt[act], device="cuda")
+    s_pool = torch.zeros((inp.n_blocks, bs), dtype=torch.float32, device="cuda") if kv == "fp8" else None
+    table = to_device(inp.block_table, "i32", "cuda")
+    lens = to_device(inp.seq_lens, "i32", "cuda")
+    d = capi.dims_from_config(cfg)
+    ws = torch.empty(capi.mla_cache_append_workspace_bytes(d, dm), dtype=torch.uint8, device="cuda")
+
+    def call(k):
+        wd, wk = reps[k % len(reps)]
+        capi.mla_cache_append(d, x, wd, wk, c_pool, r_pool, table, lens, ws, kv_scale_pool=s_pool,
+                              kv_dtype=capi.DTYPE_CODES[kv])
+
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < args.ramp_ms:
+        for _ in range(20):
+            call(n)
+            n += 1
+        torch.cuda.synchronize()
+    for k in range(args.warmup):
+        call(k)
+    torch.cuda.synchronize()
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(K):
+        ev[k][0].record()
+        call(k)
+        ev[k][1].record()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    weight_bytes = dm * (dc + dr) * ab
+    alg_bytes = weight_bytes + M * dm * ab + M * (dc * kb + dr * ab + (4 if kv == "fp8" else 0))
+    flops = 2.0 * M * dm * (dc + dr)
+    achieved = alg_bytes / (call_ms * 1e-3) / 1e9
+    print(f"[bench] cache_append {cfg.name} d_model={dm}: {call_ms * 1e3:.2f} us/call", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "MLA cache append (new-token latent + rotated RoPE key into the paged pool) GB/s",
+        "value": round(alg_bytes / (ms * 1e-3) / 1e9, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "clock_ramp": {"ms": args.ramp_ms, "steps": n},
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if act == "bf16" else "f32",
+        "data": "synthetic (seeded Gaussian hidden states and random-init projections)",
+        "config": {"workload": f"cache_append_{cfg.name}_dmodel{dm}", "batch": cfg.batch, "q_len": cfg.q_len,
+                   "d_model": dm, "d_latent": dc, "d_rope": dr, "kv_dtype": kv, "block_size": bs,
+                   "weight_replicas": len(reps)},
+        "call_us": round(call_ms * 1e3, 3), "tflops": round(flops / (call_ms * 1e-3) / 1e12, 3),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,11 +216,15 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
+    ap.add_argument("--stage", choices=("step", "cache_append"), default="step",
+                    help="step: absorb_q + decode + absorb_out (the headline); cache_append: the "
+                         "cache write of the new tokens alone")
+    ap.add_argument("--d-model", type=int, default=5120, help="hidden width for --stage cache_append")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the decode path is "
-              "not sharded across GPUs in this build.", file=sys.stderr)
+              "not sharded across GPUs.", file=sys.stderr)
         return 2
 
     import torch
@@ -154,6 +232,8 @@ def main() -> int:
     from mla_latent_kv_lat_amd.runner import DeviceWorkload
 
     cfg = configs.BY_NAME[args.workload] if args.workload else configs.HEADLINE
+    if args.stage == "cache_append":
+        return bench_cache_append(args, cfg)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, 0)
     wc = work_counts(cfg, inp.seq_lens)

@@ -35,14 +35,25 @@ __device__ __forceinline__ void load_x_block(bf16x8 (&bv)[K / 32], const uint16_
 // to the 8 XCDs round-robin, and the head is the fastest grid dimension: with H a multiple
 // of 8, all column tiles (and row groups) of one head run on one XCD and share its
 // activation rows (and weight slice) through that XCD's L2.
-template <int K, int MG>
+// F32OUT: y holds fp32 sums (the split-K partials of the cache-write projection) instead of
+// bf16 results.  Column tiles from N / 64 on take a second weight matrix w2 [H, K, N2] and
+// output y2 [M, H, N2] (N2 a multiple of 64; the grid then has N / 64 + N2 / 64 column tiles).
+template <int K, int MG, bool F32OUT = false>
 __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* __restrict__ x,
                                                                const uint16_t* __restrict__ w,
-                                                               uint16_t* __restrict__ y, int M,
-                                                               int H, int N) {
+                                                               void* __restrict__ y, int M,
+                                                               int H, int N,
+                                                               const uint16_t* __restrict__ w2 = nullptr,
+                                                               void* __restrict__ y2 = nullptr, int N2 = 0) {
   constexpr int kBlocks = MG / 16;
   __shared__ __attribute__((aligned(16))) uint16_t wt[K * kBN];  // [k][64], chunks swizzled
-  const int h = blockIdx.x, n0 = blockIdx.y * kBN, m0 = blockIdx.z * MG;
+  int h = blockIdx.x, n0 = blockIdx.y * kBN, m0 = blockIdx.z * MG;
+  if (n0 >= N) {  // a tile of the second matrix (workgroup-uniform)
+    n0 -= N;
+    w = w2;
+    y = y2;
+    N = N2;
+  }
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, mm = lane & 15;
 
@@ -73,14 +84,35 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
                                                     acc, 0, 0, 0);
     const int m = m0 + 16 * i + mm;
     if (m < M) {
-      const uint32_t w0 = uint32_t(f32_to_bf16_bits(acc[0])) | (uint32_t(f32_to_bf16_bits(acc[1])) << 16);
-      const uint32_t w1 = uint32_t(f32_to_bf16_bits(acc[2])) | (uint32_t(f32_to_bf16_bits(acc[3])) << 16);
-      *reinterpret_cast<u32x2*>(y + (int64_t(m) * H + h) * N + n0 + 16 * wv + 4 * g) = u32x2{w0, w1};
+      const int64_t off = (int64_t(m) * H + h) * N + n0 + 16 * wv + 4 * g;
+      if constexpr (F32OUT) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = acc;
+      } else {
+        const uint32_t w0 = uint32_t(f32_to_bf16_bits(acc[0])) | (uint32_t(f32_to_bf16_bits(acc[1])) << 16);
+        const uint32_t w1 = uint32_t(f32_to_bf16_bits(acc[2])) | (uint32_t(f32_to_bf16_bits(acc[3])) << 16);
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + off) = u32x2{w0, w1};
+      }
     }
   }
 }
 
 }  // namespace
+
+bool proj_mfma_supported(int32_t M, int32_t K_total, int32_t N) {
+  return K_total % 256 == 0 && N % kBN == 0 && M <= 32 * 65535;
+}
+
+// part[m, kc, n] = sum_{k < 256} x[m, 256 kc + k] * w[256 kc + k, n] (and part2 likewise
+// with w2, N2 columns; N2 may be 0): the per-head kernel with the K chunks of x and w taken
+// as the heads, fp32 out, both matrices in one launch.
+int launch_proj_mfma(const void* x, const void* w, float* part, int32_t N, const void* w2, float* part2,
+                     int32_t N2, int32_t M, int32_t K_total, hipStream_t s) {
+  const int KC = K_total / 256;
+  hipLaunchKernelGGL((absorb_mfma_kernel<256, 32, true>), dim3(KC, (N + N2) / kBN, (M + 31) / 32), dim3(kThreads),
+                     0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), part, M, KC, N,
+                     static_cast<const uint16_t*>(w2), part2, N2);
+  return int(hipGetLastError());
+}
 
 bool absorb_mfma_supported(mla_dtype dt, int32_t M, int32_t K, int32_t N) {
   // The row groups are the grid's z dimension (at most 65535 groups of 32 rows).

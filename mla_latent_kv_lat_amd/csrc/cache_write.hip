@@ -7,10 +7,14 @@
 // stored at the token's row of the paged pool (fp8 caches store per-token scaled e4m3
 // codes of c).
 //
-// Two kernels: a split-K projection (x rows against the [d_model, d_c + d_r] pair of
-// weights; one lane per output column, 8 rows per wave, fp32 partial sums per K chunk,
-// so that many workgroups stream the weights for the few rows of a decode step), then a
-// finalize kernel per row that sums the partials, rotates the key, encodes and scatters.
+// A split-K projection (the few rows of a decode step against the two weight matrices,
+// fp32 partial sums per 256-wide K chunk, so that many workgroups stream the weights), then
+// a finalize kernel per row that sums the partials, rotates the key, encodes and scatters.
+// bf16 projections with d_model a multiple of 256 and d_c, d_r multiples of 64 run on the
+// matrix-core per-head kernel (the K chunks as heads); the rest on a VALU kernel (one lane
+// per output column, 8 rows per wave).  Partials: [M, chunks, d_c] then [M, chunks, d_r].
+#include <algorithm>
+
 #include "device_common.h"
 #include "mla_internal.h"
 
@@ -21,14 +25,16 @@ constexpr int kPN = 64;   // output columns per projection workgroup (one per la
 constexpr int kPM = 32;   // rows per projection workgroup (8 per wave)
 constexpr int kPK = 256;  // K per projection workgroup (one split-K chunk)
 
-// part[kc][m][n] = sum_{k in chunk kc} x[m][k] * W[k][n], W = [w_dkv | w_kr].
+// part_c[m][kc][n] (n < dc) and part_r[m][kc][n - dc] = sum_{k in chunk kc} x[m][k] * W[k][n],
+// W = [w_dkv | w_kr].
 template <typename S>
 __global__ __launch_bounds__(256) void proj_partial_kernel(const typename S::raw* __restrict__ x,
                                                            const typename S::raw* __restrict__ w_dkv,
                                                            const typename S::raw* __restrict__ w_kr,
                                                            int M, int K, int dc, int dr,
-                                                           float* __restrict__ part) {
+                                                           float* __restrict__ part_c, float* __restrict__ part_r) {
   const int N = dc + dr;
+  const int KC = gridDim.y;
   const int lane = threadIdx.x & 63;
   const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = blockIdx.x * kPN + lane;
@@ -50,7 +56,10 @@ __global__ __launch_bounds__(256) void proj_partial_kernel(const typename S::raw
   if (n < N) {
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-      if (m0 + r < M) part[(int64_t(kc) * M + m0 + r) * N + n] = acc[r];
+      if (m0 + r < M) {
+        if (n < dc) part_c[(int64_t(m0 + r) * KC + kc) * dc + n] = acc[r];
+        else part_r[(int64_t(m0 + r) * KC + kc) * dr + (n - dc)] = acc[r];
+      }
   }
 }
 
@@ -75,29 +84,45 @@ __device__ __forceinline__ void rope_pair(int j, int dr, int pairing, int& ia, i
   }
 }
 
-// One wave per new token: sum the split-K partials, rotate the key, encode the latent and
-// write both to the token's pool row.
+// One workgroup per new token, one thread per output column: sum the split-K partials
+// (loaded 16 chunks at a time, so the loads of a batch are in flight together), rotate the
+// key, encode the latent and write both to the token's pool row.
+constexpr int kFinBatch = 16;
+
 template <typename XS, typename KVS>
-__global__ __launch_bounds__(64) void append_finalize_kernel(const float* __restrict__ part, int KC, int M,
-                                                             int sq, int dc, int dr, float base, int pairing,
-                                                             void* c_pool, float* scale_pool, void* rope_pool,
-                                                             int bs, const int32_t* __restrict__ table,
-                                                             int max_blocks, const int32_t* __restrict__ seq_lens) {
-  extern __shared__ float rowv[];  // [d_c + d_r]
-  const int m = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(1024) void append_finalize_kernel(const float* __restrict__ part_c,
+                                                               const float* __restrict__ part_r, int KC, int M,
+                                                               int sq, int dc, int dr, float base, int pairing,
+                                                               void* c_pool, float* scale_pool, void* rope_pool,
+                                                               int bs, const int32_t* __restrict__ table,
+                                                               int max_blocks, const int32_t* __restrict__ seq_lens) {
+  extern __shared__ float rowv[];  // [d_c + d_r], then one slot per wave for the max
+  float* red = rowv + dc + dr;
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nwaves = blockDim.x >> 6;
   const int b = m / sq, i = m - b * sq;
   const int pos = seq_lens[b] - sq + i;
   const int64_t prow = int64_t(table[int64_t(b) * max_blocks + pos / bs]) * bs + pos % bs;
   const int N = dc + dr;
   float amax = 0.f;
-  for (int n = lane; n < N; n += 64) {
+  for (int n = tid; n < N; n += blockDim.x) {
+    const float* src = n < dc ? part_c + int64_t(m) * KC * dc + n : part_r + int64_t(m) * KC * dr + (n - dc);
+    const int stride = n < dc ? dc : dr;
     float s = 0.f;
-    for (int kc = 0; kc < KC; ++kc) s += part[(int64_t(kc) * M + m) * N + n];
+    for (int k0 = 0; k0 < KC; k0 += kFinBatch) {
+      float v[kFinBatch];
+#pragma unroll
+      for (int k = 0; k < kFinBatch; ++k) v[k] = k0 + k < KC ? src[int64_t(min(k0 + k, KC - 1)) * stride] : 0.f;
+#pragma unroll
+      for (int k = 0; k < kFinBatch; ++k) s += v[k];
+    }
     rowv[n] = s;
     if (n < dc) amax = fmaxf(amax, fabsf(s));
   }
+  amax = wave_max(amax);
+  if (lane == 0) red[wave] = amax;
   __syncthreads();
-  for (int j = lane; j < dr / 2; j += 64) {
+  for (int j = tid; j < dr / 2; j += blockDim.x) {
     int ia, ib;
     rope_pair(j, dr, pairing, ia, ib);
     float c, s;
@@ -109,13 +134,14 @@ __global__ __launch_bounds__(64) void append_finalize_kernel(const float* __rest
   __syncthreads();
   using XR = typename XS::raw;
   XR* rp = static_cast<XR*>(rope_pool) + prow * dr;
-  for (int n = lane; n < dr; n += 64) store_from_f32<XS>(rp, n, rowv[dc + n]);
+  for (int n = tid; n < dr; n += blockDim.x) store_from_f32<XS>(rp, n, rowv[dc + n]);
   if constexpr (sizeof(typename KVS::raw) == 1) {
-    amax = wave_max(amax);
+    amax = red[0];
+    for (int w = 1; w < nwaves; ++w) amax = fmaxf(amax, red[w]);
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
-    if (lane == 0) scale_pool[prow] = scale;
+    if (tid == 0) scale_pool[prow] = scale;
     uint8_t* cp = static_cast<uint8_t*>(c_pool) + prow * dc;
-    for (int n = lane; n < dc; n += 64) {
+    for (int n = tid; n < dc; n += blockDim.x) {
       // Nearest-even e4m3fn (OCP) conversion of the gfx950 instruction; |y| <= 448 up to
       // the rounding of the division, clamped so that no code saturates to NaN.
       const float y = fminf(fmaxf(rowv[n] / scale, -448.f), 448.f);
@@ -124,7 +150,7 @@ __global__ __launch_bounds__(64) void append_finalize_kernel(const float* __rest
   } else {
     using KR = typename KVS::raw;
     KR* cp = static_cast<KR*>(c_pool) + prow * dc;
-    for (int n = lane; n < dc; n += 64) store_from_f32<KVS>(cp, n, rowv[n]);
+    for (int n = tid; n < dc; n += blockDim.x) store_from_f32<KVS>(cp, n, rowv[n]);
   }
 }
 
@@ -154,19 +180,28 @@ int64_t cache_append_chunks(int32_t d_model) { return (int64_t(d_model) + kPK - 
 int launch_cache_append(const CacheAppendArgs& a, hipStream_t s) {
   const int N = a.dc + a.dr;
   const int KC = int(cache_append_chunks(a.d_model));
-  const dim3 grid((N + kPN - 1) / kPN, KC, (a.M + kPM - 1) / kPM);
-  if (a.x_dt == MLA_F32)
-    hipLaunchKernelGGL(proj_partial_kernel<F32>, grid, dim3(256), 0, s, static_cast<const float*>(a.x),
-                       static_cast<const float*>(a.w_dkv), static_cast<const float*>(a.w_kr), a.M, a.d_model,
-                       a.dc, a.dr, a.part);
-  else
-    hipLaunchKernelGGL(proj_partial_kernel<BF16>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.x),
-                       static_cast<const uint16_t*>(a.w_dkv), static_cast<const uint16_t*>(a.w_kr), a.M,
-                       a.d_model, a.dc, a.dr, a.part);
-  if (int e = int(hipGetLastError())) return e;
-  const size_t lds = sizeof(float) * N;
+  float* part_c = a.part;
+  float* part_r = a.part + int64_t(a.M) * KC * a.dc;
+  const bool mfma = a.x_dt == MLA_BF16 && proj_mfma_supported(a.M, a.d_model, a.dc) &&
+                    (a.dr == 0 || proj_mfma_supported(a.M, a.d_model, a.dr));
+  if (mfma) {
+    if (int e = launch_proj_mfma(a.x, a.w_dkv, part_c, a.dc, a.w_kr, part_r, a.dr, a.M, a.d_model, s)) return e;
+  } else {
+    const dim3 grid((N + kPN - 1) / kPN, KC, (a.M + kPM - 1) / kPM);
+    if (a.x_dt == MLA_F32)
+      hipLaunchKernelGGL(proj_partial_kernel<F32>, grid, dim3(256), 0, s, static_cast<const float*>(a.x),
+                         static_cast<const float*>(a.w_dkv), static_cast<const float*>(a.w_kr), a.M, a.d_model,
+                         a.dc, a.dr, part_c, part_r);
+    else
+      hipLaunchKernelGGL(proj_partial_kernel<BF16>, grid, dim3(256), 0, s, static_cast<const uint16_t*>(a.x),
+                         static_cast<const uint16_t*>(a.w_dkv), static_cast<const uint16_t*>(a.w_kr), a.M,
+                         a.d_model, a.dc, a.dr, part_c, part_r);
+    if (int e = int(hipGetLastError())) return e;
+  }
+  const int fin_threads = std::min(1024, (N + 63) / 64 * 64);
+  const size_t lds = sizeof(float) * (N + 16);
 #define MLA_FIN(XS, KVS)                                                                                    \
-  hipLaunchKernelGGL((append_finalize_kernel<XS, KVS>), dim3(a.M), dim3(64), lds, s, a.part, KC, a.M, a.sq, \
+  hipLaunchKernelGGL((append_finalize_kernel<XS, KVS>), dim3(a.M), dim3(fin_threads), lds, s, part_c, part_r, KC, a.M, a.sq, \
                      a.dc, a.dr, a.base, a.pairing, a.c_pool, a.scale_pool, a.rope_pool, a.bs, a.table,      \
                      a.max_blocks, a.seq_lens)
   if (a.x_dt == MLA_F32)

@@ -66,7 +66,7 @@ struct CacheAppendArgs {
   const int32_t* table;             // [B, max_blocks]
   int32_t max_blocks;
   const int32_t* seq_lens;          // [B]
-  float* part;                      // workspace: [chunks, M, dc + dr] fp32
+  float* part;                      // workspace: [M, chunks, dc] then [M, chunks, dr] fp32
 };
 
 // Host-only validation and planning (mla_api.cpp).
@@ -89,6 +89,9 @@ int launch_gather_pages(const void* pool, int32_t block_size, int64_t row_bytes,
                         int32_t max_seq_len, void* dst, hipStream_t s);
 int launch_fp8_table(float* out, hipStream_t s);
 int64_t cache_append_chunks(int32_t d_model);  // split-K chunks of the projection
+bool proj_mfma_supported(int32_t M, int32_t K_total, int32_t N);
+int launch_proj_mfma(const void* x, const void* w, float* part, int32_t N, const void* w2, float* part2,
+                     int32_t N2, int32_t M, int32_t K_total, hipStream_t s);
 int launch_cache_append(const CacheAppendArgs& a, hipStream_t s);
 int launch_rope_query(void* q, mla_dtype dt, int32_t B, int32_t sq, int32_t H, int32_t dr, float base,
                       int32_t pairing, const int32_t* seq_lens, hipStream_t s);
