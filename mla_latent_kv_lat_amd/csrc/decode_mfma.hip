@@ -17,19 +17,20 @@
 // side, 32 query rows on the other).
 //   * score waves 0-3: wave p owns latent columns [128p, 128p + 128) and RoPE dims
 //     [16p, 16p + 16).  It streams exactly that slice of every cache row from HBM into
-//     registers, two tiles ahead, with coalesced loads (whole row slices per load); stages
-//     the tile's slice in LDS (swizzled; the output waves read it there too) and refills
-//     the registers at once; computes partial scores (MFMA, cache slice read back from LDS
-//     as the A operand, query slice as the B operand) into LDS.
+//     registers, two tiles ahead; stages the tile's slice in LDS as bf16 (swizzled; the
+//     output waves read it there as V); computes partial scores (MFMA, cache slice as the
+//     A operand, query slice as the B operand, held in registers for the whole split)
+//     into LDS.
 //   * output waves 4-7: wave 4 + q owns output columns [128q, 128q + 128) for all 64
-//     rows and accumulates O^T += V^T P^T for the previous tile (MFMA, cache slice read
-//     transposed from LDS as the A operand, probabilities as the B operand).
+//     rows and accumulates O^T += V^T P^T (MFMA, cache slice read transposed from LDS as
+//     the A operand, probabilities as the B operand).
 //   * all eight waves share the online softmax: wave w sums the four partial scores of
 //     rows [8w, 8w + 8) and publishes their bf16 probabilities.
-// Each step has two barriers.  Half A: score waves run phase 1 of tile n while output
-// waves rescale and start PV of tile n - 1.  Half B: every wave runs its rows' softmax
-// of tile n while output waves also finish PV of tile n - 1.  Slices and probabilities
-// are double buffered in LDS.  The cache is read from HBM once per workgroup.
+// The three stages are pipelined over the tiles with one barrier per step: in step n the
+// score waves stage and score tile n + 1, every wave runs the softmax of tile n, and the
+// output waves multiply tile n - 1 (whose V^T operands they read from LDS in step n - 1)
+// and read the operands of tile n.  Slices, partial scores and probabilities are double
+// buffered in LDS.  The cache is read from HBM once per workgroup.
 //
 // Softmax runs in base-2 units (scores times softmax_scale * log2(e), exponentials by the
 // hardware base-2 exponential; results that would be denormal flush to 0) against a per-row
@@ -53,7 +54,6 @@ constexpr int kThreads = 512;           // 4 score waves + 4 output waves
 constexpr int kCols = 128;              // latent columns per score wave / output wave
 constexpr int kRopeW = 16;              // RoPE dims per score wave
 constexpr int kPPitch = kTile + 8;      // bf16 per row of the probability tile
-constexpr int kSplitA = 4;              // output column blocks (of 4) done in half A
 // A row's reference max (the value its probabilities are taken relative to) only moves
 // when a tile's max exceeds it by more than this many base-2 units, so probabilities stay
 // below 2^kTau and the output waves almost never have to rescale their accumulators.
@@ -61,8 +61,8 @@ constexpr int kSplitA = 4;              // output column blocks (of 4) done in h
 constexpr float kTau = 8.f;
 
 struct alignas(16) Smem {
-  float spart[4][kRows][kTile];         // partial S of each score wave, [row][tok], swizzled
-  uint16_t v[2][4][kTile][kCols];       // cache slices (double buffered), swz32 chunks
+  float spart[2][4][kRows][kTile];      // partial S of each score wave (double buffered), swizzled
+  uint16_t v[2][4][kTile][kCols];       // staged cache slices (double buffered), swz32 chunks
   uint16_t p[2][kRows][kPPitch];        // probabilities (double buffered), [row][tok]
   float ts[2][4][kTile];                // fp8 per-token scales, one copy per score wave
   float alpha[2][kRows];                // per-row rescale factor of each buffered tile
@@ -90,9 +90,9 @@ struct SoftmaxLane {
 template <bool FP8>
 __device__ __forceinline__ void softmax_tile(Smem& sm, SoftmaxLane& st, int buf, int t0, float scale_log2) {
   const int ch = 4 * (st.tg ^ sp_swz(st.row));
-  f32x4 sv4 = *reinterpret_cast<const f32x4*>(&sm.spart[0][st.row][ch]);
+  f32x4 sv4 = *reinterpret_cast<const f32x4*>(&sm.spart[buf][0][st.row][ch]);
 #pragma unroll
-  for (int q = 1; q < 4; ++q) sv4 += *reinterpret_cast<const f32x4*>(&sm.spart[q][st.row][ch]);
+  for (int q = 1; q < 4; ++q) sv4 += *reinterpret_cast<const f32x4*>(&sm.spart[buf][q][st.row][ch]);
   float sv[4] = {sv4[0], sv4[1], sv4[2], sv4[3]};
   if (t0 + kTile > st.lim_w) {
 #pragma unroll
@@ -130,11 +130,14 @@ __device__ __forceinline__ int kcol(int s, int h) { return 32 * (s >> 1) + 16 * 
 template <bool FP8>
 struct TileRegs;
 
-// A score wave's tile registers.  The latent slice is loaded coalesced: load k covers
-// whole 256-byte (bf16) or 128-byte (fp8) row slices of consecutive tokens, 16 bytes per
-// lane, so each load instruction touches few cache lines; the slice then goes through LDS,
-// where the score product reads it back in operand layout.  The RoPE slice is loaded in
-// operand layout directly (token n = lane % 32, dims 8h .. 8h + 7 of the wave's 16).
+// A score wave's tile registers.  A bf16 latent slice is loaded coalesced: load k covers
+// whole 256-byte row slices of 4 consecutive tokens, 16 bytes per lane, so each load
+// instruction touches few cache lines; the slice then goes through LDS, where the score
+// product reads it back in operand layout.  An fp8 slice is half as many bytes and its
+// tiles are compute-bound: it is loaded in operand layout (token n = lane % 32, the 16
+// codes of k-steps 2k and 2k + 1 of lane half h), converted in registers and used as the
+// score operand directly; LDS only gets the converted copy for the output waves.  The
+// RoPE slice is loaded in operand layout (dims 8h .. 8h + 7 of the wave's 16).
 template <>
 struct TileRegs<false> {
   u32x4 lat[8];      // load k: token 4k + lane / 16, columns 8 (lane % 16) + (0..7)
@@ -143,13 +146,13 @@ struct TileRegs<false> {
 
 template <>
 struct TileRegs<true> {
-  u32x4 lat[4];      // load k: token 8k + lane / 8, columns 16 (lane % 8) + (0..15), fp8 codes
+  u32x4 lat[4];      // load k: token lane % 32, columns 32k + 16h + (0..15), fp8 codes
   u32x4 rope;
   float ts;          // scale of token lane % 32
 };
 
-// Token held by load k of this lane.
-__device__ __forceinline__ int lat_token(bool fp8, int k, int lane) { return fp8 ? 8 * k + (lane >> 3) : 4 * k + (lane >> 4); }
+// Token held by load k of this lane (bf16 caches).
+__device__ __forceinline__ int lat_token(int k, int lane) { return 4 * k + (lane >> 4); }
 
 struct Ctx {
   int b, lane, n, h, w;
@@ -220,19 +223,27 @@ __device__ __forceinline__ void load_tile(TileRegs<FP8>& r, const Ctx& c, const 
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(lat_base, nrows * kLatBytes);
     const __amdgpu_buffer_rsrc_t rr = make_rsrc(rope_base, nrows * kRopeBytes);
     const uint32_t row = row0 + uint32_t(c.n);
-    const uint32_t col_off = (kLatBytes / 4) * c.w + 16 * (FP8 ? (c.lane & 7) : (c.lane & 15));
+    const uint32_t col0 = (kLatBytes / 4) * c.w;  // the wave's slice
 #pragma unroll
-    for (int k = 0; k < (FP8 ? 4 : 8); ++k)
-      r.lat[k] = buf_ld16(rl, (row0 + uint32_t(lat_token(FP8, k, c.lane))) * kLatBytes + col_off);
+    for (int k = 0; k < (FP8 ? 4 : 8); ++k) {
+      if constexpr (FP8)
+        r.lat[k] = buf_ld16(rl, row * kLatBytes + col0 + 32 * k + 16 * c.h);
+      else
+        r.lat[k] = buf_ld16(rl, (row0 + uint32_t(lat_token(k, c.lane))) * kLatBytes + col0 + 16 * (c.lane & 15));
+    }
     if constexpr (FP8) r.ts = buf_ld4f(make_rsrc(sc_base, nrows * 4), row * 4);
     r.rope = buf_ld16(rr, row * kRopeBytes + 2 * (kRopeW * c.w + 8 * c.h));
   } else {
     const char* lat = static_cast<const char*>(a.c_kv);
-    const int64_t col_off = (kLatBytes / 4) * c.w + 16 * (FP8 ? (c.lane & 7) : (c.lane & 15));
-#pragma unroll
-    for (int k = 0; k < (FP8 ? 4 : 8); ++k)
-      r.lat[k] = ld16(lat + any_row(c, t0 + lat_token(FP8, k, c.lane)) * kLatBytes + col_off);
+    const int64_t col0 = (kLatBytes / 4) * c.w;
     const int64_t row = any_row(c, t0 + c.n);
+#pragma unroll
+    for (int k = 0; k < (FP8 ? 4 : 8); ++k) {
+      if constexpr (FP8)
+        r.lat[k] = ld16(lat + row * kLatBytes + col0 + 32 * k + 16 * c.h);
+      else
+        r.lat[k] = ld16(lat + any_row(c, t0 + lat_token(k, c.lane)) * kLatBytes + col0 + 16 * (c.lane & 15));
+    }
     if constexpr (FP8) r.ts = a.kv_scale[row];
     r.rope = ld16(static_cast<const uint16_t*>(a.k_rope) + row * kDR + kRopeW * c.w + 8 * c.h);
   }
@@ -274,18 +285,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
   const bool single = num_splits == 1;
 
   // Softmax ownership (all eight waves): row 8w + lane / 8, tokens 4 (lane % 8) + (0..3).
-  SoftmaxLane st;
-  st.row = 8 * c.w + (c.lane >> 3);
-  st.tg = c.lane & 7;
-  {
-    const int iq = (r0 + st.row) / a.H;  // query token of the row
-    st.lim = min(min(max(L - a.sq + iq + 1, 0), L), c.t_hi);
-    // The wave's first row has the smallest query index, hence the smallest limit.
-    const int iq_w = (r0 + 8 * c.w) / a.H;
-    st.lim_w = min(min(max(L - a.sq + iq_w + 1, 0), L), c.t_hi);
-  }
-  st.m_run = -INFINITY;
-  st.l_run = 0.f;
+  auto init_lane = [&](SoftmaxLane& sl, int row8) {
+    sl.row = row8 + (c.lane >> 3);
+    sl.tg = c.lane & 7;
+    const int iq = (r0 + sl.row) / a.H;  // query token of the row
+    sl.lim = min(min(max(L - a.sq + iq + 1, 0), L), c.t_hi);
+    // The group's first row has the smallest query index, hence the smallest limit.
+    const int iq_w = (r0 + row8) / a.H;
+    sl.lim_w = min(min(max(L - a.sq + iq_w + 1, 0), L), c.t_hi);
+    sl.m_run = -INFINITY;
+    sl.l_run = 0.f;
+  };
+  SoftmaxLane st, st2;
+  init_lane(st, 8 * c.w);
+  (void)st2;
 
   // Row sums and log-sum-exp of this lane's row, once its last tile is done.
   auto finish_rows = [&](const SoftmaxLane& sl) {
@@ -318,44 +331,62 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
         qrb[rb2] = __builtin_bit_cast(bf16x8, ld16(qr + row * kDR + kRopeW * c.w + 8 * c.h));
       }
     }
-    // Half A (phase 1 of tile n into buffer n % 2) and half B (its softmax).
-    auto step = [&](TileRegs<FP8>& tr, int n) {
-      const int t0 = t_lo + n * kTile;
+    // Tile n moves through the pipeline as: registers (loaded two tiles ahead) -> staged in
+    // LDS and scored in step n - 1 -> softmax in step n -> product with V in step n + 1.
+    // Each step ends with the workgroup's only barrier of that step.
+    u32x4 av[8];  // latent score operands of the tile being scored
+    bf16x8 ar;    // RoPE score operand
+    // Stage tile n: write this wave's latent slice to v[n % 2] as bf16 (the output waves'
+    // V) and set the score operands.  bf16: refill the registers with tile n + 2 at once and
+    // read the slice back in operand layout (LDS operations of one wave complete in order,
+    // so no barrier is needed).  fp8: convert the codes, which are already the operands;
+    // the registers are refilled after the score product.
+    auto stage = [&](TileRegs<FP8>& tr, int n) {
+      const int buf = n & 1;
+      uint16_t* vs = &sm.v[buf][c.w][0][0];
+      if constexpr (FP8) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const u32x4 w = tr.lat[j];
+          av[2 * j] = e4m3x8_to_bf16x8(w[0], w[1]);
+          av[2 * j + 1] = e4m3x8_to_bf16x8(w[2], w[3]);
+        }
+        if (c.h == 0) sm.ts[buf][c.w][c.n] = tr.ts;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          *reinterpret_cast<u32x4*>(vs + c.n * kCols + 8 * ((kcol(s, c.h) >> 3) ^ swz32(c.n))) = av[s];
+        ar = __builtin_bit_cast(bf16x8, tr.rope);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int tok = lat_token(k, c.lane);
+          *reinterpret_cast<u32x4*>(vs + tok * kCols + 8 * ((c.lane & 15) ^ swz32(tok))) = tr.lat[k];
+        }
+        ar = __builtin_bit_cast(bf16x8, tr.rope);
+        load_tile<FP8, PK>(tr, c, a, t_lo + (n + 2) * kTile);
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+          av[s] = *reinterpret_cast<const u32x4*>(vs + c.n * kCols + 8 * ((kcol(s, c.h) >> 3) ^ swz32(c.n)));
+      }
+    };
+    // fp8: refill the registers of tile n with tile n + 2 once its score operands are used.
+    auto refill_after_score = [&](TileRegs<FP8>& tr, int n) {
+      if constexpr (FP8) load_tile<FP8, PK>(tr, c, a, t_lo + (n + 2) * kTile);
+    };
+    // Partial scores of the staged tile n into spart[n % 2].
+    auto score = [&](int n) {
       const int buf = n & 1;
       f32x16 sacc[2];
 #pragma unroll
       for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[rb2][e] = 0.f;
-      // Stage the tile's latent slice in LDS (bf16; also the output waves' V), keep the
-      // RoPE operand and token scale, and refill the registers at once.  LDS operations of
-      // one wave complete in order, so the wave reads its own slice back without a barrier.
-      uint16_t* vs = &sm.v[buf][c.w][0][0];
-      if constexpr (FP8) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int tok = lat_token(true, k, c.lane), c16 = c.lane & 7;
-          const u32x4 w = tr.lat[k];
-          *reinterpret_cast<u32x4*>(vs + tok * kCols + 8 * ((2 * c16) ^ swz32(tok))) = e4m3x8_to_bf16x8(w[0], w[1]);
-          *reinterpret_cast<u32x4*>(vs + tok * kCols + 8 * ((2 * c16 + 1) ^ swz32(tok))) = e4m3x8_to_bf16x8(w[2], w[3]);
-        }
-        if (c.h == 0) sm.ts[buf][c.w][c.n] = tr.ts;
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int tok = lat_token(false, k, c.lane);
-          *reinterpret_cast<u32x4*>(vs + tok * kCols + 8 * ((c.lane & 15) ^ swz32(tok))) = tr.lat[k];
-        }
-      }
-      const bf16x8 ar = __builtin_bit_cast(bf16x8, tr.rope);
-      load_tile<FP8, PK>(tr, c, a, t0 + 2 * kTile);  // refill: two tiles ahead
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(vs + c.n * kCols + 8 * ((kcol(s, c.h) >> 3) ^ swz32(c.n)));
+      for (int s = 0; s < 8; ++s)
 #pragma unroll
         for (int rb2 = 0; rb2 < 2; ++rb2)
-          sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[rb2][s], sacc[rb2], 0, 0, 0);
-      }
+          sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[s]), qb[rb2][s],
+                                                              sacc[rb2], 0, 0, 0);
       if constexpr (FP8) {
         // Scale the latent part of tokens 8i + 4h + r by their per-token scales.
 #pragma unroll
@@ -375,28 +406,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
         const int row = 32 * rb2 + c.n;
 #pragma unroll
         for (int i = 0; i < 4; ++i)  // tokens 8i + 4h + (0..3) = chunk 2i + h
-          *reinterpret_cast<f32x4*>(&sm.spart[c.w][row][4 * ((2 * i + c.h) ^ sp_swz(row))]) =
+          *reinterpret_cast<f32x4*>(&sm.spart[buf][c.w][row][4 * ((2 * i + c.h) ^ sp_swz(row))]) =
               f32x4{sacc[rb2][4 * i], sacc[rb2][4 * i + 1], sacc[rb2][4 * i + 2], sacc[rb2][4 * i + 3]};
       }
-      __syncthreads();
-
-      softmax_tile<FP8>(sm, st, buf, t0, a.scale_log2);
+    };
+    // Step n (n + 1 < ntiles): stage and score tile n + 1, softmax of tile n.
+    auto step = [&](TileRegs<FP8>& tr, int n) {
+      stage(tr, n + 1);
+      score(n + 1);
+      refill_after_score(tr, n + 1);
+      softmax_tile<FP8>(sm, st, n & 1, t_lo + n * kTile, a.scale_log2);
       __syncthreads();
     };
 
     if (steps > 0) {
+      // Register set ra holds the even tiles, rb2 the odd ones.
       TileRegs<FP8> ra, rb2;
       load_tile<FP8, PK>(ra, c, a, t_lo);
       load_tile<FP8, PK>(rb2, c, a, t_lo + kTile);
+      stage(ra, 0);
+      score(0);
+      refill_after_score(ra, 0);
+      __syncthreads();
       // Straight-line pairs: every path into the loop header has the same loads in flight.
       int n = 0;
-      for (; n + 1 < ntiles; n += 2) {
-        step(ra, n);
-        step(rb2, n + 1);
+      for (; n + 2 < ntiles; n += 2) {
+        step(rb2, n);
+        step(ra, n + 1);
       }
-      if (n < ntiles) step(ra, n);
-      // The output waves' last step (PV of the last tile).
-      __syncthreads();
+      if (n + 1 < ntiles) {
+        step(rb2, n);
+        ++n;
+      }
+      softmax_tile<FP8>(sm, st, n & 1, t_lo + n * kTile, a.scale_log2);  // the last tile
       __syncthreads();
     }
 
@@ -412,46 +454,55 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
       for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[cb][rb2][e] = 0.f;
-    bf16x8 pb[2][2];  // [row block][token half]
+    bf16x8 vop[4][2];  // V^T operands of one tile: [column block][token half]
 
-    auto pv = [&](const uint16_t* vt, int cb) {
+    // V^T operands of tile n, read from LDS one step before its product.
+    auto read_v = [&](int n) {
+      const uint16_t* vt = &sm.v[n & 1][q][0][0];
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 av = lds_operand_tr32(vt, 16 * ks, 32 * cb, c.lane);
+      for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int rb2 = 0; rb2 < 2; ++rb2)
-          oacc[cb][rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rb2][ks], oacc[cb][rb2], 0, 0, 0);
+        for (int ks = 0; ks < 2; ++ks) vop[cb][ks] = lds_operand_tr32(vt, 16 * ks, 32 * cb, c.lane);
+    };
+    // O^T = O^T * alpha + V^T P^T for tile n.
+    auto pv = [&](int n) {
+      const int buf = n & 1;
+      float al[2];
+#pragma unroll
+      for (int rb2 = 0; rb2 < 2; ++rb2) al[rb2] = sm.alpha[buf][32 * rb2 + c.n];
+      bf16x8 pb[2][2];  // [row block][token half]
+#pragma unroll
+      for (int rb2 = 0; rb2 < 2; ++rb2)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+          pb[rb2][ks] = *reinterpret_cast<const bf16x8*>(&sm.p[buf][32 * rb2 + c.n][16 * ks + 8 * c.h]);
+      if (__any((al[0] != 1.f) | (al[1] != 1.f))) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rb2 = 0; rb2 < 2; ++rb2) oacc[cb][rb2] *= al[rb2];
       }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+          for (int rb2 = 0; rb2 < 2; ++rb2)
+            oacc[cb][rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[cb][ks], pb[rb2][ks], oacc[cb][rb2], 0, 0, 0);
     };
 
-    for (int n = 0; n < steps; ++n) {
-      const int buf = (n - 1) & 1;
-      const uint16_t* vt = &sm.v[buf][q][0][0];
-      if (n > 0) {
-        float al[2];
-#pragma unroll
-        for (int rb2 = 0; rb2 < 2; ++rb2) al[rb2] = sm.alpha[buf][32 * rb2 + c.n];
-        if (__any((al[0] != 1.f) | (al[1] != 1.f))) {
-#pragma unroll
-          for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int rb2 = 0; rb2 < 2; ++rb2) oacc[cb][rb2] *= al[rb2];
-        }
-#pragma unroll
-        for (int rb2 = 0; rb2 < 2; ++rb2)
-#pragma unroll
-          for (int ks = 0; ks < 2; ++ks)
-            pb[rb2][ks] = *reinterpret_cast<const bf16x8*>(&sm.p[buf][32 * rb2 + c.n][16 * ks + 8 * c.h]);
-#pragma unroll
-        for (int cb = 0; cb < kSplitA; ++cb) pv(vt, cb);
-      }
+    if (steps > 0) {
+      __syncthreads();  // tile 0 staged and scored
+      read_v(0);
+      softmax_tile<FP8>(sm, st, 0, t_lo, a.scale_log2);
       __syncthreads();
-      if (n > 0) {
-#pragma unroll
-        for (int cb = kSplitA; cb < 4; ++cb) pv(vt, cb);
+      for (int n = 1; n < ntiles; ++n) {
+        pv(n - 1);
+        read_v(n);
+        softmax_tile<FP8>(sm, st, n & 1, t_lo + n * kTile, a.scale_log2);
+        __syncthreads();
       }
-      if (n < ntiles) softmax_tile<FP8>(sm, st, n & 1, t_lo + n * kTile, a.scale_log2);
-      __syncthreads();
+      pv(ntiles - 1);
     }
     finish_rows(st);
     __syncthreads();  // every row sum published
