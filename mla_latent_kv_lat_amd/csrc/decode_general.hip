@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads) void decode_general_kernel(DecodeArgs a, 
       if (a.lse && tid == 0) a.lse[int64_t(b) * rows + row] = lse2 * kLn2;
     } else {
       const int64_t prow = (int64_t(b) * num_splits + split) * rows + row;
-      float* o = a.part_o + prow * a.dc;
+      float* o = static_cast<float*>(a.part_o) + prow * a.dc;
 #pragma unroll
       for (int j = 0; j < kMaxCols; ++j) {
         const int c = tid + j * kThreads;
@@ -210,7 +210,18 @@ __device__ __forceinline__ void load8_f32(float (&v)[8], const float* p, int c, 
   }
 }
 
-template <typename OS, bool VEC>
+// The same for bf16 partials (only written when dc % 8 == 0).
+__device__ __forceinline__ void load8_f32(float (&v)[8], const uint16_t* p, int c, int dc) {
+  const uint4 x = c < dc ? *reinterpret_cast<const uint4*>(p) : uint4{0u, 0u, 0u, 0u};
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = bf16_bits_to_f32(w[k] & 0xFFFFu);
+    v[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+  }
+}
+
+template <typename OS, typename PS, bool VEC>
 __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int chunk) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rows = a.sq * a.H;
@@ -220,7 +231,8 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int c
   const int nvalid = min(S, (L + chunk - 1) / chunk);
   const float* pl = a.part_lse + int64_t(b) * S * rows + row;
   const int64_t sstride = int64_t(rows) * a.dc;
-  const float* po = a.part_o + (int64_t(b) * S * rows + row) * a.dc;
+  using PR = typename PS::raw;
+  const PR* po = static_cast<const PR*>(a.part_o) + (int64_t(b) * S * rows + row) * a.dc;
   using OR = typename OS::raw;
   OR* o = static_cast<OR*>(a.o_lat) + (int64_t(b) * rows + row) * a.dc;
 
@@ -235,7 +247,10 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int c
         const int sj = min(s0 + j, nvalid - 1);  // in range; surplus entries get weight 0
         const float lj = pl[int64_t(sj) * rows];
         ls[j] = s0 + j < nvalid ? lj : -INFINITY;
-        load8_f32<VEC>(v[j], po + sj * sstride + c, c, a.dc);
+        if constexpr (sizeof(PR) == 2)
+          load8_f32(v[j], po + sj * sstride + c, c, a.dc);
+        else
+          load8_f32<VEC>(v[j], po + sj * sstride + c, c, a.dc);
       }
       float bm = ls[0];
 #pragma unroll
@@ -300,12 +315,16 @@ int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t 
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const dim3 grid((p.rows + kCombRows - 1) / kCombRows, a.B);
   const bool vec = a.dc % 8 == 0;
-  if (a.q_dt == MLA_F32) {
-    if (vec) hipLaunchKernelGGL((combine_kernel<F32, true>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
-    else hipLaunchKernelGGL((combine_kernel<F32, false>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+  if (a.part_bf16) {
+    // Written only by the matrix-core kernel: bf16 output, dc a multiple of 8.
+    if (a.q_dt != MLA_BF16 || !vec) return int(hipErrorInvalidValue);
+    hipLaunchKernelGGL((combine_kernel<BF16, BF16, true>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+  } else if (a.q_dt == MLA_F32) {
+    if (vec) hipLaunchKernelGGL((combine_kernel<F32, F32, true>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+    else hipLaunchKernelGGL((combine_kernel<F32, F32, false>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
   } else {
-    if (vec) hipLaunchKernelGGL((combine_kernel<BF16, true>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
-    else hipLaunchKernelGGL((combine_kernel<BF16, false>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+    if (vec) hipLaunchKernelGGL((combine_kernel<BF16, F32, true>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
+    else hipLaunchKernelGGL((combine_kernel<BF16, F32, false>), grid, dim3(256), 0, s, a, p.num_splits, p.split_tokens);
   }
   return int(hipGetLastError());
 }

@@ -523,8 +523,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
             uint16_t* o = static_cast<uint16_t*>(a.o_lat) + (int64_t(b) * rows + row) * kDC + col;
             *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           } else {
-            float* o = a.part_o + ((int64_t(b) * num_splits + split) * rows + row) * kDC + col;
-            *reinterpret_cast<f32x4*>(o) = v;
+            uint16_t* o = static_cast<uint16_t*>(a.part_o) + ((int64_t(b) * num_splits + split) * rows + row) * kDC + col;
+            *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           }
         }
     }

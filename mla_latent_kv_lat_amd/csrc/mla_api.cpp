@@ -91,14 +91,16 @@ void fill_common(DecodeArgs* a, const mla_dims* d, const void* q_lat, const void
   a->block_table = nullptr;
   a->max_blocks = 0;
   a->part_o = nullptr;
+  a->part_bf16 = false;
   a->part_lse = nullptr;
 }
 
 mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t ws_bytes) {
   if (p.workspace == 0) return MLA_OK;
   if (!ws || ws_bytes < p.workspace || !aligned(ws, 256)) return MLA_ERR_WORKSPACE;
-  const size_t o_bytes = align_up(size_t(a->B) * p.num_splits * p.rows * a->dc * 4, 256);
-  a->part_o = static_cast<float*>(ws);
+  const size_t o_bytes = align_up(size_t(a->B) * p.num_splits * p.rows * a->dc * (p.part_bf16 ? 2 : 4), 256);
+  a->part_o = ws;
+  a->part_bf16 = p.part_bf16;
   a->part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
   return MLA_OK;
 }
@@ -166,8 +168,11 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
   if (splits > 8192 || chunk > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   p.num_splits = int32_t(splits);
   p.split_tokens = int32_t(chunk);
+  // The matrix-core path stores its normalised partial outputs as bf16: they are combined
+  // into a bf16 output, and halving them halves the extra traffic of splitting.
+  p.part_bf16 = p.kernel == DecodeKernel::kMfma;
   if (p.num_splits > 1) {
-    p.workspace = align_up(size_t(d->batch) * splits * p.rows * d->d_latent * 4, 256) +
+    p.workspace = align_up(size_t(d->batch) * splits * p.rows * d->d_latent * (p.part_bf16 ? 2 : 4), 256) +
                   align_up(size_t(d->batch) * splits * p.rows * 4, 256);
   }
   *plan = p;

@@ -24,6 +24,7 @@ struct DecodePlan {
   int32_t row_block;     // query rows per workgroup
   int32_t num_splits;    // context splits per sequence (grid dimension)
   int32_t split_tokens;  // tokens per split (multiple of the token tile)
+  bool part_bf16;        // partial outputs stored as bf16 (else fp32)
   size_t workspace;      // bytes of partial results (0 when num_splits == 1)
 };
 
@@ -46,7 +47,8 @@ struct DecodeArgs {
   int32_t max_blocks;
   void* o_lat;           // [B, sq, H, dc], dtype q_dt
   float* lse;            // [B, sq, H] or nullptr
-  float* part_o;         // [B, S, rows, dc] normalised partial outputs (S > 1)
+  void* part_o;          // [B, S, rows, dc] normalised partial outputs (S > 1), fp32 or bf16
+  bool part_bf16;        // element type of part_o
   float* part_lse;       // [B, S, rows] base-2 log-sum-exp of each split (S > 1)
 };
 
