@@ -221,36 +221,29 @@ __device__ __forceinline__ void load8_f32(float (&v)[8], const uint16_t* p, int 
   }
 }
 
-template <typename OS, typename PS, bool VEC>
-__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int chunk) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rows = a.sq * a.H;
-  const int row = blockIdx.x * kCombRows + wave, b = blockIdx.y;
-  if (row >= rows) return;
-  const int L = a.seq_lens ? a.seq_lens[b] : int(a.T);
-  const int nvalid = min(S, (L + chunk - 1) / chunk);
-  const float* pl = a.part_lse + int64_t(b) * S * rows + row;
-  const int64_t sstride = int64_t(rows) * a.dc;
+// Weighted merge of np pieces of one row: piece j has base-2 log-sum-exp lse_of(j) (-inf:
+// no weight) and its dc normalised values at part_of(j).  Writes the row of o and, if
+// lse_out is set, its natural-log lse.
+template <typename OS, typename PS, bool VEC, typename LseF, typename PartF>
+__device__ __forceinline__ void merge_row(const DecodeArgs& a, int np, LseF lse_of, PartF part_of,
+                                          typename OS::raw* o, float* lse_out, int lane) {
   using PR = typename PS::raw;
-  const PR* po = static_cast<const PR*>(a.part_o) + (int64_t(b) * S * rows + row) * a.dc;
-  using OR = typename OS::raw;
-  OR* o = static_cast<OR*>(a.o_lat) + (int64_t(b) * rows + row) * a.dc;
-
   for (int c0 = 0; c0 < a.dc; c0 += 512) {
     const int c = c0 + 8 * lane;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float M = -INFINITY, tot = 0.f;
-    for (int s0 = 0; s0 < nvalid; s0 += kCombBatch) {
+    for (int s0 = 0; s0 < np; s0 += kCombBatch) {
       float ls[kCombBatch], v[kCombBatch][8];
 #pragma unroll
       for (int j = 0; j < kCombBatch; ++j) {
-        const int sj = min(s0 + j, nvalid - 1);  // in range; surplus entries get weight 0
-        const float lj = pl[int64_t(sj) * rows];
-        ls[j] = s0 + j < nvalid ? lj : -INFINITY;
+        const int sj = min(s0 + j, np - 1);  // in range; surplus entries get weight 0
+        const float lj = lse_of(sj);
+        ls[j] = s0 + j < np ? lj : -INFINITY;
+        const PR* pj = part_of(sj) + c;
         if constexpr (sizeof(PR) == 2)
-          load8_f32(v[j], po + sj * sstride + c, c, a.dc);
+          load8_f32(v[j], pj, c, a.dc);
         else
-          load8_f32<VEC>(v[j], po + sj * sstride + c, c, a.dc);
+          load8_f32<VEC>(v[j], pj, c, a.dc);
       }
       float bm = ls[0];
 #pragma unroll
@@ -271,7 +264,7 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int c
       M = Mn;
     }
     const float inv = tot > 0.f ? 1.f / tot : 0.f;
-    if constexpr (VEC && sizeof(OR) == 2) {
+    if constexpr (VEC && sizeof(typename OS::raw) == 2) {
       if (c < a.dc) {
         uint32_t pk[4];
 #pragma unroll
@@ -285,9 +278,96 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int c
       for (int k = 0; k < 8; ++k)
         if (c + k < a.dc) store_from_f32<OS>(o, c + k, acc[k] * inv);
     }
-    if (c0 == 0 && lane == 0 && a.lse)
-      a.lse[int64_t(b) * rows + row] = tot > 0.f ? (M + log2f(tot)) * kLn2 : -INFINITY;
+    if (c0 == 0 && lane == 0 && lse_out) *lse_out = tot > 0.f ? (M + log2f(tot)) * kLn2 : -INFINITY;
   }
+}
+
+// Static splits: split s of sequence b covers tokens [s chunk, (s + 1) chunk); splits that
+// start at or past the sequence length were not run.
+template <typename OS, typename PS, bool VEC>
+__global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int chunk) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rows = a.sq * a.H;
+  const int row = blockIdx.x * kCombRows + wave, b = blockIdx.y;
+  if (row >= rows) return;
+  const int L = min(max(a.seq_lens ? a.seq_lens[b] : int(a.T), 0), int(a.T));
+  const int nvalid = min(S, (L + chunk - 1) / chunk);
+  const float* pl = a.part_lse + int64_t(b) * S * rows + row;
+  const int64_t sstride = int64_t(rows) * a.dc;
+  using PR = typename PS::raw;
+  const PR* po = static_cast<const PR*>(a.part_o) + (int64_t(b) * S * rows + row) * a.dc;
+  using OR = typename OS::raw;
+  OR* o = static_cast<OR*>(a.o_lat) + (int64_t(b) * rows + row) * a.dc;
+  merge_row<OS, PS, VEC>(
+      a, nvalid, [&](int j) { return pl[int64_t(j) * rows]; }, [&](int j) { return po + j * sstride; }, o,
+      a.lse ? a.lse + int64_t(b) * rows + row : nullptr, lane);
+}
+
+// Balanced ranges (bf16 output and partials): range w holds tiles
+// [floor(total w / R), floor(total (w + 1) / R)) of the batch's concatenated tiles.  A
+// sequence inside one range was written by the decode kernel; a sequence cut by range
+// boundaries is merged from the partial of its first range (slot 1 when that range began
+// in an earlier sequence, else slot 0) and slot 0 of each later range it reaches.  A
+// sequence without tiles gets zeros and lse = -inf.
+__global__ __launch_bounds__(256) void combine_ranges_kernel(DecodeArgs a, int R) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rows = a.sq * a.H;
+  const int row = blockIdx.x * kCombRows + wave, b = blockIdx.y;
+  if (row >= rows) return;
+  const int64_t total = a.prefix[a.B], p0 = a.prefix[b], p1 = a.prefix[b + 1];
+  uint16_t* o = static_cast<uint16_t*>(a.o_lat) + (int64_t(b) * rows + row) * a.dc;
+  float* lse_out = a.lse ? a.lse + int64_t(b) * rows + row : nullptr;
+  if (p1 == p0) {
+    for (int c = 8 * lane; c < a.dc; c += 512) *reinterpret_cast<uint4*>(o + c) = uint4{0u, 0u, 0u, 0u};
+    if (lane == 0 && lse_out) *lse_out = -INFINITY;
+    return;
+  }
+  auto range_lo = [&](int64_t w) { return total * w / R; };
+  auto range_of = [&](int64_t x) { return int(((x + 1) * R + total - 1) / total - 1); };  // holds tile x
+  const int w0 = range_of(p0), w1 = range_of(p1 - 1);
+  if (w0 == w1) return;
+  const int64_t slot0 = int64_t(w0) * 2 + (range_lo(w0) == p0 ? 0 : 1);
+  // Piece j > 0 is slot 0 of range w0 + j; ranges without tiles (only when the batch has
+  // fewer tiles than ranges) get weight 0 and read piece 0's values.
+  const bool dense = total >= R;  // then every range holds a tile
+  auto has_piece = [&](int j) { return j == 0 || dense || range_lo(w0 + j) < range_lo(w0 + j + 1); };
+  auto slot_of = [&](int j) { return j == 0 || !has_piece(j) ? slot0 : int64_t(w0 + j) * 2; };
+  const uint16_t* po = static_cast<const uint16_t*>(a.part_o) + int64_t(row) * a.dc;
+  merge_row<BF16, BF16, true>(
+      a, w1 - w0 + 1,
+      [&](int j) { return has_piece(j) ? a.part_lse[slot_of(j) * rows + row] : -INFINITY; },
+      [&](int j) { return po + slot_of(j) * rows * a.dc; }, o, lse_out, lane);
+}
+
+// Exclusive prefix sum over the batch of each sequence's 32-token tile count (lengths
+// clamped to [0, T]); prefix[B] is the total.  One workgroup of 1024 threads, each summing
+// a contiguous run of sequences, then a scan over the threads in LDS.
+__global__ __launch_bounds__(1024) void tile_prefix_kernel(const int32_t* seq_lens, int B, int64_t T,
+                                                           int64_t* prefix) {
+  __shared__ int64_t part[1024];
+  const int tid = threadIdx.x;
+  auto tiles = [&](int b) {
+    const int64_t L = min(max(int64_t(seq_lens ? seq_lens[b] : T), int64_t(0)), T);
+    return (L + 31) / 32;
+  };
+  const int per = (B + 1023) / 1024;
+  const int lo = min(B, tid * per), hi = min(B, lo + per);
+  int64_t sum = 0;
+  for (int b = lo; b < hi; ++b) sum += tiles(b);
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int64_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int64_t run = tid > 0 ? part[tid - 1] : 0;
+  for (int b = lo; b < hi; ++b) {
+    prefix[b] = run;
+    run += tiles(b);
+  }
+  if (tid == 1023) prefix[B] = part[1023];
 }
 
 template <typename QS, typename KVS, bool PAGED>
@@ -312,9 +392,20 @@ int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t 
   return launch_general_p<BF16, BF16>(a, p, s);
 }
 
+int launch_tile_prefix(const DecodeArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(tile_prefix_kernel, dim3(1), dim3(1024), 0, s, a.seq_lens, a.B, a.T,
+                     const_cast<int64_t*>(a.prefix));
+  return int(hipGetLastError());
+}
+
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const dim3 grid((p.rows + kCombRows - 1) / kCombRows, a.B);
   const bool vec = a.dc % 8 == 0;
+  if (p.balanced) {
+    if (!a.part_bf16 || a.q_dt != MLA_BF16 || !vec) return int(hipErrorInvalidValue);
+    hipLaunchKernelGGL(combine_ranges_kernel, grid, dim3(256), 0, s, a, p.num_splits);
+    return int(hipGetLastError());
+  }
   if (a.part_bf16) {
     // Written only by the matrix-core kernel: bf16 output, dc a multiple of 8.
     if (a.q_dt != MLA_BF16 || !vec) return int(hipErrorInvalidValue);

@@ -54,6 +54,7 @@ constexpr int kThreads = 512;           // 4 score waves + 4 output waves
 constexpr int kCols = 128;              // latent columns per score wave / output wave
 constexpr int kRopeW = 16;              // RoPE dims per score wave
 constexpr int kPPitch = kTile + 8;      // bf16 per row of the probability tile
+constexpr int kMaxPrefixBatch = 2 * kThreads;  // largest batch whose tile prefix each workgroup computes
 // A row's reference max (the value its probabilities are taken relative to) only moves
 // when a tile's max exceeds it by more than this many base-2 units, so probabilities stay
 // below 2^kTau and the output waves almost never have to rescale their accumulators.
@@ -67,7 +68,10 @@ struct alignas(16) Smem {
   float ts[2][4][kTile];                // fp8 per-token scales, one copy per score wave
   float alpha[2][kRows];                // per-row rescale factor of each buffered tile
   float lsum[kRows];
+  int64_t prefix[kMaxPrefixBatch + 1];  // balanced ranges: the batch's tile prefix (small batches)
+  int64_t wave_tot[kThreads / 64];
 };
+static_assert(kMaxInKernelPrefixBatch <= kMaxPrefixBatch, "in-kernel tile prefix does not fit");
 
 // Partial-score rows hold 8 chunks of 4 tokens; chunk c of row r is stored at c ^ sp_swz(r),
 // which keeps both the score waves' writes (16 rows, one chunk) and the softmax reads
@@ -249,26 +253,25 @@ __device__ __forceinline__ void load_tile(TileRegs<FP8>& r, const Ctx& c, const 
   }
 }
 
+// One piece of work: query rows [64 rb, 64 rb + 64) of sequence b (length L) over its
+// tokens [t_lo, t_hi).  A final piece covers the whole sequence and writes o_lat and lse;
+// any other piece writes its normalised partial output and base-2 log-sum-exp.  Row r of
+// the row block goes to row out_base + 64 rb + r of the target arrays.  Every wave of
+// the workgroup calls it with the same arguments (it contains barriers).
 template <bool FP8, int PK>
-__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, int num_splits,
-                                                                  int chunk, int rblocks, int n_units) {
-  __shared__ Smem sm;
-
-  // Workgroups are handed to the 8 XCDs round-robin by id; give each XCD a contiguous
-  // range of work units so that the row blocks (and splits) of one sequence share an L2.
-  const int per_xcd = gridDim.x / 8;
-  const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
-  if (unit >= n_units) return;
-  const int rb = unit % rblocks;
-  const int split = (unit / rblocks) % num_splits;
-  const int b = unit / (rblocks * num_splits);
-
+__device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int b, int rb, int t_lo,
+                                             int t_hi, int L, bool final_out, int64_t out_base) {
+  // The thread index goes through an opaque copy so that nothing derived from it is
+  // hoisted out of the caller's loop over pieces (that would keep it in registers across
+  // the whole piece).
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(int(threadIdx.x)));
   Ctx c;
   c.b = b;
-  c.lane = threadIdx.x & 63;
+  c.lane = tid & 63;
   c.n = c.lane & 31;
   c.h = c.lane >> 5;
-  c.w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.w = __builtin_amdgcn_readfirstlane(tid >> 6);
   c.table = a.block_table;
   c.max_blocks = a.max_blocks;
   c.bs = a.block_size;
@@ -276,13 +279,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
 
   const int rows = a.sq * a.H;
   const int r0 = rb * kRows;
-  const int L = a.seq_lens ? a.seq_lens[b] : int(a.T);
-  const int t_lo = split * chunk;
-  c.t_hi = min(L, t_lo + chunk);
-  if (num_splits > 1 && t_lo >= L) return;  // the combine reads only splits below L
-  const int ntiles = (c.t_hi - t_lo + kTile - 1) / kTile;
+  c.t_hi = t_hi;
+  const int ntiles = t_hi > t_lo ? (t_hi - t_lo + kTile - 1) / kTile : 0;
   const int steps = ntiles > 0 ? ntiles + 1 : 0;
-  const bool single = num_splits == 1;
+  const bool single = final_out;
 
   // Softmax ownership (all eight waves): row 8w + lane / 8, tokens 4 (lane % 8) + (0..3).
   auto init_lane = [&](SoftmaxLane& sl, int row8) {
@@ -307,9 +307,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
       sm.lsum[sl.row] = l_tot;
       const float lse2 = l_tot > 0.f ? sl.m_run + log2f(l_tot) : -INFINITY;
       if (single) {
-        if (a.lse) a.lse[int64_t(b) * rows + r0 + sl.row] = lse2 * kLn2;
+        if (a.lse) a.lse[out_base + r0 + sl.row] = lse2 * kLn2;
       } else {
-        a.part_lse[(int64_t(b) * num_splits + split) * rows + r0 + sl.row] = lse2;
+        a.part_lse[out_base + r0 + sl.row] = lse2;
       }
     }
   };
@@ -520,10 +520,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
           const f32x4 v = f32x4{oacc[cb][rb2][4 * i], oacc[cb][rb2][4 * i + 1], oacc[cb][rb2][4 * i + 2],
                                 oacc[cb][rb2][4 * i + 3]} * inv;
           if (single) {
-            uint16_t* o = static_cast<uint16_t*>(a.o_lat) + (int64_t(b) * rows + row) * kDC + col;
+            uint16_t* o = static_cast<uint16_t*>(a.o_lat) + (out_base + row) * kDC + col;
             *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           } else {
-            uint16_t* o = static_cast<uint16_t*>(a.part_o) + ((int64_t(b) * num_splits + split) * rows + row) * kDC + col;
+            uint16_t* o = static_cast<uint16_t*>(a.part_o) + (out_base + row) * kDC + col;
             *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           }
         }
@@ -531,10 +531,97 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
   }
 }
 
+// Grid: one workgroup per (row block, work unit), handed out XCD-aware.  Static splits:
+// the unit is (sequence, split) and the piece is the split's token chunk.  Balanced ranges:
+// the unit is a range of the batch's concatenated tiles, walked sequence by sequence; a
+// sequence that lies wholly inside the range is a final piece, the range's cut first and
+// last sequences write partials to the range's slots 0 and 1 (slot 0 when one sequence
+// covers the whole range).
+template <bool FP8, int PK>
+__global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, int num_splits,
+                                                                  int chunk, int rblocks, int n_units) {
+  __shared__ Smem sm;
+
+  // Workgroups are handed to the 8 XCDs round-robin by id; give each XCD a contiguous
+  // range of work units so that the row blocks of one piece share an L2.
+  const int per_xcd = gridDim.x / 8;
+  const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if (unit >= n_units) return;
+  const int rb = unit % rblocks;
+  const int rows = a.sq * a.H;
+  auto seq_len = [&](int b) { return min(max(a.seq_lens ? a.seq_lens[b] : int(a.T), 0), int(a.T)); };
+
+  if (a.prefix == nullptr) {
+    const int split = (unit / rblocks) % num_splits;
+    const int b = unit / (rblocks * num_splits);
+    const int L = seq_len(b);
+    const int t_lo = split * chunk;
+    if (num_splits > 1 && t_lo >= L) return;  // the combine reads only splits below L
+    const bool fin = num_splits == 1;
+    decode_piece<FP8, PK>(sm, a, b, rb, t_lo, min(L, t_lo + chunk), L, fin,
+                          fin ? int64_t(b) * rows : (int64_t(b) * num_splits + split) * rows);
+    return;
+  }
+
+  // Tile prefix of the batch: computed here for small batches (every workgroup, in LDS;
+  // unit 0 also stores it for the combine), else read from the prefix kernel's output.
+  if (a.prefix_here) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    auto tiles = [&](int i) { return i < a.B ? int64_t((seq_len(i) + kTile - 1) / kTile) : int64_t(0); };
+    const int64_t t0 = tiles(2 * tid), t1 = tiles(2 * tid + 1);
+    int64_t incl = t0 + t1;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int64_t v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) sm.wave_tot[wave] = incl;
+    __syncthreads();
+    for (int k = 0; k < wave; ++k) incl += sm.wave_tot[k];
+    const int64_t excl = incl - t0 - t1;
+    if (2 * tid < a.B) sm.prefix[2 * tid] = excl;
+    if (2 * tid + 1 < a.B) sm.prefix[2 * tid + 1] = excl + t0;
+    if (tid == kThreads - 1) sm.prefix[a.B] = incl;  // 2 kThreads >= B: the total
+    __syncthreads();
+    if (unit == 0)
+      for (int i = tid; i <= a.B; i += kThreads) const_cast<int64_t*>(a.prefix)[i] = sm.prefix[i];
+  }
+  // Prefix entries are the same for every lane: keep them in scalar registers.
+  auto pre = [&](int i) {
+    const int64_t v = a.prefix_here ? sm.prefix[i] : a.prefix[i];
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
+    return int64_t((uint64_t(hi) << 32) | lo);
+  };
+
+  const int w = unit / rblocks, n_ranges = n_units / rblocks;
+  const int64_t total = pre(a.B);
+  int64_t cur = total * w / n_ranges;
+  const int64_t end = total * (w + 1) / n_ranges;
+  if (cur >= end) return;
+  // First sequence with tiles past the range start.
+  int b = 0;
+  for (int hi = a.B - 1; b < hi;) {
+    const int mid = (b + hi) / 2;
+    if (pre(mid + 1) > cur) hi = mid;
+    else b = mid + 1;
+  }
+  for (bool first = true; cur < end; first = false) {
+    const int64_t p0 = pre(b), p1 = pre(b + 1);
+    const int64_t e = min(end, p1);
+    const int L = seq_len(b);
+    const bool fin = cur == p0 && e == p1;
+    const int64_t base = fin ? int64_t(b) * rows : (int64_t(w) * 2 + (first ? 0 : 1)) * rows;
+    decode_piece<FP8, PK>(sm, a, b, rb, int(cur - p0) * kTile, min(L, int(e - p0) * kTile), L, fin, base);
+    cur = e;
+    for (++b; b < a.B && pre(b + 1) <= cur;) ++b;  // skip sequences without tiles
+  }
+}
+
 template <bool FP8, int PK>
 int launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const int rblocks = p.rows / kRows;
-  const int n_units = a.B * p.num_splits * rblocks;
+  const int n_units = p.balanced ? p.num_splits * rblocks : a.B * p.num_splits * rblocks;
   const int grid = (n_units + 7) / 8 * 8;
   hipLaunchKernelGGL((decode_mfma_kernel<FP8, PK>), dim3(grid), dim3(kThreads), 0, s, a,
                      p.num_splits, p.split_tokens, rblocks, n_units);

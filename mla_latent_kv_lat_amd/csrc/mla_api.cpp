@@ -3,6 +3,7 @@
 // Validation and planning are pure host logic and run before any HIP call, so every
 // error path can be exercised on a machine without a GPU.  Launch failures surface as
 // MLA_ERR_HIP with the hipError_t kept per thread.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 
@@ -93,23 +94,38 @@ void fill_common(DecodeArgs* a, const mla_dims* d, const void* q_lat, const void
   a->part_o = nullptr;
   a->part_bf16 = false;
   a->part_lse = nullptr;
+  a->prefix = nullptr;
+  a->prefix_here = false;
 }
 
 mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t ws_bytes) {
   if (p.workspace == 0) return MLA_OK;
   if (!ws || ws_bytes < p.workspace || !aligned(ws, 256)) return MLA_ERR_WORKSPACE;
-  const size_t o_bytes = align_up(size_t(a->B) * p.num_splits * p.rows * a->dc * (p.part_bf16 ? 2 : 4), 256);
-  a->part_o = ws;
+  char* w = static_cast<char*>(ws);
+  size_t o_bytes;
+  if (p.balanced) {
+    a->prefix = reinterpret_cast<const int64_t*>(w);
+    a->prefix_here = a->B <= kMaxInKernelPrefixBatch;
+    w += align_up(size_t(a->B + 1) * 8, 256);
+    o_bytes = align_up(size_t(p.num_splits) * 2 * p.rows * a->dc * 2, 256);
+  } else {
+    o_bytes = align_up(size_t(a->B) * p.num_splits * p.rows * a->dc * (p.part_bf16 ? 2 : 4), 256);
+  }
+  a->part_o = w;
   a->part_bf16 = p.part_bf16;
-  a->part_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+  a->part_lse = reinterpret_cast<float*>(w + o_bytes);
   return MLA_OK;
 }
 
 mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+  if (p.balanced && !a.prefix_here) {
+    const int err = launch_tile_prefix(a, s);
+    if (err) return hip_status(err);
+  }
   int err = p.kernel == DecodeKernel::kMfma ? launch_decode_mfma(a, p, s)
                                             : launch_decode_general(a, p, s);
   if (err) return hip_status(err);
-  if (p.num_splits > 1) return hip_status(launch_combine(a, p, s));
+  if (p.balanced || p.num_splits > 1) return hip_status(launch_combine(a, p, s));
   return MLA_OK;
 }
 
@@ -154,6 +170,26 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
     min_chunk = 256;
   }
   const int64_t units = int64_t(d->batch) * ceil_div(p.rows, p.row_block);
+  // The matrix-core path stores its normalised partial outputs as bf16: they are combined
+  // into a bf16 output, and halving them halves the extra traffic of splitting.
+  p.part_bf16 = p.kernel == DecodeKernel::kMfma;
+  if (d->split_tokens == 0 && p.kernel == DecodeKernel::kMfma) {
+    // Balanced ranges: the 32-token tiles of the whole batch (per row block) are divided
+    // into num_splits contiguous ranges of equal size on the device, from the actual
+    // sequence lengths, so that ragged batches keep every compute unit busy.  Each range
+    // runs on one workgroup per row block; a sequence cut by range boundaries is merged
+    // afterwards.
+    const int64_t rblocks = ceil_div(p.rows, p.row_block);
+    const int64_t ranges = std::max<int64_t>(1, kNumCUs / rblocks);
+    p.balanced = true;
+    p.num_splits = int32_t(ranges);
+    p.split_tokens = 0;
+    p.workspace = align_up(size_t(d->batch + 1) * 8, 256) +
+                  align_up(size_t(ranges) * 2 * p.rows * d->d_latent * 2, 256) +
+                  align_up(size_t(ranges) * 2 * p.rows * 4, 256);
+    *plan = p;
+    return MLA_OK;
+  }
   int64_t chunk;
   if (d->split_tokens > 0) {
     chunk = ceil_div(d->split_tokens, tile) * tile;
@@ -168,9 +204,6 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
   if (splits > 8192 || chunk > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   p.num_splits = int32_t(splits);
   p.split_tokens = int32_t(chunk);
-  // The matrix-core path stores its normalised partial outputs as bf16: they are combined
-  // into a bf16 output, and halving them halves the extra traffic of splitting.
-  p.part_bf16 = p.kernel == DecodeKernel::kMfma;
   if (p.num_splits > 1) {
     p.workspace = align_up(size_t(d->batch) * splits * p.rows * d->d_latent * (p.part_bf16 ? 2 : 4), 256) +
                   align_up(size_t(d->batch) * splits * p.rows * 4, 256);

@@ -23,7 +23,8 @@ struct DecodePlan {
   int32_t rows;          // s_q * n_h query rows per sequence
   int32_t row_block;     // query rows per workgroup
   int32_t num_splits;    // context splits per sequence (grid dimension)
-  int32_t split_tokens;  // tokens per split (multiple of the token tile)
+  int32_t split_tokens;  // tokens per split (multiple of the token tile); 0 when balanced
+  bool balanced;         // num_splits ranges of equal work over the whole batch (see below)
   bool part_bf16;        // partial outputs stored as bf16 (else fp32)
   size_t workspace;      // bytes of partial results (0 when num_splits == 1)
 };
@@ -47,8 +48,13 @@ struct DecodeArgs {
   int32_t max_blocks;
   void* o_lat;           // [B, sq, H, dc], dtype q_dt
   float* lse;            // [B, sq, H] or nullptr
-  void* part_o;          // [B, S, rows, dc] normalised partial outputs (S > 1), fp32 or bf16
+  // Static splits: part_o [B, S, rows, dc], part_lse [B, S, rows].  Balanced ranges:
+  // part_o [R, 2, rows, dc], part_lse [R, 2, rows] (a range's first and last piece).
+  void* part_o;          // normalised partial outputs, fp32 or bf16
   bool part_bf16;        // element type of part_o
+  const int64_t* prefix; // balanced ranges: [B + 1] exclusive prefix sum of 32-token tiles per
+                         // sequence (lengths clamped to [0, T]); nullptr for static splits
+  bool prefix_here;      // the decode kernel computes and stores prefix itself (small batches)
   float* part_lse;       // [B, S, rows] base-2 log-sum-exp of each split (S > 1)
 };
 
@@ -81,6 +87,8 @@ bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, in
 int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+int launch_tile_prefix(const DecodeArgs& a, hipStream_t s);
+constexpr int kMaxInKernelPrefixBatch = 1024;  // batches up to this size skip the prefix kernel
 int launch_absorb(const void* x, const void* w, void* y, mla_dtype dt, int32_t M, int32_t H,
                   int32_t K, int32_t N, hipStream_t s);
 bool absorb_mfma_supported(mla_dtype dt, int32_t M, int32_t K, int32_t N);

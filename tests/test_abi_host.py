@@ -180,19 +180,24 @@ def test_utility_argument_errors():
 def test_plan_covers_the_context(cfg):
     d = L.dims_from_config(cfg)
     n, tok = L.mla_decode_plan(d, cfg.kv_dtype, cfg.seq_len)
-    assert n >= 1 and tok >= 1
-    assert (n - 1) * tok < cfg.seq_len <= n * tok
     ws = L.mla_decode_workspace_bytes(d, cfg.kv_dtype, cfg.seq_len)
     rows = cfg.q_len * cfg.n_heads
+    r = lambda x: (x + 255) // 256 * 256
+    # The matrix-core path (bf16 queries, d_c 512, d_r 64, rows a multiple of 64) balances
+    # the batch's tiles over n ranges on the device (tok = 0): one range per compute unit
+    # and row block, two bf16 partial slots per range, plus the [B + 1] int64 tile prefix.
+    mfma = cfg.act_dtype == "bf16" and cfg.d_latent == 512 and cfg.d_rope == 64 and rows % 64 == 0
+    if mfma:
+        assert tok == 0 and n == max(1, 256 // (rows // 64))
+        assert ws == r((cfg.batch + 1) * 8) + r(n * 2 * rows * cfg.d_latent * 2) + r(n * 2 * rows * 4)
+        return
+    assert n >= 1 and tok >= 1
+    assert (n - 1) * tok < cfg.seq_len <= n * tok
     if n == 1:
         assert ws == 0
     else:
-        # The matrix-core path (bf16 queries, d_c 512, d_r 64, rows a multiple of 64) keeps
-        # bf16 partial outputs, the general path fp32.
-        mfma = cfg.act_dtype == "bf16" and cfg.d_latent == 512 and cfg.d_rope == 64 and rows % 64 == 0
-        po = cfg.batch * n * rows * cfg.d_latent * (2 if mfma else 4)
+        po = cfg.batch * n * rows * cfg.d_latent * 4
         pl = cfg.batch * n * rows * 4
-        r = lambda x: (x + 255) // 256 * 256
         assert ws == r(po) + r(pl)
 
 

@@ -292,3 +292,33 @@ def test_empty_and_short_sequences():
     o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [0, 1, 256], 64)
     assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
     assert max_rel_err(o, o_ref) <= TOL["bf16"]
+
+
+# Balanced ranges (the default plan of the matrix-core path): the batch's tiles are cut into
+# equal ranges on the device, so sequences are split at data-dependent places, several
+# whole sequences can share a workgroup, ranges can be empty (fewer tiles than ranges), and
+# batches above 1024 sequences take the separate prefix kernel.
+BALANCED_CASES = {
+    "many_short": (dict(batch=200, seq_len=200, n_heads=128), None),
+    "fewer_tiles_than_ranges": (dict(batch=2, seq_len=40, n_heads=128), [1, 40]),
+    "empty_sequences": (dict(batch=5, seq_len=300, n_heads=128), [0, 300, 0, 1, 65]),
+    "prefix_kernel_batch": (dict(batch=1100, seq_len=64, n_heads=64), None),
+}
+
+
+@pytest.mark.parametrize("case", list(BALANCED_CASES))
+def test_decode_balanced_ranges(case):
+    kw, lengths = BALANCED_CASES[case]
+    cfg = configs.V2_DECODE.with_(cfg_id=30, **kw)
+    if lengths is None:
+        lengths = np.random.default_rng(7).integers(1, cfg.seq_len + 1, size=cfg.batch)
+    say("decode balanced", case, cfg.batch, cfg.n_heads, cfg.seq_len)
+    o, l, o_ref, l_ref, inp, d, w = decode_stage_case(cfg, 0, lengths, 0)
+    assert w.plan[1] == 0, w.plan  # balanced ranges
+    empty = np.asarray(lengths) == 0
+    assert np.all(o[empty] == 0) and np.all(np.isneginf(l[empty]))
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(l), np.isneginf(l_ref))
+    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l[fin], l_ref[fin])
+    print(f"  o_lat {e_o:.2e} lse {e_l:.2e}", flush=True)
+    assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
