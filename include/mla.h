@@ -68,8 +68,13 @@ typedef struct {
   int32_t d_rope;        /* d_r >= 0 */
   float softmax_scale;   /* finite, > 0; multiplies the whole [latent | rope] dot product */
   int32_t split_tokens;  /* tokens per split of the context (split-K); 0 = library's choice.
-                            Any value gives the same result up to rounding; a fixed value
-                            gives bitwise-reproducible results. */
+                            On the matrix-core kernel the choice is balanced ranges: the
+                            batch's 32-token tiles (from the device seq_lens) are cut into
+                            equal contiguous ranges, one workgroup each, so ragged batches
+                            keep every compute unit busy; elsewhere it is a fixed split
+                            from max_seq_len.  Any value gives the same result up to
+                            rounding; every plan is bitwise reproducible run to run for
+                            the same lengths. */
 } mla_dims;
 
 /* Supported kernel set (anything else returns MLA_ERR_UNSUPPORTED):
@@ -142,7 +147,9 @@ mla_status mla_decode_paged(const mla_dims* dims, const void* q_lat, const void*
 size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype kv_dt, int32_t max_seq_len);
 
 /* Host-only: the split-K plan mla_decode would use.  Writes the number of context splits
- * and the tokens per split (host pointers, either may be NULL).  No HIP call. */
+ * and the tokens per split (host pointers, either may be NULL); for balanced ranges
+ * (split_tokens == 0 on the matrix-core kernel) it writes the number of ranges per row
+ * block of 64 query rows and 0 tokens.  No HIP call. */
 mla_status mla_decode_plan(const mla_dims* dims, mla_dtype kv_dt, int32_t max_seq_len,
                            int32_t* num_splits, int32_t* split_tokens);
 
