@@ -212,6 +212,8 @@ def main() -> int:
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--fp8-scores", type=int, choices=(0, 1), default=0,
+                    help="1: latent score term as an fp8 matrix product (fp8-cache workloads)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -237,7 +239,8 @@ def main() -> int:
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, 0)
     wc = work_counts(cfg, inp.seq_lens)
-    w = DeviceWorkload(inp, split_tokens=args.split_tokens, replicas=args.replicas)
+    w = DeviceWorkload(inp, split_tokens=args.split_tokens, replicas=args.replicas,
+                       fp8_scores=args.fp8_scores)
     print(f"[bench] plan (splits, tokens/split) = {w.plan}; workspace {w.ws_bytes} B",
           file=sys.stderr, flush=True)
 
@@ -311,6 +314,7 @@ def main() -> int:
                    "n_heads": cfg.n_heads, "d_head": cfg.d_head, "d_latent": cfg.d_latent,
                    "d_rope": cfg.d_rope, "seq_len": cfg.seq_len, "kv_dtype": cfg.kv_dtype,
                    "paged": cfg.paged, "splits": w.plan[0], "split_tokens": w.plan[1],
+                   "fp8_scores": args.fp8_scores,
                    "cache_replicas": len(w.caches)},
         "tflops": round(wc["attn_flops"] / (ms_step * 1e-3) / 1e12, 2),
         "decode_tokens_per_s": round(cfg.batch * cfg.q_len / (ms_step * 1e-3), 1),

@@ -75,6 +75,14 @@ typedef struct {
                             from max_seq_len.  Any value gives the same result up to
                             rounding; every plan is bitwise reproducible run to run for
                             the same lengths. */
+  int32_t fp8_scores;    /* 0 or 1.  1: the latent part of the score is an fp8 matrix
+                            product: each row's 128-column slices of q_lat are rounded to
+                            e4m3 with their own scale (max|x| / 448) and multiplied with the
+                            cache codes as stored; the RoPE term, the softmax and the product
+                            with V are unchanged.  Twice the matrix rate for the score, at
+                            the cost of the query rounding.  Needs an MLA_FP8_E4M3 cache on
+                            the matrix-core kernel (else MLA_ERR_UNSUPPORTED); mla_decode /
+                            mla_decode_paged only. */
 } mla_dims;
 
 /* Supported kernel set (anything else returns MLA_ERR_UNSUPPORTED):

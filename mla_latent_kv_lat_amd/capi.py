@@ -47,16 +47,19 @@ class MlaDims(ctypes.Structure):
         ("batch", ctypes.c_int32), ("q_len", ctypes.c_int32), ("n_heads", ctypes.c_int32),
         ("d_head", ctypes.c_int32), ("d_latent", ctypes.c_int32), ("d_rope", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float), ("split_tokens", ctypes.c_int32),
+        ("fp8_scores", ctypes.c_int32),
     ]
 
 
-def dims(batch, q_len, n_heads, d_head, d_latent, d_rope, softmax_scale, split_tokens=0) -> MlaDims:
-    return MlaDims(batch, q_len, n_heads, d_head, d_latent, d_rope, softmax_scale, split_tokens)
+def dims(batch, q_len, n_heads, d_head, d_latent, d_rope, softmax_scale, split_tokens=0,
+         fp8_scores=0) -> MlaDims:
+    return MlaDims(batch, q_len, n_heads, d_head, d_latent, d_rope, softmax_scale, split_tokens,
+                   fp8_scores)
 
 
-def dims_from_config(cfg, split_tokens: int = 0) -> MlaDims:
+def dims_from_config(cfg, split_tokens: int = 0, fp8_scores: int = 0) -> MlaDims:
     return dims(cfg.batch, cfg.q_len, cfg.n_heads, cfg.d_head, cfg.d_latent, cfg.d_rope,
-                cfg.softmax_scale, split_tokens)
+                cfg.softmax_scale, split_tokens, fp8_scores)
 
 
 _LIB: Optional[ctypes.CDLL] = None

@@ -258,7 +258,7 @@ __device__ __forceinline__ void load_tile(TileRegs<FP8>& r, const Ctx& c, const 
 // any other piece writes its normalised partial output and base-2 log-sum-exp.  Row r of
 // the row block goes to row out_base + 64 rb + r of the target arrays.  Every wave of
 // the workgroup calls it with the same arguments (it contains barriers).
-template <bool FP8, int PK>
+template <bool FP8, int PK, bool QK8>
 __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int b, int rb, int t_lo,
                                              int t_hi, int L, bool final_out, int64_t out_base) {
   // The thread index goes through an opaque copy so that nothing derived from it is
@@ -331,6 +331,35 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
         qrb[rb2] = __builtin_bit_cast(bf16x8, ld16(qr + row * kDR + kRopeW * c.w + 8 * c.h));
       }
     }
+    // fp8 score product: each row's 128-column slice (this wave's) is rounded to e4m3 with
+    // scale max|x| / 448; q8[rb2][m] holds the codes of columns 64m + 32j + 16h + (0..15),
+    // j = 0, 1, in the byte order of the cache operand (tr.lat[2m + j]).
+    v8i q8[2][2];
+    float qs[2];
+    if constexpr (QK8) {
+#pragma unroll
+      for (int rb2 = 0; rb2 < 2; ++rb2) {
+        float amax = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(float(qb[rb2][s][e])));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));  // the row's other 64 columns
+        qs[rb2] = amax > 0.f ? amax * (1.f / 448.f) : 1.f;
+        const float inv = amax > 0.f ? 448.f / amax : 1.f;
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int d = 0; d < 8; ++d) {  // dword d: columns of k-step 4m + d / 2, half d % 2
+            const bf16x8 src = qb[rb2][4 * m + d / 2];
+            const int o = 4 * (d % 2);
+            auto q = [&](int e) { return fminf(fmaxf(float(src[o + e]) * inv, -448.f), 448.f); };
+            int w = __builtin_amdgcn_cvt_pk_fp8_f32(q(0), q(1), 0, false);
+            w = __builtin_amdgcn_cvt_pk_fp8_f32(q(2), q(3), w, true);
+            q8[rb2][m][d] = w;
+          }
+      }
+    }
     // Tile n moves through the pipeline as: registers (loaded two tiles ahead) -> staged in
     // LDS and scored in step n - 1 -> softmax in step n -> product with V in step n + 1.
     // Each step ends with the workgroup's only barrier of that step.
@@ -374,28 +403,42 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
       if constexpr (FP8) load_tile<FP8, PK>(tr, c, a, t_lo + (n + 2) * kTile);
     };
     // Partial scores of the staged tile n into spart[n % 2].
-    auto score = [&](int n) {
+    auto score = [&](const TileRegs<FP8>& tr, int n) {
       const int buf = n & 1;
       f32x16 sacc[2];
 #pragma unroll
       for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[rb2][e] = 0.f;
+      if constexpr (QK8) {
+        // Codes times codes, 64 columns per instruction (unit block scales).
 #pragma unroll
-      for (int s = 0; s < 8; ++s)
+        for (int m = 0; m < 2; ++m) {
+          const v8i av8 = {int(tr.lat[2 * m][0]), int(tr.lat[2 * m][1]), int(tr.lat[2 * m][2]), int(tr.lat[2 * m][3]),
+                           int(tr.lat[2 * m + 1][0]), int(tr.lat[2 * m + 1][1]), int(tr.lat[2 * m + 1][2]),
+                           int(tr.lat[2 * m + 1][3])};
 #pragma unroll
-        for (int rb2 = 0; rb2 < 2; ++rb2)
-          sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[s]), qb[rb2][s],
-                                                              sacc[rb2], 0, 0, 0);
+          for (int rb2 = 0; rb2 < 2; ++rb2)
+            sacc[rb2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av8, q8[rb2][m], sacc[rb2], 0, 0, 0, 127, 0, 127);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+#pragma unroll
+          for (int rb2 = 0; rb2 < 2; ++rb2)
+            sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[s]), qb[rb2][s],
+                                                                sacc[rb2], 0, 0, 0);
+      }
       if constexpr (FP8) {
-        // Scale the latent part of tokens 8i + 4h + r by their per-token scales.
+        // Scale the latent part of tokens 8i + 4h + r by their per-token scales (and, for
+        // the fp8 product, row n's query scale).
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const f32x4 tsv = *reinterpret_cast<const f32x4*>(&sm.ts[buf][c.w][8 * i + 4 * c.h]);
 #pragma unroll
           for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sacc[rb2][4 * i + r] *= tsv[r];
+            for (int r = 0; r < 4; ++r) sacc[rb2][4 * i + r] *= QK8 ? tsv[r] * qs[rb2] : tsv[r];
         }
       }
 #pragma unroll
@@ -413,7 +456,7 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
     // Step n (n + 1 < ntiles): stage and score tile n + 1, softmax of tile n.
     auto step = [&](TileRegs<FP8>& tr, int n) {
       stage(tr, n + 1);
-      score(n + 1);
+      score(tr, n + 1);
       refill_after_score(tr, n + 1);
       softmax_tile<FP8>(sm, st, n & 1, t_lo + n * kTile, a.scale_log2);
       __syncthreads();
@@ -425,7 +468,7 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
       load_tile<FP8, PK>(ra, c, a, t_lo);
       load_tile<FP8, PK>(rb2, c, a, t_lo + kTile);
       stage(ra, 0);
-      score(0);
+      score(ra, 0);
       refill_after_score(ra, 0);
       __syncthreads();
       // Straight-line pairs: every path into the loop header has the same loads in flight.
@@ -537,7 +580,7 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
 // sequence that lies wholly inside the range is a final piece, the range's cut first and
 // last sequences write partials to the range's slots 0 and 1 (slot 0 when one sequence
 // covers the whole range).
-template <bool FP8, int PK>
+template <bool FP8, int PK, bool QK8>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, int num_splits,
                                                                   int chunk, int rblocks, int n_units) {
   __shared__ Smem sm;
@@ -558,7 +601,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
     const int t_lo = split * chunk;
     if (num_splits > 1 && t_lo >= L) return;  // the combine reads only splits below L
     const bool fin = num_splits == 1;
-    decode_piece<FP8, PK>(sm, a, b, rb, t_lo, min(L, t_lo + chunk), L, fin,
+    decode_piece<FP8, PK, QK8>(sm, a, b, rb, t_lo, min(L, t_lo + chunk), L, fin,
                           fin ? int64_t(b) * rows : (int64_t(b) * num_splits + split) * rows);
     return;
   }
@@ -612,18 +655,18 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
     const int L = seq_len(b);
     const bool fin = cur == p0 && e == p1;
     const int64_t base = fin ? int64_t(b) * rows : (int64_t(w) * 2 + (first ? 0 : 1)) * rows;
-    decode_piece<FP8, PK>(sm, a, b, rb, int(cur - p0) * kTile, min(L, int(e - p0) * kTile), L, fin, base);
+    decode_piece<FP8, PK, QK8>(sm, a, b, rb, int(cur - p0) * kTile, min(L, int(e - p0) * kTile), L, fin, base);
     cur = e;
     for (++b; b < a.B && pre(b + 1) <= cur;) ++b;  // skip sequences without tiles
   }
 }
 
-template <bool FP8, int PK>
+template <bool FP8, int PK, bool QK8 = false>
 int launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const int rblocks = p.rows / kRows;
   const int n_units = p.balanced ? p.num_splits * rblocks : a.B * p.num_splits * rblocks;
   const int grid = (n_units + 7) / 8 * 8;
-  hipLaunchKernelGGL((decode_mfma_kernel<FP8, PK>), dim3(grid), dim3(kThreads), 0, s, a,
+  hipLaunchKernelGGL((decode_mfma_kernel<FP8, PK, QK8>), dim3(grid), dim3(kThreads), 0, s, a,
                      p.num_splits, p.split_tokens, rblocks, n_units);
   return int(hipGetLastError());
 }
@@ -632,6 +675,10 @@ int launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
 
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const int pk = !a.paged ? kContig : (a.block_size % kTile == 0 ? kPagedTile : kPagedAny);
+  if (a.kv_dt == MLA_FP8_E4M3 && a.fp8_scores) {
+    if (pk == kContig) return launch_t<true, kContig, true>(a, p, s);
+    return pk == kPagedTile ? launch_t<true, kPagedTile, true>(a, p, s) : launch_t<true, kPagedAny, true>(a, p, s);
+  }
   if (a.kv_dt == MLA_FP8_E4M3) {
     if (pk == kContig) return launch_t<true, kContig>(a, p, s);
     return pk == kPagedTile ? launch_t<true, kPagedTile>(a, p, s) : launch_t<true, kPagedAny>(a, p, s);

@@ -20,6 +20,7 @@
 namespace mla {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef int v8i __attribute__((ext_vector_type(8)));  // 32 fp8 codes: one f8f6f4 MFMA operand
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));

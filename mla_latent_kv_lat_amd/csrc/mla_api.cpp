@@ -96,6 +96,7 @@ void fill_common(DecodeArgs* a, const mla_dims* d, const void* q_lat, const void
   a->part_lse = nullptr;
   a->prefix = nullptr;
   a->prefix_here = false;
+  a->fp8_scores = d->fp8_scores != 0;
 }
 
 mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t ws_bytes) {
@@ -134,7 +135,8 @@ mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
 mla_status check_dims(const mla_dims* d) {
   if (!d) return MLA_ERR_INVALID_ARG;
   if (d->batch < 1 || d->q_len < 1 || d->q_len > kMaxQLen || d->n_heads < 1 || d->d_head < 1 ||
-      d->d_latent < 1 || d->d_rope < 0 || d->split_tokens < 0)
+      d->d_latent < 1 || d->d_rope < 0 || d->split_tokens < 0 || d->fp8_scores < 0 ||
+      d->fp8_scores > 1)
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if (int64_t(d->q_len) * d->n_heads > kMaxRows) return MLA_ERR_UNSUPPORTED;
@@ -169,6 +171,8 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
     tile = 256;
     min_chunk = 256;
   }
+  if (d->fp8_scores && (p.kernel != DecodeKernel::kMfma || kv_dt != MLA_FP8_E4M3))
+    return MLA_ERR_UNSUPPORTED;
   const int64_t units = int64_t(d->batch) * ceil_div(p.rows, p.row_block);
   // The matrix-core path stores its normalised partial outputs as bf16: they are combined
   // into a bf16 output, and halving them halves the extra traffic of splitting.

@@ -55,6 +55,7 @@ struct DecodeArgs {
   const int64_t* prefix; // balanced ranges: [B + 1] exclusive prefix sum of 32-token tiles per
                          // sequence (lengths clamped to [0, T]); nullptr for static splits
   bool prefix_here;      // the decode kernel computes and stores prefix itself (small batches)
+  bool fp8_scores;       // latent score term as an fp8 product (fp8 cache, matrix-core kernel)
   float* part_lse;       // [B, S, rows] base-2 log-sum-exp of each split (S > 1)
 };
 

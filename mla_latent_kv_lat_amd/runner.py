@@ -39,11 +39,12 @@ def to_host_f64(t: torch.Tensor) -> np.ndarray:
 class DeviceWorkload:
     """One workload resident in device memory, with its outputs and workspace."""
 
-    def __init__(self, inp: Inputs, device="cuda", split_tokens: int = 0, replicas: int = 1):
+    def __init__(self, inp: Inputs, device="cuda", split_tokens: int = 0, replicas: int = 1,
+                 fp8_scores: int = 0):
         cfg = inp.cfg
         self.cfg, self.inp, self.device = cfg, inp, device
         act, kvk = cfg.act_dtype, cfg.kv_dtype
-        self.dims = libmla.dims_from_config(cfg, split_tokens)
+        self.dims = libmla.dims_from_config(cfg, split_tokens, fp8_scores)
         self.q_nope = to_device(inp.q_nope, act, device)
         self.q_rope = to_device(inp.q_rope, act, device)
         self.seq_lens = to_device(inp.seq_lens, "i32", device)

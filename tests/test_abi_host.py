@@ -273,3 +273,18 @@ def test_rope_query_argument_errors(kw, status):
     st = L.library().mla_rope_query(ctypes.byref(d), args["q"], args["dt"], args["seq_lens"], args["base"],
                                     args["pairing"], None)
     assert st == status
+
+
+def test_fp8_scores_argument():
+    """fp8_scores must be 0 or 1, and needs the fp8 cache on the matrix-core kernel."""
+    cfg = configs.SPEC_FP8
+    assert L.mla_decode_plan(L.dims_from_config(cfg, fp8_scores=2), "fp8", cfg.seq_len,
+                             check=False)[0] == L.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_plan(L.dims_from_config(cfg, fp8_scores=1), "fp8", cfg.seq_len) == \
+        L.mla_decode_plan(L.dims_from_config(cfg), "fp8", cfg.seq_len)
+    v2 = configs.V2_DECODE
+    assert L.mla_decode_plan(L.dims_from_config(v2, fp8_scores=1), "bf16", v2.seq_len,
+                             check=False)[0] == L.MLA_ERR_UNSUPPORTED
+    small = cfg.with_(n_heads=8)  # general kernel
+    assert L.mla_decode_plan(L.dims_from_config(small, fp8_scores=1), "fp8", small.seq_len,
+                             check=False)[0] == L.MLA_ERR_UNSUPPORTED

@@ -141,7 +141,7 @@ def test_absorb_q_and_out_v2_shapes():
     assert e_q <= TOL["bf16"] and e_o <= TOL["bf16"]
 
 
-def decode_stage_case(cfg, seed, lengths, split_tokens, poison=True, q_gain=1.0):
+def decode_stage_case(cfg, seed, lengths, split_tokens, poison=True, q_gain=1.0, fp8_scores=0):
     """mla_decode alone: both sides read the same stored q_lat (the oracle's q_lat rounded
     to the stored dtype), so only the attention stage is compared."""
     inp = synth.make_inputs(cfg, seed, lengths=np.array(lengths, np.int32), poison_tail=poison,
@@ -150,7 +150,7 @@ def decode_stage_case(cfg, seed, lengths, split_tokens, poison=True, q_gain=1.0)
     q_lat = O.absorb_query(d["q_nope"], d["w_uk"])
     q_bits = synth.store(q_lat.astype(np.float32), cfg.act_dtype)
     q_dec = O.decode(q_bits, cfg.act_dtype)
-    w = DeviceWorkload(inp, split_tokens=split_tokens)
+    w = DeviceWorkload(inp, split_tokens=split_tokens, fp8_scores=fp8_scores)
     w.decode(q_lat=to_device(q_bits, cfg.act_dtype, "cuda"))
     torch.cuda.synchronize()
     o_ref, lse_ref = O.latent_attention(q_dec, d["q_rope"], d["c_kv"], d["k_rope"], d["seq_lens"],
@@ -322,3 +322,45 @@ def test_decode_balanced_ranges(case):
     e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l[fin], l_ref[fin])
     print(f"  o_lat {e_o:.2e} lse {e_l:.2e}", flush=True)
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
+
+
+# fp8 score product (dims.fp8_scores = 1): the kernel rounds each row's 128-column query
+# slices to e4m3 and multiplies them with the stored codes.  The oracle stays the plain
+# definition on the stored cache, so the comparison includes the query rounding; the bar is
+# the fp8 workload's 6e-2, against the dequantized cache and against the latent before
+# quantization.
+@pytest.mark.parametrize("split_tokens,q_gain", [(0, 1.0), (128, 1.0), (0, 4.0)],
+                         ids=["balanced", "split128", "peaked"])
+def test_decode_fp8_scores(split_tokens, q_gain):
+    cfg = configs.SPEC_FP8.with_(batch=3, seq_len=700, cfg_id=31)
+    say("decode fp8 scores", split_tokens, q_gain, cfg)
+    o, l, o_ref, l_ref, inp, d, _ = decode_stage_case(cfg, 0, [700, 130, 4], split_tokens,
+                                                      q_gain=q_gain, fp8_scores=1)
+    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
+    pre = np.where(np.isfinite(inp.c_kv_prequant), inp.c_kv_prequant, 0).astype(np.float64)
+    q_dec = O.decode(synth.store(O.absorb_query(d["q_nope"], d["w_uk"]).astype(np.float32), "bf16"), "bf16")
+    o_pre, _ = O.latent_attention(q_dec, d["q_rope"], pre, d["k_rope"], d["seq_lens"], d["scale"])
+    e_pre = max_rel_err(o, o_pre)
+    print(f"  o_lat {e_o:.2e} lse {e_l:.2e} (dequantized cache), {e_pre:.2e} (pre-quantization)", flush=True)
+    # The query rounding costs about 2^-4 of each logit, so the error grows with the logits:
+    # at 4x the workload's logit scale (peaked attention) it is about twice the bar, which
+    # is checked here as a characterisation, not as parity.
+    bar = TOL_FP8_PREQUANT if q_gain == 1.0 else 2.5 * TOL_FP8_PREQUANT
+    assert e_o <= bar and e_l <= bar and e_pre <= bar
+
+
+def test_full_size_sampled_fp8_scores():
+    cfg = configs.SPEC_FP8
+    say("full size fp8 scores", cfg.name)
+    inp = synth.make_inputs(cfg, 0)
+    w = DeviceWorkload(inp, fp8_scores=1)
+    w.step()
+    torch.cuda.synchronize()
+    res = {"q_lat": to_host_f64(w.q_lat), "o_lat": to_host_f64(w.o_lat), "lse": to_host_f64(w.lse),
+           "out": to_host_f64(w.out)}
+    for k in ("o_lat", "out", "lse"):
+        assert np.all(np.isfinite(res[k])), k
+    batches = SAMPLE[cfg.name]
+    check_all(res, oracle_full(decoded_batches(inp, batches)), TOL_FP8_PREQUANT, batches=batches,
+              what=cfg.name + " fp8 scores")
+    del w
