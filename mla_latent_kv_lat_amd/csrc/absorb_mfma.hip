@@ -3,11 +3,13 @@
 // query, with W = W_UV it applies the value up-projection once to the attended latent
 // ("multi-head latent attention" glossary entry, paragraph on the decoupled RoPE key).
 //
-// A workgroup owns one head, 64 output columns and a group of 16 or 32 rows; it stages that
-// K x 64 slice of W[h] in LDS and multiplies its rows by it.  The product is formed transposed,
-// y^T[n, m] = W^T[n, :] . x^T[:, m], so that the staged weights are the A operand (read
-// transposed from LDS), the activation rows are the B operand straight from global
-// memory, and each lane stores 4 consecutive output columns.
+// A workgroup owns one head, 64 output columns and a group of 32 rows; it stages that K x 64
+// slice of W[h] and its rows of x in LDS and multiplies them.  The product is formed
+// transposed, y^T[n, m] = W^T[n, :] . x^T[:, m], so that the staged weights are the A operand
+// (read transposed from LDS), the activation rows the B operand, and each lane stores 4
+// consecutive output columns.  Every byte is fetched once per workgroup: the four waves
+// share the activation rows through LDS (the load path of a compute unit, not HBM, bounds
+// these small products).
 #include "device_common.h"
 #include "mfma_common.h"
 #include "mla_internal.h"
@@ -18,16 +20,9 @@ namespace {
 constexpr int kBN = 64;      // output columns per workgroup (one 16-column block per wave)
 constexpr int kThreads = 256;
 
-// Rows m .. m + 15 of head h as the B operand chunks of one 16-row block.  A row past M
-// loads row M - 1 instead (always in range): row m of the product depends on x row m only,
-// and rows past M are never stored, so the stand-in needs no masking.
-template <int K>
-__device__ __forceinline__ void load_x_block(bf16x8 (&bv)[K / 32], const uint16_t* __restrict__ x,
-                                             int m, int M, int H, int h, int g) {
-  const uint16_t* xr = x + (int64_t(min(m, M - 1)) * H + h) * K + 8 * g;
-#pragma unroll
-  for (int s = 0; s < K / 32; ++s) bv[s] = __builtin_bit_cast(bf16x8, ld16(xr + 32 * s));
-}
+// Activation rows in LDS: row r's 8-column chunk c is stored at chunk c ^ (r & 15), so the
+// 16 rows of one B-operand read hit distinct banks.
+__device__ __forceinline__ int xswz(int r) { return r & 15; }
 
 // Grid (H, N / 64, ceil(M / MG)): one workgroup per (head, 64-column tile, MG-row group).
 // Every load of the workgroup (its MG activation rows and the K x 64 weight slice) is issued
@@ -47,6 +42,7 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
                                                                void* __restrict__ y2 = nullptr, int N2 = 0) {
   constexpr int kBlocks = MG / 16;
   __shared__ __attribute__((aligned(16))) uint16_t wt[K * kBN];  // [k][64], chunks swizzled
+  __shared__ __attribute__((aligned(16))) uint16_t xs[MG * K];   // [row][k], chunks swizzled
   int h = blockIdx.x, n0 = blockIdx.y * kBN, m0 = blockIdx.z * MG;
   if (n0 >= N) {  // a tile of the second matrix (workgroup-uniform)
     n0 -= N;
@@ -57,10 +53,16 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, mm = lane & 15;
 
-  bf16x8 bv[kBlocks][K / 32];
+  // The MG rows of x (a row past M loads row M - 1 instead, always in range: row m of the
+  // product depends on x row m only, and rows past M are never stored) and the weight slice.
+  constexpr int kXPer = MG * K / 8 / kThreads;  // 16-byte activation chunks per thread
+  constexpr int kPer = K * 8 / kThreads;        // 16-byte weight chunks per thread
+  u32x4 xr[kXPer];
 #pragma unroll
-  for (int i = 0; i < kBlocks; ++i) load_x_block<K>(bv[i], x, m0 + 16 * i + mm, M, H, h, g);
-  constexpr int kPer = K * 8 / kThreads;  // 16-byte weight chunks per thread
+  for (int i = 0; i < kXPer; ++i) {
+    const int idx = tid + i * kThreads, r = idx / (K / 8), ch = idx % (K / 8);
+    xr[i] = ld16(x + (int64_t(min(m0 + r, M - 1)) * H + h) * K + 8 * ch);
+  }
   const uint16_t* wh = w + int64_t(h) * K * N + n0;
   u32x4 wr[kPer];
 #pragma unroll
@@ -69,11 +71,25 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
     wr[i] = ld16(wh + int64_t(k) * N + 8 * ch);
   }
 #pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int idx = tid + i * kThreads, r = idx / (K / 8), ch = idx % (K / 8);
+    *reinterpret_cast<u32x4*>(&xs[r * K + 8 * (ch ^ xswz(r))]) = xr[i];
+  }
+#pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int idx = tid + i * kThreads, k = idx >> 3, ch = idx & 7;
     *reinterpret_cast<u32x4*>(&wt[k * kBN + 8 * (ch ^ swz128(k))]) = wr[i];
   }
   __syncthreads();
+  // B operands: rows 16 i + mm, columns 32 s + 8 g + (0..7).
+  bf16x8 bv[kBlocks][K / 32];
+#pragma unroll
+  for (int i = 0; i < kBlocks; ++i)
+#pragma unroll
+    for (int s2 = 0; s2 < K / 32; ++s2) {
+      const int r = 16 * i + mm;
+      bv[i][s2] = *reinterpret_cast<const bf16x8*>(&xs[r * K + 8 * ((4 * s2 + g) ^ xswz(r))]);
+    }
 
 #pragma unroll
   for (int i = 0; i < kBlocks; ++i) {
