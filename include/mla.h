@@ -212,6 +212,30 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t d_model, const void* x
 mla_status mla_rope_query(const mla_dims* dims, void* q_rope, mla_dtype q_dt, const int32_t* seq_lens,
                           float rope_base, mla_rope_pairing pairing, void* stream);
 
+/* ---- prefill (explicit form) --------------------------------------------------------
+ * "Operator Notes (1): MLA", section 2 (restore K and V from the latent with the
+ * up-projections, then scaled dot-product attention), with the decoupled RoPE key of the
+ * glossary entry appended to every head's key.  For each sequence b of length
+ * L = seq_lens[b] (NULL: T) the s_q = dims.q_len queries are its last s_q rows; query i sees
+ * rows t <= L - s_q + i:
+ *   K_h[t] = [ W_UK[h] c_kv[b,t] | k_rope[b,t] ],  V_h[t] = W_UV[h]^T c_kv[b,t]
+ *   s = scale * (q_nope[b,i,h] . K_h[t][:128] + q_rope[b,i,h] . k_rope[b,t])
+ *   out[b,i,h,:] = sum_t softmax(s)_t V_h[t],  lse[b,i,h] = log sum_t exp(s_t)
+ * Shapes (all MLA_BF16, d_h = 128, d_c = 512, d_r = 64, any n_h <= 32767):
+ *   q_nope [B, s_q, n_h, 128], q_rope [B, s_q, n_h, 64] (already rotated),
+ *   c_kv [B, T, 512], k_rope [B, T, 64], w_uk [n_h, 128, 512], w_uv [n_h, 512, 128],
+ *   out [B, s_q, n_h, 128], lse [B, s_q, n_h] f32 or NULL; 1 <= s_q <= T; seq_lens [B] device
+ *   int32 with s_q <= L <= T (not validated: queries left without a visible row return 0
+ *   and -inf).  dims.split_tokens is ignored; dims.fp8_scores must be 0.
+ * workspace: at least mla_prefill_workspace_bytes(dims, T) bytes (256-byte aligned) of
+ * device scratch, holding the concatenated weights and every cache row's decompressed key
+ * and value (B * T * n_h * 512 bytes).  Other errors and the stream as for mla_decode. */
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t T);
+mla_status mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_rope, const void* c_kv,
+                       const void* k_rope, int32_t T, const int32_t* seq_lens, const void* w_uk,
+                       const void* w_uv, mla_dtype dt, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
 /* ---- utilities -------------------------------------------------------------------- */
 
 /* Copy rows of a block pool into a contiguous per-sequence array (the paged lookup alone):

@@ -29,7 +29,7 @@ EXPORTED = (
     "mla_absorb_q", "mla_decode", "mla_decode_paged", "mla_decode_workspace_bytes",
     "mla_decode_plan", "mla_absorb_out", "mla_gather_pages", "mla_fp8_e4m3_table",
     "mla_status_str", "mla_last_hip_error", "mla_version", "mla_cache_append_workspace_bytes",
-    "mla_cache_append", "mla_rope_query",
+    "mla_cache_append", "mla_rope_query", "mla_prefill_workspace_bytes", "mla_prefill",
 )
 
 
@@ -81,6 +81,8 @@ _SIGNATURES = {
     "mla_cache_append": [_dims_p, _i32, _vp, _vp, _vp, _i32, ctypes.c_float, _i32, _vp, _i32, _vp, _vp,
                          _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp],
     "mla_rope_query": [_dims_p, _vp, _i32, _vp, ctypes.c_float, _i32, _vp],
+    "mla_prefill_workspace_bytes": [_dims_p, _i32],
+    "mla_prefill": [_dims_p, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
     "mla_status_str": [_i32],
     "mla_last_hip_error": [],
     "mla_version": [],
@@ -100,6 +102,7 @@ def _lib() -> ctypes.CDLL:
             fn.restype = _i32
         lib.mla_decode_workspace_bytes.restype = _sz
         lib.mla_cache_append_workspace_bytes.restype = _sz
+        lib.mla_prefill_workspace_bytes.restype = _sz
         lib.mla_status_str.restype = ctypes.c_char_p
         _LIB = lib
     return _LIB
@@ -266,6 +269,22 @@ def mla_rope_query(d: MlaDims, q_rope, seq_lens, *, rope_base: float = 10000.0, 
     st = _lib().mla_rope_query(ctypes.byref(d), _ptr(q_rope), _dt(q_rope, dtype), _ptr(seq_lens), rope_base,
                                ROPE_PAIRING[pairing], _stream(stream))
     return _done(st, "mla_rope_query", check)
+
+
+def mla_prefill_workspace_bytes(d: MlaDims, T: int) -> int:
+    return int(_lib().mla_prefill_workspace_bytes(ctypes.byref(d), T))
+
+
+def mla_prefill(d: MlaDims, q_nope, q_rope, c_kv, k_rope, T: int, seq_lens, w_uk, w_uv, out, lse,
+                workspace, *, workspace_bytes=None, dtype=None, stream=None, check=True) -> int:
+    """Explicit-form causal prefill (argument marshalling only)."""
+    wsb = workspace_bytes
+    if wsb is None:
+        wsb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib().mla_prefill(ctypes.byref(d), _ptr(q_nope), _ptr(q_rope), _ptr(c_kv), _ptr(k_rope), T,
+                            _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _dt(q_nope, dtype), _ptr(out), _ptr(lse),
+                            _ptr(workspace), wsb, _stream(stream))
+    return _done(st, "mla_prefill", check)
 
 
 def mla_fp8_e4m3_table(out, *, stream=None, check=True) -> int:

@@ -316,6 +316,60 @@ mla_status mla_rope_query(const mla_dims* d, void* q_rope, mla_dtype q_dt, const
                                       int32_t(pairing), seq_lens, static_cast<hipStream_t>(stream)));
 }
 
+// Prefill shapes: every dimension but the latent-attention ones as in check_dims, any
+// q_len up to T.
+static mla_status check_prefill(const mla_dims* d, int32_t T, mla_dtype dt) {
+  if (!d) return MLA_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->q_len < 1 || d->n_heads < 1 || d->d_head < 1 || d->d_latent < 1 ||
+      d->d_rope < 0 || d->split_tokens < 0 || d->fp8_scores < 0 || d->fp8_scores > 1 || T < 1 ||
+      d->q_len > T)
+    return MLA_ERR_INVALID_ARG;
+  if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  if (!valid_dtype(dt)) return MLA_ERR_INVALID_ARG;
+  if (dt != MLA_BF16 || d->d_head != 128 || d->d_latent != 512 || d->d_rope != 64 || d->fp8_scores)
+    return MLA_ERR_UNSUPPORTED;
+  if (d->batch > kMaxGridDim || 2 * int64_t(d->n_heads) > kMaxGridDim ||
+      int64_t(d->batch) * T > INT32_MAX)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+size_t mla_prefill_workspace_bytes(const mla_dims* d, int32_t T) {
+  if (check_prefill(d, T, MLA_BF16) != MLA_OK) return 0;
+  return prefill_workspace_bytes(d->batch, T, d->n_heads);
+}
+
+mla_status mla_prefill(const mla_dims* d, const void* q_nope, const void* q_rope, const void* c_kv,
+                       const void* k_rope, int32_t T, const int32_t* seq_lens, const void* w_uk,
+                       const void* w_uv, mla_dtype dt, void* out, float* lse, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  mla_status st = check_prefill(d, T, dt);
+  if (st != MLA_OK) return st;
+  if (!q_nope || !q_rope || !c_kv || !k_rope || !w_uk || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  for (const void* p : {q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, static_cast<const void*>(out)})
+    if (!aligned(p, 16)) return MLA_ERR_INVALID_ARG;
+  if ((seq_lens && !aligned(seq_lens, 4)) || (lse && !aligned(lse, 4))) return MLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < prefill_workspace_bytes(d->batch, T, d->n_heads) ||
+      !aligned(workspace, 256))
+    return MLA_ERR_WORKSPACE;
+  PrefillArgs a{};
+  a.B = d->batch;
+  a.S = d->q_len;
+  a.H = d->n_heads;
+  a.T = T;
+  a.scale_log2 = d->softmax_scale * 1.4426950408889634f;
+  a.q_nope = q_nope;
+  a.q_rope = q_rope;
+  a.c_kv = c_kv;
+  a.k_rope = k_rope;
+  a.seq_lens = seq_lens;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.out = out;
+  a.lse = lse;
+  return hip_status(launch_prefill(a, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t mla_decode_workspace_bytes(const mla_dims* d, mla_dtype kv_dt, int32_t max_seq_len) {
   DecodePlan p;
   mla_dtype q_dt = kv_dt == MLA_F32 ? MLA_F32 : MLA_BF16;

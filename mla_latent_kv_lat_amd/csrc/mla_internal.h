@@ -59,6 +59,23 @@ struct DecodeArgs {
   float* part_lse;       // [B, S, rows] base-2 log-sum-exp of each split (S > 1)
 };
 
+// Everything the prefill kernels read or write.  Pointers are device pointers; the shapes
+// are d_h = 128, d_c = 512, d_r = 64, bf16.
+struct PrefillArgs {
+  int32_t B, S, H, T;    // S queries per sequence: the last S of its L rows
+  float scale_log2;      // softmax_scale * log2(e)
+  const void* q_nope;    // [B, S, H, 128]
+  const void* q_rope;    // [B, S, H, 64]
+  const void* c_kv;      // [B, T, 512]
+  const void* k_rope;    // [B, T, 64]
+  const int32_t* seq_lens;  // [B] or nullptr (every sequence has T rows)
+  const void* w_uk;      // [H, 128, 512]
+  const void* w_uv;      // [H, 512, 128]
+  void* out;             // [B, S, H, 128]
+  float* lse;            // [B, S, H] or nullptr
+  const void* kv;        // set by the launcher: decompressed [B * T, H, 256] in the workspace
+};
+
 // Everything the cache-write kernels read or write.  Pointers are device pointers.
 struct CacheAppendArgs {
   int32_t M, sq, d_model, dc, dr;   // M = B * s_q new tokens
@@ -107,5 +124,7 @@ int launch_cache_append(const CacheAppendArgs& a, hipStream_t s);
 int launch_rope_query(void* q, mla_dtype dt, int32_t B, int32_t sq, int32_t H, int32_t dr, float base,
                       int32_t pairing, const int32_t* seq_lens, hipStream_t s);
 int launch_fp8_bf16_table(float* out, hipStream_t s);
+size_t prefill_workspace_bytes(int32_t B, int32_t T, int32_t H);
+int launch_prefill(PrefillArgs a, void* ws, hipStream_t s);
 
 }  // namespace mla

@@ -1,0 +1,366 @@
+// Prefill in the explicit form: decompress the keys and values of every head from the
+// latent, then run causal attention over them ("Operator Notes (1): MLA", section 2: K and
+// V are restored from c_kv by the up-projections, then scaled dot-product attention with a
+// softmax and a product with V; the RoPE key of the "multi-head latent attention" glossary
+// entry, paragraph on the decoupled RoPE key, is appended to every head's key).  For long
+// prompts this is cheaper than the absorbed form used by decode: per query, key and head it
+// costs 2 (d_h + d_r) + 2 d_h flops instead of 2 (d_c + d_r) + 2 d_c, for a decompression
+// of 2 d_c (2 d_h) flops per token and head.
+//
+// Three kernels:
+//   * prefill_weights_kernel: wcat[h] = [W_UK[h] ; W_UV[h]^T] as 256 rows of d_c, so that
+//     both halves of the decompression read their weights as rows;
+//   * decompress_kernel: kv[m, h, 0:128] = c_kv[m] . W_UK[h]^T (the head's key),
+//     kv[m, h, 128:256] = c_kv[m] . W_UV[h] (its value), a 128 x 128-tiled matrix product
+//     over all B * T cache rows;
+//   * prefill_attn_kernel: 128 queries of one (sequence, head) per workgroup, 64-key tiles,
+//     scores as S^T = K Q^T and outputs as O^T += V^T P^T on the 32 x 32 x 16 bf16 matrix
+//     instruction, online softmax in base 2 per query lane.
+#include "device_common.h"
+#include "mfma_common.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kDH = 128;             // d_h
+constexpr int kDC = 512;             // d_c
+constexpr int kDR = 64;              // d_r
+constexpr int kDQK = kDH + kDR;      // 192: key width of one head
+constexpr int kNcat = 2 * kDH;       // 256: decompressed key then value of one head
+
+// ---------------------------------------------------------------------------------------
+// wcat[h][n][c] = W_UK[h][n][c] for n < 128, W_UV[h][c][n - 128] for n >= 128.
+// Grid (H, 8): block y copies or transposes 32 rows of the head's 256.
+__global__ __launch_bounds__(256) void prefill_weights_kernel(const uint16_t* __restrict__ w_uk,
+                                                              const uint16_t* __restrict__ w_uv,
+                                                              uint16_t* __restrict__ wcat) {
+  __shared__ uint16_t t[kDC][34];  // [c][n], padded against bank conflicts
+  const int h = blockIdx.x, n0 = blockIdx.y * 32, tid = threadIdx.x;
+  uint16_t* dst = wcat + (int64_t(h) * kNcat + n0) * kDC;
+  if (n0 < kDH) {
+    const uint16_t* src = w_uk + (int64_t(h) * kDH + n0) * kDC;
+    for (int i = tid; i < 32 * kDC / 8; i += 256)
+      *reinterpret_cast<u32x4*>(dst + 8 * i) = *reinterpret_cast<const u32x4*>(src + 8 * i);
+  } else {
+    const uint16_t* src = w_uv + int64_t(h) * kDC * kDH + (n0 - kDH);
+    for (int i = tid; i < kDC * 32; i += 256) t[i / 32][i % 32] = src[int64_t(i / 32) * kDH + i % 32];
+    __syncthreads();
+    for (int i = tid; i < 32 * kDC; i += 256) dst[i] = t[i % kDC][i / kDC];
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// kv[m, h, n0 + n] = sum_c x[m, c] * wcat[h][n0 + n][c] for a 128 (m) x 128 (n) tile.
+// Four waves, each a 64 x 64 block formed as D^T[n][m] (weights as the A operand, cache
+// rows as the B operand), in K steps of 64 staged through LDS (double buffered).  LDS
+// rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at c ^ ((r >> 1) & 7),
+// so the 16 rows of one operand read hit distinct banks.
+constexpr int kGT = 128;   // tile edge
+constexpr int kGK = 64;    // K per stage
+
+__device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
+
+__global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restrict__ x,
+                                                         const uint16_t* __restrict__ wcat,
+                                                         uint16_t* __restrict__ kv, int M, int H) {
+  __shared__ __attribute__((aligned(16))) uint16_t sm[2][2][kGT * kGK];  // [buf][A = w, B = x]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int h = blockIdx.y >> 1, nt = blockIdx.y & 1;
+  const int m0 = blockIdx.x * kGT, n0 = nt * kGT;
+  const int wn = wv >> 1, wm = wv & 1;  // this wave's 64 x 64 block: n 64 wn.., m 64 wm..
+  const int n32 = lane & 31, hh = lane >> 5;
+
+  // Global -> register loads of one stage: 128 rows x 8 chunks of each operand, 4 chunks
+  // per thread per operand.
+  const uint16_t* wrow = wcat + (int64_t(h) * kNcat + n0) * kDC;
+  u32x4 ra[4], rb[4];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, r = idx >> 3, ch = idx & 7;
+      ra[i] = ld16(wrow + int64_t(r) * kDC + k0 + 8 * ch);
+      rb[i] = ld16(x + int64_t(min(m0 + r, M - 1)) * kDC + k0 + 8 * ch);
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + 256 * i, r = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(&sm[buf][0][r * kGK + 8 * (ch ^ gswz(r))]) = ra[i];
+      *reinterpret_cast<u32x4*>(&sm[buf][1][r * kGK + 8 * (ch ^ gswz(r))]) = rb[i];
+    }
+  };
+
+  f32x16 acc[2][2];  // [n block][m block]
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
+
+  load(0);
+  store(0);
+  __syncthreads();
+  constexpr int kStages = kDC / kGK;
+  for (int st = 0; st < kStages; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < kStages) load((st + 1) * kGK);
+#pragma unroll
+    for (int ks = 0; ks < kGK / 16; ++ks) {
+      const int ch = 2 * ks + hh;
+      bf16x8 av[2], bv[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int rn = 64 * wn + 32 * j + n32, rm = 64 * wm + 32 * j + n32;
+        av[j] = *reinterpret_cast<const bf16x8*>(&sm[buf][0][rn * kGK + 8 * (ch ^ gswz(rn))]);
+        bv[j] = *reinterpret_cast<const bf16x8*>(&sm[buf][1][rm * kGK + 8 * (ch ^ gswz(rm))]);
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+    }
+    if (st + 1 < kStages) {
+      store(buf ^ 1);
+      __syncthreads();
+    }
+  }
+  __syncthreads();  // every wave done with the operand buffers
+  // Stage the bf16 tile as [m][n] (reusing the operand buffers), then store whole rows.
+  uint16_t* ot = &sm[0][0][0];  // 128 x 128 bf16 = 32 KB
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int m = 64 * wm + 32 * b + n32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = 64 * wn + 32 * a + 8 * i + 4 * hh;  // 4 consecutive n
+        const uint32_t w0 = pack_bf16x2(acc[a][b][4 * i], acc[a][b][4 * i + 1]);
+        const uint32_t w1 = pack_bf16x2(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3]);
+        *reinterpret_cast<u32x2*>(&ot[m * kGT + 8 * ((n >> 3) ^ (m & 15)) + (n & 7)]) = u32x2{w0, w1};
+      }
+    }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int idx = tid + 256 * i, m = idx >> 4, ch = idx & 15;
+    if (m0 + m < M)
+      *reinterpret_cast<u32x4*>(kv + (int64_t(m0 + m) * H + h) * kNcat + n0 + 8 * ch) =
+          *reinterpret_cast<const u32x4*>(&ot[m * kGT + 8 * (ch ^ (m & 15))]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Causal attention of the decompressed heads.  Query i of sequence b (length L) sits at
+// position L - S + i and sees keys t <= L - S + i.
+constexpr int kQB = 128;    // queries per workgroup (32 per wave)
+constexpr int kKT = 64;     // keys per tile
+constexpr int kKPitch = kDQK;  // bf16 per staged key row (384 bytes)
+
+struct alignas(16) AttnSmem {
+  uint16_t k[kKT * kKPitch];  // [key][192]: decompressed key then RoPE key, chunks swizzled
+  uint16_t v[kKT * kDH];      // [key][128], swz32 chunks (read transposed)
+};
+
+// Chunk (16 bytes) c of staged key row r sits at (c & ~7) | ((c ^ (r >> 1)) & 7).
+__device__ __forceinline__ int kswz(int r, int c) { return (c & ~7) | ((c ^ (r >> 1)) & 7); }
+
+__device__ __forceinline__ void swap32_u32(uint32_t& a, uint32_t& b) {
+  float fa = __builtin_bit_cast(float, a), fb = __builtin_bit_cast(float, b);
+  permlane32_swap(fa, fb);
+  a = __builtin_bit_cast(uint32_t, fa);
+  b = __builtin_bit_cast(uint32_t, fb);
+}
+
+__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ AttnSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int n = lane & 31, hh = lane >> 5;
+  const int qblk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int S = a.S, H = a.H;
+  const int L = min(max(a.seq_lens ? a.seq_lens[b] : a.T, 0), a.T);
+  const int q0 = qblk * kQB;
+  const int qi = q0 + 32 * wv + n;        // this lane's query
+  const int pos = L - S + qi;             // its position; keys t <= pos are visible
+  // Keys the workgroup needs: up to the position of its last query.
+  const int pos_last = L - S + min(q0 + kQB, S) - 1;
+  const int nkeys = min(L, pos_last + 1);
+  const int ntiles = nkeys > 0 ? (nkeys + kKT - 1) / kKT : 0;
+
+  // Query operand (B of S^T = K Q^T): k-step s covers dims 16 s + 8 hh + (0..7) of
+  // [q_nope | q_rope].
+  bf16x8 qb[kDQK / 16];
+  {
+    const int64_t row = (int64_t(b) * S + min(qi, S - 1)) * H + h;
+    const uint16_t* qn = static_cast<const uint16_t*>(a.q_nope) + row * kDH;
+    const uint16_t* qr = static_cast<const uint16_t*>(a.q_rope) + row * kDR;
+#pragma unroll
+    for (int s = 0; s < kDQK / 16; ++s)
+      qb[s] = __builtin_bit_cast(bf16x8, s < kDH / 16 ? ld16(qn + 16 * s + 8 * hh) : ld16(qr + 16 * (s - kDH / 16) + 8 * hh));
+  }
+
+  // Tile loads: per key the 32 chunks of its kv row (16 of key, 16 of value) and the 8
+  // chunks of its RoPE key; 8 + 2 chunks per thread.  Keys past the sequence load its last
+  // row (always valid) and are masked.
+  u32x4 pf[10];
+  const uint16_t* kvh = static_cast<const uint16_t*>(a.kv) + int64_t(h) * kNcat;
+  const uint16_t* kr = static_cast<const uint16_t*>(a.k_rope);
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, key = idx >> 5, ch = idx & 31;
+      const int64_t t = int64_t(b) * a.T + min(t0 + key, L - 1);
+      pf[i] = ld16(kvh + t * H * kNcat + 8 * ch);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i, key = idx >> 3, ch = idx & 7;
+      const int64_t t = int64_t(b) * a.T + min(t0 + key, L - 1);
+      pf[8 + i] = ld16(kr + t * kDR + 8 * ch);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int idx = tid + 256 * i, key = idx >> 5, ch = idx & 31;
+      uint16_t* dst = (ch < 16) ? &sm.k[key * kKPitch + 8 * kswz(key, ch)]
+                                : &sm.v[key * kDH + 8 * ((ch - 16) ^ swz32(key))];
+      *reinterpret_cast<u32x4*>(dst) = pf[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int idx = tid + 256 * i, key = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(&sm.k[key * kKPitch + 8 * kswz(key, 16 + ch)]) = pf[8 + i];  // RoPE after the key
+    }
+  };
+
+  f32x16 oacc[kDH / 32];  // O^T: dims 32 db + 8 i + 4 hh + r, query n
+#pragma unroll
+  for (int d = 0; d < kDH / 32; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  if (ntiles > 0) load(0);
+  for (int j = 0; j < ntiles; ++j) {
+    const int t0 = j * kKT;
+    __syncthreads();  // previous tile consumed
+    store();
+    __syncthreads();
+    if (j + 1 < ntiles) load(t0 + kKT);
+
+    // S^T[key][query] for keys t0 + 32 kb + (8 i + 4 hh + r).
+    f32x16 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
+      const int key = 32 * kb + n;
+#pragma unroll
+      for (int s = 0; s < kDQK / 16; ++s) {
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.k[key * kKPitch + 8 * kswz(key, 2 * s + hh)]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[s], sacc[kb], 0, 0, 0);
+      }
+    }
+    // Mask, scale to base 2, and the running max over this query's 64 keys (half in the
+    // partner lane n + 32).
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int t = t0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+        const float v = t <= pos ? sacc[kb][e] * a.scale_log2 : -INFINITY;
+        sacc[kb][e] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    {
+      float x0 = tmax, x1 = tmax;
+      permlane32_swap(x0, x1);
+      tmax = fmaxf(x0, x1);
+    }
+    const float m_new = fmaxf(m_run, tmax);
+    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
+    m_run = m_new;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sacc[kb][e] + neg_m);
+        sacc[kb][e] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+#pragma unroll
+    for (int d = 0; d < kDH / 32; ++d) oacc[d] *= alpha;
+
+    // P^T operands: k-step ks covers keys 16 ks + 8 hh + (0..7); this lane holds keys
+    // 16 (ks % 2) + 4 hh + (0..3) (register group 2 (ks % 2)) and + 8 (group 2 (ks % 2) + 1)
+    // of block ks / 2; one swap with the partner lane completes the operand.
+#pragma unroll
+    for (int ks = 0; ks < kKT / 16; ++ks) {
+      const int kb = ks >> 1, g = 2 * (ks & 1);
+      uint32_t u0 = pack_bf16x2(sacc[kb][4 * g], sacc[kb][4 * g + 1]);
+      uint32_t u1 = pack_bf16x2(sacc[kb][4 * g + 2], sacc[kb][4 * g + 3]);
+      uint32_t v0 = pack_bf16x2(sacc[kb][4 * g + 4], sacc[kb][4 * g + 5]);
+      uint32_t v1 = pack_bf16x2(sacc[kb][4 * g + 6], sacc[kb][4 * g + 7]);
+      swap32_u32(u0, v0);
+      swap32_u32(u1, v1);
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{u0, u1, v0, v1});
+#pragma unroll
+      for (int d = 0; d < kDH / 32; ++d)
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_operand_tr32(sm.v, 16 * ks, 32 * d, lane), pb,
+                                                          oacc[d], 0, 0, 0);
+    }
+  }
+
+  float lt = l_run;
+  {
+    float x0 = lt, x1 = lt;
+    permlane32_swap(x0, x1);
+    lt = x0 + x1;
+  }
+  if (qi >= S) return;
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const int64_t row = (int64_t(b) * S + qi) * H + h;
+  uint16_t* o = static_cast<uint16_t*>(a.out) + row * kDH;
+#pragma unroll
+  for (int d = 0; d < kDH / 32; ++d)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int col = 32 * d + 8 * i + 4 * hh;
+      *reinterpret_cast<u32x2*>(o + col) = u32x2{pack_bf16x2(oacc[d][4 * i] * inv, oacc[d][4 * i + 1] * inv),
+                                                 pack_bf16x2(oacc[d][4 * i + 2] * inv, oacc[d][4 * i + 3] * inv)};
+    }
+  if (a.lse && hh == 0) a.lse[row] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+}
+
+}  // namespace
+
+namespace {
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+}  // namespace
+
+size_t prefill_workspace_bytes(int32_t B, int32_t T, int32_t H) {
+  return round256(size_t(H) * kNcat * kDC * 2) + round256(size_t(B) * T * H * kNcat * 2);
+}
+
+int launch_prefill(PrefillArgs a, void* ws, hipStream_t s) {
+  uint16_t* wcat = static_cast<uint16_t*>(ws);
+  uint16_t* kv = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + round256(size_t(a.H) * kNcat * kDC * 2));
+  hipLaunchKernelGGL(prefill_weights_kernel, dim3(a.H, kNcat / 32), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(a.w_uk), static_cast<const uint16_t*>(a.w_uv), wcat);
+  const int M = a.B * a.T;
+  hipLaunchKernelGGL(decompress_kernel, dim3((M + kGT - 1) / kGT, 2 * a.H), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(a.c_kv), wcat, kv, M, a.H);
+  a.kv = kv;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((a.S + kQB - 1) / kQB, a.H, a.B), dim3(256), 0, s, a);
+  return int(hipGetLastError());
+}
+
+}  // namespace mla

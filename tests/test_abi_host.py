@@ -288,3 +288,40 @@ def test_fp8_scores_argument():
     small = cfg.with_(n_heads=8)  # general kernel
     assert L.mla_decode_plan(L.dims_from_config(small, fp8_scores=1), "fp8", small.seq_len,
                              check=False)[0] == L.MLA_ERR_UNSUPPORTED
+
+
+def test_prefill_workspace_and_argument_errors():
+    """mla_prefill: workspace formula, and every rejected argument returns before a launch."""
+    r = lambda x: (x + 255) // 256 * 256
+    d = v2(batch=2, q_len=300, n_heads=8)
+    assert L.mla_prefill_workspace_bytes(d, 300) == r(8 * 256 * 512 * 2) + r(2 * 300 * 8 * 256 * 2)
+    assert L.mla_prefill_workspace_bytes(d, 299) == 0            # q_len > T
+    assert L.mla_prefill_workspace_bytes(v2(d_head=64), 300) == 0  # no kernel for d_h = 64
+
+    def call(dims=d, T=300, dtype="bf16", ws=A, ws_bytes=1 << 40, **ptrs):
+        p = dict(q_nope=A, q_rope=A, c_kv=A, k_rope=A, seq_lens=A, w_uk=A, w_uv=A, out=A, lse=A)
+        p.update(ptrs)
+        return L.mla_prefill(dims, p["q_nope"], p["q_rope"], p["c_kv"], p["k_rope"], T, p["seq_lens"],
+                             p["w_uk"], p["w_uv"], p["out"], p["lse"], ws, workspace_bytes=ws_bytes,
+                             dtype=dtype, check=False)
+
+    E, U, W = L.MLA_ERR_INVALID_ARG, L.MLA_ERR_UNSUPPORTED, L.MLA_ERR_WORKSPACE
+    assert L.library().mla_prefill_workspace_bytes(None, 300) == 0
+    assert call(T=0) == E
+    assert call(T=299) == E                      # more queries than rows
+    assert call(dims=v2(batch=0)) == E
+    assert call(dims=v2(softmax_scale=0.0)) == E
+    assert call(dtype="f32") == U
+    assert call(dims=v2(d_latent=256)) == U
+    assert call(dims=v2(d_rope=32)) == U
+    assert call(dims=v2(fp8_scores=1)) == U
+    assert call(dims=v2(n_heads=40000)) == U      # 2 n_h column tiles exceed a grid dimension
+    for k in ("q_nope", "q_rope", "c_kv", "k_rope", "w_uk", "w_uv", "out"):
+        assert call(**{k: None}) == E, k
+        assert call(**{k: A + 8}) == E, k         # not 16-byte aligned
+    assert call(seq_lens=A + 2) == E
+    assert call(lse=A + 2) == E
+    need = L.mla_prefill_workspace_bytes(d, 300)
+    assert call(ws=None) == W
+    assert call(ws_bytes=need - 1) == W
+    assert call(ws=A + 16, ws_bytes=need) == W     # not 256-byte aligned
