@@ -201,6 +201,63 @@ def bench_cache_append(args, cfg) -> int:
     return 0
 
 
+def bench_prefill(args, cfg) -> int:
+    """Time mla_prefill alone: B prompts of T tokens, every token a query (explicit form:
+    decompression of K and V per head, then causal attention).  Bound by the matrix cores."""
+    import torch
+    from mla_latent_kv_lat_amd import capi, synth
+    from mla_latent_kv_lat_amd.runner import to_device
+    B, T = args.prefill_batch, args.prefill_len
+    pc = cfg.with_(batch=B, q_len=T, seq_len=T, cfg_id=50, paged=False, kv_dtype="bf16")
+    print(f"[bench] prefill B={B} T={T} n_h={pc.n_heads}: generating inputs", file=sys.stderr, flush=True)
+    inp = synth.make_inputs(pc, 0, lengths=np.full(B, T, np.int32))
+    dev = lambda a, k="bf16": to_device(a, k, "cuda")
+    q_nope, q_rope, c_kv, k_rope = dev(inp.q_nope), dev(inp.q_rope), dev(inp.c_kv), dev(inp.k_rope)
+    w_uk, w_uv, lens = dev(inp.w_uk), dev(inp.w_uv), dev(inp.seq_lens, "i32")
+    H, dh = pc.n_heads, pc.d_head
+    out = torch.empty(B, T, H, dh, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(B, T, H, dtype=torch.float32, device="cuda")
+    d = capi.dims_from_config(pc)
+    ws = torch.empty(capi.mla_prefill_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+
+    def call():
+        capi.mla_prefill(d, q_nope, q_rope, c_kv, k_rope, T, lens, w_uk, w_uv, out, lse, ws)
+
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < args.ramp_ms:
+        call()
+        n += 1
+        torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    K = args.steps
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(K):
+        call()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / K
+    decomp = 2.0 * B * T * pc.d_latent * H * 2 * dh
+    attn = 2.0 * H * B * (T * (T + 1) / 2) * (dh + pc.d_rope + dh)
+    tf = (decomp + attn) / (ms * 1e-3) / 1e12
+    print(f"[bench] prefill: {ms * 1e3:.1f} us/call", file=sys.stderr, flush=True)
+    print(json.dumps({
+        "metric": "MLA prefill (explicit form) TFLOP/s", "value": round(tf, 1), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": K, "warmup": args.warmup, "clock_ramp": {"ms": args.ramp_ms, "steps": n},
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded Gaussian prompts, cache and random-init weights)",
+        "config": {"workload": f"prefill_bf16_b{B}_t{T}_h{H}", "batch": B, "seq_len": T, "n_heads": H,
+                   "d_head": dh, "d_latent": pc.d_latent, "d_rope": pc.d_rope},
+        "gflop": {"decompression": round(decomp / 1e9, 1), "attention": round(attn / 1e9, 1)},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 1), "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tf / BF16_MFMA_PEAK_TFS, 4), "traffic": None},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,9 +275,11 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
-    ap.add_argument("--stage", choices=("step", "cache_append"), default="step",
+    ap.add_argument("--prefill-batch", type=int, default=1, help="prompts for --stage prefill")
+    ap.add_argument("--prefill-len", type=int, default=4096, help="prompt length for --stage prefill")
+    ap.add_argument("--stage", choices=("step", "cache_append", "prefill"), default="step",
                     help="step: absorb_q + decode + absorb_out (the headline); cache_append: the "
-                         "cache write of the new tokens alone")
+                         "cache write of the new tokens alone; prefill: mla_prefill of whole prompts")
     ap.add_argument("--d-model", type=int, default=5120, help="hidden width for --stage cache_append")
     args = ap.parse_args()
 
@@ -236,6 +295,8 @@ def main() -> int:
     cfg = configs.BY_NAME[args.workload] if args.workload else configs.HEADLINE
     if args.stage == "cache_append":
         return bench_cache_append(args, cfg)
+    if args.stage == "prefill":
+        return bench_prefill(args, cfg)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, 0)
     wc = work_counts(cfg, inp.seq_lens)
