@@ -13,7 +13,7 @@
 //   * decompress_kernel: kv[m, h, 0:128] = c_kv[m] . W_UK[h]^T (the head's key),
 //     kv[m, h, 128:256] = c_kv[m] . W_UV[h] (its value), a 128 x 128-tiled matrix product
 //     over all B * T cache rows;
-//   * prefill_attn_kernel: 128 queries of one (sequence, head) per workgroup, 64-key tiles,
+//   * prefill_attn_kernel: 256 queries of one (sequence, head) per workgroup, 64-key tiles,
 //     scores as S^T = K Q^T and outputs as O^T += V^T P^T on the 32 x 32 x 16 bf16 matrix
 //     instruction, online softmax in base 2 per query lane.
 #include "device_common.h"
@@ -156,11 +156,23 @@ __global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------------------
 // Causal attention of the decompressed heads.  Query i of sequence b (length L) sits at
 // position L - S + i and sees keys t <= L - S + i.
-constexpr int kQB = 128;    // queries per workgroup (32 per wave)
-constexpr int kKT = 64;     // keys per tile
+//
+// A workgroup (8 waves, one per compute unit) owns 256 queries of one (sequence, head);
+// wave w owns queries 32 w .. 32 w + 31.  Key tiles of 64 keys are staged in LDS (double
+// buffered, one barrier per tile; the next tile's loads are in flight in registers while a
+// tile is computed).  Per tile a wave forms S^T = K Q^T (keys as the A operand from LDS, its
+// queries as the B operand held in registers), the online softmax in its lanes (lane n and
+// n + 32 share query n), and O^T += V^T P^T (V read transposed from LDS).  The query lane's
+// reference max only moves when a tile exceeds it by more than kTau (base 2), so the
+// accumulators are rarely rescaled; masking is applied only to tiles that reach past the
+// wave's first query, and tiles entirely past its last query are skipped.
+constexpr int kQB = 256;       // queries per workgroup
+constexpr int kAttnThreads = 512;
+constexpr int kKT = 64;        // keys per tile
 constexpr int kKPitch = kDQK;  // bf16 per staged key row (384 bytes)
+constexpr float kTau = 8.f;
 
-struct alignas(16) AttnSmem {
+struct alignas(16) AttnTile {
   uint16_t k[kKT * kKPitch];  // [key][192]: decompressed key then RoPE key, chunks swizzled
   uint16_t v[kKT * kDH];      // [key][128], swz32 chunks (read transposed)
 };
@@ -175,9 +187,10 @@ __device__ __forceinline__ void swap32_u32(uint32_t& a, uint32_t& b) {
   b = __builtin_bit_cast(uint32_t, fb);
 }
 
-__global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
-  __shared__ AttnSmem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+__global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillArgs a) {
+  __shared__ AttnTile sm[2];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
   const int qblk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int S = a.S, H = a.H;
@@ -185,6 +198,8 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   const int q0 = qblk * kQB;
   const int qi = q0 + 32 * wv + n;        // this lane's query
   const int pos = L - S + qi;             // its position; keys t <= pos are visible
+  const int pos_first_w = L - S + q0 + 32 * wv;            // the wave's first query
+  const int pos_last_w = L - S + min(q0 + 32 * wv + 32, S) - 1;
   // Keys the workgroup needs: up to the position of its last query.
   const int pos_last = L - S + min(q0 + kQB, S) - 1;
   const int nkeys = min(L, pos_last + 1);
@@ -203,38 +218,32 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   }
 
   // Tile loads: per key the 32 chunks of its kv row (16 of key, 16 of value) and the 8
-  // chunks of its RoPE key; 8 + 2 chunks per thread.  Keys past the sequence load its last
+  // chunks of its RoPE key; 4 + 1 chunks per thread.  Keys past the sequence load its last
   // row (always valid) and are masked.
-  u32x4 pf[10];
+  u32x4 pf[5];
   const uint16_t* kvh = static_cast<const uint16_t*>(a.kv) + int64_t(h) * kNcat;
   const uint16_t* kr = static_cast<const uint16_t*>(a.k_rope);
   auto load = [&](int t0) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i, key = idx >> 5, ch = idx & 31;
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + kAttnThreads * i, key = idx >> 5, ch = idx & 31;
       const int64_t t = int64_t(b) * a.T + min(t0 + key, L - 1);
       pf[i] = ld16(kvh + t * H * kNcat + 8 * ch);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i, key = idx >> 3, ch = idx & 7;
-      const int64_t t = int64_t(b) * a.T + min(t0 + key, L - 1);
-      pf[8 + i] = ld16(kr + t * kDR + 8 * ch);
-    }
+    const int key = tid >> 3, ch = tid & 7;
+    const int64_t t = int64_t(b) * a.T + min(t0 + key, L - 1);
+    pf[4] = ld16(kr + t * kDR + 8 * ch);
   };
-  auto store = [&]() {
+  auto store = [&](AttnTile& tl) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int idx = tid + 256 * i, key = idx >> 5, ch = idx & 31;
-      uint16_t* dst = (ch < 16) ? &sm.k[key * kKPitch + 8 * kswz(key, ch)]
-                                : &sm.v[key * kDH + 8 * ((ch - 16) ^ swz32(key))];
+    for (int i = 0; i < 4; ++i) {
+      const int idx = tid + kAttnThreads * i, key = idx >> 5, ch = idx & 31;
+      uint16_t* dst = (ch < 16) ? &tl.k[key * kKPitch + 8 * kswz(key, ch)]
+                                : &tl.v[key * kDH + 8 * ((ch - 16) ^ swz32(key))];
       *reinterpret_cast<u32x4*>(dst) = pf[i];
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int idx = tid + 256 * i, key = idx >> 3, ch = idx & 7;
-      *reinterpret_cast<u32x4*>(&sm.k[key * kKPitch + 8 * kswz(key, 16 + ch)]) = pf[8 + i];  // RoPE after the key
-    }
+    const int key = tid >> 3, ch = tid & 7;
+    *reinterpret_cast<u32x4*>(&tl.k[key * kKPitch + 8 * kswz(key, 16 + ch)]) = pf[4];  // RoPE after the key
   };
 
   f32x16 oacc[kDH / 32];  // O^T: dims 32 db + 8 i + 4 hh + r, query n
@@ -242,16 +251,9 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
   for (int d = 0; d < kDH / 32; ++d)
 #pragma unroll
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
-  float m_run = -INFINITY, l_run = 0.f;
+  float m_ref = -INFINITY, l_run = 0.f;
 
-  if (ntiles > 0) load(0);
-  for (int j = 0; j < ntiles; ++j) {
-    const int t0 = j * kKT;
-    __syncthreads();  // previous tile consumed
-    store();
-    __syncthreads();
-    if (j + 1 < ntiles) load(t0 + kKT);
-
+  auto compute = [&](const AttnTile& tl, int t0) {
     // S^T[key][query] for keys t0 + 32 kb + (8 i + 4 hh + r).
     f32x16 sacc[2];
 #pragma unroll
@@ -261,31 +263,41 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
       const int key = 32 * kb + n;
 #pragma unroll
       for (int s = 0; s < kDQK / 16; ++s) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&sm.k[key * kKPitch + 8 * kswz(key, 2 * s + hh)]);
+        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&tl.k[key * kKPitch + 8 * kswz(key, 2 * s + hh)]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[s], sacc[kb], 0, 0, 0);
       }
     }
-    // Mask, scale to base 2, and the running max over this query's 64 keys (half in the
-    // partner lane n + 32).
+    // Scale to base 2 (masking only where the tile reaches past the wave's first query),
+    // and the tile max of this query's 64 keys (half of them in the partner lane).
     float tmax = -INFINITY;
+    if (t0 + kKT - 1 > pos_first_w) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int t = t0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-        const float v = t <= pos ? sacc[kb][e] * a.scale_log2 : -INFINITY;
-        sacc[kb][e] = v;
-        tmax = fmaxf(tmax, v);
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int t = t0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
+          sacc[kb][e] = t <= pos ? sacc[kb][e] * a.scale_log2 : -INFINITY;
+          tmax = fmaxf(tmax, sacc[kb][e]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          sacc[kb][e] *= a.scale_log2;
+          tmax = fmaxf(tmax, sacc[kb][e]);
+        }
+    }
     {
       float x0 = tmax, x1 = tmax;
       permlane32_swap(x0, x1);
       tmax = fmaxf(x0, x1);
     }
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
-    const float neg_m = m_new == -INFINITY ? 0.f : -m_new;
-    m_run = m_new;
+    // Move the reference only when the tile exceeds it by more than kTau.
+    const bool grow = tmax > m_ref + kTau;  // false while nothing is visible
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_ref - tmax) : 1.f;
+    if (grow) m_ref = tmax;
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
     float psum = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -296,8 +308,10 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
         psum += p;
       }
     l_run = l_run * alpha + psum;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int d = 0; d < kDH / 32; ++d) oacc[d] *= alpha;
+      for (int d = 0; d < kDH / 32; ++d) oacc[d] *= alpha;
+    }
 
     // P^T operands: k-step ks covers keys 16 ks + 8 hh + (0..7); this lane holds keys
     // 16 (ks % 2) + 4 hh + (0..3) (register group 2 (ks % 2)) and + 8 (group 2 (ks % 2) + 1)
@@ -314,8 +328,24 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{u0, u1, v0, v1});
 #pragma unroll
       for (int d = 0; d < kDH / 32; ++d)
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_operand_tr32(sm.v, 16 * ks, 32 * d, lane), pb,
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_operand_tr32(tl.v, 16 * ks, 32 * d, lane), pb,
                                                           oacc[d], 0, 0, 0);
+    }
+  };
+
+  if (ntiles > 0) {
+    load(0);
+    store(sm[0]);
+    __syncthreads();
+    if (ntiles > 1) load(kKT);
+  }
+  for (int j = 0; j < ntiles; ++j) {
+    const int t0 = j * kKT;
+    if (t0 <= pos_last_w) compute(sm[j & 1], t0);  // tiles past the wave's last query add nothing
+    if (j + 1 < ntiles) {
+      store(sm[(j + 1) & 1]);  // that buffer was last read in step j - 1, before its barrier
+      __syncthreads();
+      if (j + 2 < ntiles) load(t0 + 2 * kKT);
     }
   }
 
@@ -337,7 +367,7 @@ __global__ __launch_bounds__(256, 2) void prefill_attn_kernel(PrefillArgs a) {
       *reinterpret_cast<u32x2*>(o + col) = u32x2{pack_bf16x2(oacc[d][4 * i] * inv, oacc[d][4 * i + 1] * inv),
                                                  pack_bf16x2(oacc[d][4 * i + 2] * inv, oacc[d][4 * i + 3] * inv)};
     }
-  if (a.lse && hh == 0) a.lse[row] = lt > 0.f ? (m_run + log2f(lt)) * kLn2 : -INFINITY;
+  if (a.lse && hh == 0) a.lse[row] = lt > 0.f ? (m_ref + log2f(lt)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
@@ -359,7 +389,7 @@ int launch_prefill(PrefillArgs a, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(decompress_kernel, dim3((M + kGT - 1) / kGT, 2 * a.H), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.c_kv), wcat, kv, M, a.H);
   a.kv = kv;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((a.S + kQB - 1) / kQB, a.H, a.B), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((a.S + kQB - 1) / kQB, a.H, a.B), dim3(kAttnThreads), 0, s, a);
   return int(hipGetLastError());
 }
 
