@@ -14,7 +14,8 @@ named by page title and section:
   key, which also states that the up-projections can be absorbed into the query
   and output projections);
 * "Multi-Head Latent Attention and the compression of the KV cache" dispatch (the
-  paragraph on mathematical equivalence through associativity).
+  paragraph on mathematical equivalence through associativity);
+* the same Operator Notes page, section 4 (query compression).
 
 Readings of points the pages leave open (stated once here, used throughout):
 
@@ -370,3 +371,47 @@ def quantize_e4m3fn_rows(c):
     mag = cand_codes[np.argmin(pref * 1e9 + d, axis=-1)]
     sign = np.where(np.signbit(y), 0x80, 0x00).astype(np.uint8)
     return (mag | sign).astype(np.uint8), scale
+
+
+# ---------------------------------------------------------------------------------
+# Query compression and the output projection ("Operator Notes (1): MLA", section 4: the
+# query is compressed too, c_q = x W_DQ and Q = c_q W_UQ; section 2: out = O W_O), and the
+# folds of the glossary entry's paragraph on the decoupled RoPE key (W_UK absorbed into
+# the query side, W_UV into the output side).
+# ---------------------------------------------------------------------------------
+#
+# Readings: the query latent width d_cq is a parameter (the page writes "d_c dim"); the
+# up-projection of the query yields, per head, the d_h content part followed by the d_r
+# RoPE part, kept as two matrices w_uq [d_cq, n_h, d_h] and w_qr [d_cq, n_h, d_r]; no
+# normalisation sits between the two projections (the pages show none).
+
+
+def query_from_hidden(x, w_dq, w_uq, w_qr):
+    """x [M, d_model] -> (q_nope [M, n_h, d_h], q_rope [M, n_h, d_r]) through c_q = x W_DQ."""
+    c_q = np.asarray(x, np.float64) @ np.asarray(w_dq, np.float64)
+    w_uq = np.asarray(w_uq, np.float64)
+    w_qr = np.asarray(w_qr, np.float64)
+    q_nope = np.einsum("mk,khj->mhj", c_q, w_uq)
+    q_rope = np.einsum("mk,khj->mhj", c_q, w_qr)
+    return q_nope, q_rope
+
+
+def fold_query_weights(w_uq, w_uk):
+    """W_UQK[k, h, c] = sum_j w_uq[k, h, j] w_uk[h, j, c]: the query up-projection
+    followed by the key absorption, as one matrix from c_q to the latent query."""
+    return np.einsum("khj,hjc->khc", np.asarray(w_uq, np.float64), np.asarray(w_uk, np.float64))
+
+
+def output_projection(out_heads, w_o):
+    """out_heads [M, n_h, d_h] (the concatenated head outputs O) -> O W_O [M, d_model]."""
+    o = np.asarray(out_heads, np.float64)
+    return o.reshape(o.shape[0], -1) @ np.asarray(w_o, np.float64)
+
+
+def fold_output_weights(w_uv, w_o):
+    """W_UVO[h, c, :] = sum_j w_uv[h, c, j] w_o[h d_h + j, :]: the value up-projection
+    followed by the output projection, per head, so that out = sum_h o_lat[h] W_UVO[h]."""
+    w_uv = np.asarray(w_uv, np.float64)
+    n_h, d_c, d_h = w_uv.shape
+    w_o = np.asarray(w_o, np.float64).reshape(n_h, d_h, -1)
+    return np.einsum("hcj,hjd->hcd", w_uv, w_o)

@@ -9,6 +9,7 @@ import pytest
 from oracle import mla_oracle as O
 import test_oracle as P
 import test_oracle_cache_write as PC
+import test_oracle_query as PQ
 
 _orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
 
@@ -91,6 +92,27 @@ def _quantize_ties_up(c):
     return codes, scale
 
 
+def _fold_query_head_swapped(w_uq, w_uk):
+    return np.einsum("khj,hjc->khc", np.asarray(w_uq, np.float64), np.asarray(w_uk, np.float64)[::-1])
+
+
+def _query_rope_from_content_matrix(x, w_dq, w_uq, w_qr):
+    c_q = np.asarray(x, np.float64) @ np.asarray(w_dq, np.float64)
+    return np.einsum("mk,khj->mhj", c_q, w_uq), np.einsum("mk,khj->mhj", c_q, w_uq)[..., :w_qr.shape[2]]
+
+
+def _output_transposed_heads(out_heads, w_o):
+    o = np.asarray(out_heads, np.float64)
+    return o.transpose(0, 2, 1).reshape(o.shape[0], -1) @ np.asarray(w_o, np.float64)
+
+
+def _fold_output_wrong_slice(w_uv, w_o):
+    w_uv = np.asarray(w_uv, np.float64)
+    n_h, d_c, d_h = w_uv.shape
+    w_o = np.asarray(w_o, np.float64).reshape(d_h, n_h, -1).transpose(1, 0, 2)
+    return np.einsum("hcj,hjd->hcd", w_uv, w_o)
+
+
 CASES = [
     ("latent_attention", _latent_attention_no_rope, lambda: P.pin_absorbed_vs_explicit(P.small_inputs())),
     ("latent_attention", _latent_attention_scale_on_latent_only,
@@ -112,6 +134,10 @@ CASES = [
     ("new_token_positions", _positions_off_by_one, PC.pin_cache_append_brute),
     ("quantize_e4m3fn_rows", _quantize_half_scale, PC.pin_quantize_special),
     ("quantize_e4m3fn_rows", _quantize_ties_up, PC.pin_quantize_special),
+    ("fold_query_weights", _fold_query_head_swapped, PQ.pin_fold_query_selection),
+    ("query_from_hidden", _query_rope_from_content_matrix, PQ.pin_query_brute_force),
+    ("output_projection", _output_transposed_heads, PQ.pin_output_identity_and_brute_force),
+    ("fold_output_weights", _fold_output_wrong_slice, PQ.pin_fold_output_brute_force),
 ]
 
 
