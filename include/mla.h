@@ -236,6 +236,18 @@ mla_status mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_r
                        const void* w_uv, mla_dtype dt, void* out, float* lse, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/* ---- projections: query compression, output projection, folds ------------------------
+ * y[m, n] = sum_k x[m, k] * w[k, n] (MLA_BF16 in and out, fp32 accumulation), row-major
+ * x [M, K], w [K, N], y [M, N].  The weight-streaming products around the attention:
+ * c_q = x W_DQ and the query up-projections ("Operator Notes (1): MLA", section 4), the
+ * output projection O W_O (section 2), and products with folded weights.  K must be a
+ * multiple of 256 and N of 64 (else MLA_ERR_UNSUPPORTED); 1 <= M <= 32 * 65535.  The
+ * workspace (at least mla_linear_workspace_bytes(M, K, N) bytes, 16-byte aligned) holds
+ * the fp32 partial sums of the 256-wide slices of K; contents irrelevant on entry. */
+size_t mla_linear_workspace_bytes(int32_t M, int32_t K, int32_t N);
+mla_status mla_linear(const void* x, const void* w, void* y, int32_t M, int32_t K, int32_t N, mla_dtype dt,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---- utilities -------------------------------------------------------------------- */
 
 /* Copy rows of a block pool into a contiguous per-sequence array (the paged lookup alone):

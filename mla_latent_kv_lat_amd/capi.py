@@ -30,6 +30,7 @@ EXPORTED = (
     "mla_decode_plan", "mla_absorb_out", "mla_gather_pages", "mla_fp8_e4m3_table",
     "mla_status_str", "mla_last_hip_error", "mla_version", "mla_cache_append_workspace_bytes",
     "mla_cache_append", "mla_rope_query", "mla_prefill_workspace_bytes", "mla_prefill",
+    "mla_linear_workspace_bytes", "mla_linear",
 )
 
 
@@ -82,6 +83,8 @@ _SIGNATURES = {
                          _i32, _i32, _vp, _i32, _vp, _vp, _sz, _vp],
     "mla_rope_query": [_dims_p, _vp, _i32, _vp, ctypes.c_float, _i32, _vp],
     "mla_prefill_workspace_bytes": [_dims_p, _i32],
+    "mla_linear_workspace_bytes": [_i32, _i32, _i32],
+    "mla_linear": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp],
     "mla_prefill": [_dims_p, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
     "mla_status_str": [_i32],
     "mla_last_hip_error": [],
@@ -103,6 +106,7 @@ def _lib() -> ctypes.CDLL:
         lib.mla_decode_workspace_bytes.restype = _sz
         lib.mla_cache_append_workspace_bytes.restype = _sz
         lib.mla_prefill_workspace_bytes.restype = _sz
+        lib.mla_linear_workspace_bytes.restype = _sz
         lib.mla_status_str.restype = ctypes.c_char_p
         _LIB = lib
     return _LIB
@@ -285,6 +289,26 @@ def mla_prefill(d: MlaDims, q_nope, q_rope, c_kv, k_rope, T: int, seq_lens, w_uk
                             _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _dt(q_nope, dtype), _ptr(out), _ptr(lse),
                             _ptr(workspace), wsb, _stream(stream))
     return _done(st, "mla_prefill", check)
+
+
+def mla_linear_workspace_bytes(M: int, K: int, N: int) -> int:
+    return int(_lib().mla_linear_workspace_bytes(M, K, N))
+
+
+def mla_linear(x, w, y, workspace, *, M=None, K=None, N=None, workspace_bytes=None, dtype=None,
+               stream=None, check=True) -> int:
+    """y = x . w for row-major x [M, K], w [K, N], y [M, N] (argument marshalling only)."""
+    if M is None:
+        M = y.shape[0]
+    if K is None:
+        K = w.shape[0]
+    if N is None:
+        N = w.shape[1]
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib().mla_linear(_ptr(x), _ptr(w), _ptr(y), M, K, N, _dt(x, dtype), _ptr(workspace),
+                           workspace_bytes, _stream(stream))
+    return _done(st, "mla_linear", check)
 
 
 def mla_fp8_e4m3_table(out, *, stream=None, check=True) -> int:

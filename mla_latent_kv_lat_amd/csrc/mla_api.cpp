@@ -334,6 +334,32 @@ static mla_status check_prefill(const mla_dims* d, int32_t T, mla_dtype dt) {
   return MLA_OK;
 }
 
+// Projections: bf16, K a multiple of 256, N a multiple of 64, M in [1, 32 * 65535].
+static mla_status check_linear(int32_t M, int32_t K, int32_t N, mla_dtype dt) {
+  if (M < 1 || K < 1 || N < 1 || !valid_dtype(dt)) return MLA_ERR_INVALID_ARG;
+  if (dt != MLA_BF16 || K % 256 != 0 || N % 64 != 0 || int64_t(M) > 32 * int64_t(kMaxGridDim) ||
+      K / 256 > kMaxGridDim || N / 64 > kMaxGridDim || int64_t(M) * N / 8 > int64_t(INT32_MAX) * 256)
+    return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+size_t mla_linear_workspace_bytes(int32_t M, int32_t K, int32_t N) {
+  if (check_linear(M, K, N, MLA_BF16) != MLA_OK) return 0;
+  return size_t(M) * (K / 256) * N * 4;
+}
+
+mla_status mla_linear(const void* x, const void* w, void* y, int32_t M, int32_t K, int32_t N, mla_dtype dt,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  mla_status st = check_linear(M, K, N, dt);
+  if (st != MLA_OK) return st;
+  if (!x || !w || !y) return MLA_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16)) return MLA_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < size_t(M) * (K / 256) * N * 4 || !aligned(workspace, 16))
+    return MLA_ERR_WORKSPACE;
+  return hip_status(launch_linear(x, w, y, M, K, N, static_cast<float*>(workspace),
+                                  static_cast<hipStream_t>(stream)));
+}
+
 size_t mla_prefill_workspace_bytes(const mla_dims* d, int32_t T) {
   if (check_prefill(d, T, MLA_BF16) != MLA_OK) return 0;
   return prefill_workspace_bytes(d->batch, T, d->n_heads);

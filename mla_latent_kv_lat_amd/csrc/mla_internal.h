@@ -125,6 +125,8 @@ int launch_rope_query(void* q, mla_dtype dt, int32_t B, int32_t sq, int32_t H, i
                       int32_t pairing, const int32_t* seq_lens, hipStream_t s);
 int launch_fp8_bf16_table(float* out, hipStream_t s);
 size_t prefill_workspace_bytes(int32_t B, int32_t T, int32_t H);
+int launch_linear(const void* x, const void* w, void* y, int32_t M, int32_t K, int32_t N, float* part,
+                  hipStream_t s);
 int launch_prefill(PrefillArgs a, void* ws, hipStream_t s);
 
 }  // namespace mla

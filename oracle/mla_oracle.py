@@ -391,15 +391,15 @@ def query_from_hidden(x, w_dq, w_uq, w_qr):
     c_q = np.asarray(x, np.float64) @ np.asarray(w_dq, np.float64)
     w_uq = np.asarray(w_uq, np.float64)
     w_qr = np.asarray(w_qr, np.float64)
-    q_nope = np.einsum("mk,khj->mhj", c_q, w_uq)
-    q_rope = np.einsum("mk,khj->mhj", c_q, w_qr)
+    q_nope = np.einsum("mk,khj->mhj", c_q, w_uq, optimize=True)
+    q_rope = np.einsum("mk,khj->mhj", c_q, w_qr, optimize=True)
     return q_nope, q_rope
 
 
 def fold_query_weights(w_uq, w_uk):
     """W_UQK[k, h, c] = sum_j w_uq[k, h, j] w_uk[h, j, c]: the query up-projection
     followed by the key absorption, as one matrix from c_q to the latent query."""
-    return np.einsum("khj,hjc->khc", np.asarray(w_uq, np.float64), np.asarray(w_uk, np.float64))
+    return np.einsum("khj,hjc->khc", np.asarray(w_uq, np.float64), np.asarray(w_uk, np.float64), optimize=True)
 
 
 def output_projection(out_heads, w_o):
@@ -414,4 +414,4 @@ def fold_output_weights(w_uv, w_o):
     w_uv = np.asarray(w_uv, np.float64)
     n_h, d_c, d_h = w_uv.shape
     w_o = np.asarray(w_o, np.float64).reshape(n_h, d_h, -1)
-    return np.einsum("hcj,hjd->hcd", w_uv, w_o)
+    return np.einsum("hcj,hjd->hcd", w_uv, w_o, optimize=True)

@@ -325,3 +325,23 @@ def test_prefill_workspace_and_argument_errors():
     assert call(ws=None) == W
     assert call(ws_bytes=need - 1) == W
     assert call(ws=A + 16, ws_bytes=need) == W     # not 256-byte aligned
+
+
+def test_linear_workspace_and_argument_errors():
+    assert L.mla_linear_workspace_bytes(32, 5120, 1536) == 32 * 20 * 1536 * 4
+    assert L.mla_linear_workspace_bytes(32, 5000, 1536) == 0     # K not a multiple of 256
+    assert L.mla_linear_workspace_bytes(32, 5120, 100) == 0      # N not a multiple of 64
+    assert L.mla_linear_workspace_bytes(0, 5120, 1536) == 0
+
+    def call(x=A, w=A, y=A, M=32, K=512, N=128, dtype="bf16", ws=A, ws_bytes=1 << 30):
+        return L.mla_linear(x, w, y, ws, M=M, K=K, N=N, workspace_bytes=ws_bytes, dtype=dtype, check=False)
+
+    E, U, W = L.MLA_ERR_INVALID_ARG, L.MLA_ERR_UNSUPPORTED, L.MLA_ERR_WORKSPACE
+    assert call(M=0) == E and call(K=0) == E and call(N=-64) == E
+    assert call(K=300) == U and call(N=100) == U and call(dtype="f32") == U
+    assert call(M=32 * 65535 + 1) == U
+    for k in ("x", "w", "y"):
+        assert call(**{k: None}) == E, k
+        assert call(**{k: A + 8}) == E, k
+    need = L.mla_linear_workspace_bytes(32, 512, 128)
+    assert call(ws=None) == W and call(ws_bytes=need - 1) == W and call(ws=A + 4, ws_bytes=need) == W
