@@ -258,6 +258,96 @@ def bench_prefill(args, cfg) -> int:
     return 0
 
 
+def bench_projections(args, cfg) -> int:
+    """Time the weight-streaming steps around the attention at DeepSeek-V2 widths for the
+    batch's new tokens: the query path from hidden states, unfolded (c_q = x W_DQ, the
+    content and RoPE up-projections, key absorption) and folded (c_q, the RoPE
+    up-projection, c_q W_UQK), and the output path (value absorption, O W_O).  Each is
+    bound by its weight bytes, streamed from HBM (replicas cycled)."""
+    import torch
+    from mla_latent_kv_lat_amd import capi
+    M, dm, dcq, H, dh, dr, dc = cfg.batch * cfg.q_len, args.d_model, args.d_cq, cfg.n_heads, cfg.d_head, cfg.d_rope, cfg.d_latent
+    g = torch.Generator(device="cpu").manual_seed(0)
+    rnd = lambda *shape, std=1.0: (torch.randn(*shape, generator=g) * std).to(torch.bfloat16).cuda()
+    x = rnd(M, dm)
+    reps = []
+    for _ in range(max(1, args.replicas)):
+        w = {"dq": rnd(dm, dcq, std=dm ** -0.5), "uq": rnd(dcq, H * dh, std=dcq ** -0.5),
+             "qr": rnd(dcq, H * dr, std=dcq ** -0.5), "uk": rnd(H, dh, dc, std=dc ** -0.5),
+             "uv": rnd(H, dc, dh, std=dc ** -0.5), "o": rnd(H * dh, dm, std=(H * dh) ** -0.5)}
+        w["uqk"] = torch.empty(dcq, H * dc, dtype=torch.bfloat16, device="cuda")
+        capi.mla_absorb_q(capi.dims(dcq, 1, H, dh, dc, dr, 1.0), w["uq"].view(dcq, 1, H, dh), w["uk"], w["uqk"])
+        reps.append(w)
+    c_q = torch.empty(M, dcq, dtype=torch.bfloat16, device="cuda")
+    q_nope = torch.empty(M, H * dh, dtype=torch.bfloat16, device="cuda")
+    q_rope = torch.empty(M, H * dr, dtype=torch.bfloat16, device="cuda")
+    q_lat = torch.empty(M, H * dc, dtype=torch.bfloat16, device="cuda")
+    o_lat = rnd(M, H * dc)
+    heads = torch.empty(M, H * dh, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(M, dm, dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(max(capi.mla_linear_workspace_bytes(M, K, N) for K, N in
+                         ((dm, dcq), (dcq, H * dh), (dcq, H * dr), (dcq, H * dc), (H * dh, dm))),
+                     dtype=torch.uint8, device="cuda")
+    dq = capi.dims(M, 1, H, dh, dc, dr, 1.0)
+
+    def query_unfolded(w):
+        capi.mla_linear(x, w["dq"], c_q, ws)
+        capi.mla_linear(c_q, w["uq"], q_nope, ws)
+        capi.mla_linear(c_q, w["qr"], q_rope, ws)
+        capi.mla_absorb_q(dq, q_nope.view(M, 1, H, dh), w["uk"], q_lat.view(M, 1, H, dc))
+
+    def query_folded(w):
+        capi.mla_linear(x, w["dq"], c_q, ws)
+        capi.mla_linear(c_q, w["qr"], q_rope, ws)
+        capi.mla_linear(c_q, w["uqk"], q_lat, ws)
+
+    def output(w):
+        capi.mla_absorb_out(dq, o_lat.view(M, 1, H, dc), w["uv"], heads.view(M, 1, H, dh))
+        capi.mla_linear(heads, w["o"], y, ws)
+
+    def timed(fn):
+        for k in range(args.warmup):
+            fn(reps[k % len(reps)])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for k in range(args.steps):
+            fn(reps[k % len(reps)])
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < args.ramp_ms:
+        query_unfolded(reps[0])
+        torch.cuda.synchronize()
+    ms_u, ms_f, ms_o = timed(query_unfolded), timed(query_folded), timed(output)
+    b = lambda n: 2 * n
+    bytes_u = b(dm * dcq + dcq * H * dh + dcq * H * dr + H * dh * dc)
+    bytes_f = b(dm * dcq + dcq * H * dr + dcq * H * dc)
+    bytes_o = b(H * dc * dh + H * dh * dm)
+    gbs = lambda nb, ms: nb / (ms * 1e-3) / 1e9
+    print(f"[bench] query unfolded {ms_u * 1e3:.1f} us, folded {ms_f * 1e3:.1f} us, output {ms_o * 1e3:.1f} us",
+          file=sys.stderr, flush=True)
+    ach = gbs(bytes_u, ms_u)
+    print(json.dumps({
+        "metric": "MLA query path from hidden states (unfolded), weight GB/s", "value": round(ach, 1),
+        "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_u, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded Gaussian hidden states and random-init weights)",
+        "config": {"workload": f"projections_m{M}_dmodel{dm}_dcq{dcq}_h{H}", "tokens": M, "d_model": dm,
+                   "d_cq": dcq, "n_heads": H, "d_head": dh, "d_rope": dr, "d_latent": dc,
+                   "weight_replicas": len(reps)},
+        "query_unfolded_us": round(ms_u * 1e3, 2), "query_unfolded_weight_MB": round(bytes_u / 1e6, 1),
+        "query_folded_us": round(ms_f * 1e3, 2), "query_folded_weight_MB": round(bytes_f / 1e6, 1),
+        "output_us": round(ms_o * 1e3, 2), "output_weight_MB": round(bytes_o / 1e6, 1),
+        "output_GBs": round(gbs(bytes_o, ms_o), 1), "query_folded_GBs": round(gbs(bytes_f, ms_f), 1),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+    }), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -277,9 +367,11 @@ def main() -> int:
                     help="also run one plain device copy of this size (for counter calibration)")
     ap.add_argument("--prefill-batch", type=int, default=1, help="prompts for --stage prefill")
     ap.add_argument("--prefill-len", type=int, default=4096, help="prompt length for --stage prefill")
-    ap.add_argument("--stage", choices=("step", "cache_append", "prefill"), default="step",
+    ap.add_argument("--d-cq", type=int, default=1536, help="query latent width for --stage projections")
+    ap.add_argument("--stage", choices=("step", "cache_append", "prefill", "projections"), default="step",
                     help="step: absorb_q + decode + absorb_out (the headline); cache_append: the "
-                         "cache write of the new tokens alone; prefill: mla_prefill of whole prompts")
+                         "cache write of the new tokens alone; prefill: mla_prefill of whole prompts; "
+                         "projections: query path from hidden states (unfolded and folded) and output path")
     ap.add_argument("--d-model", type=int, default=5120, help="hidden width for --stage cache_append")
     args = ap.parse_args()
 
@@ -297,6 +389,8 @@ def main() -> int:
         return bench_cache_append(args, cfg)
     if args.stage == "prefill":
         return bench_prefill(args, cfg)
+    if args.stage == "projections":
+        return bench_projections(args, cfg)
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     inp = synth.make_inputs(cfg, 0)
     wc = work_counts(cfg, inp.seq_lens)
