@@ -53,7 +53,7 @@ constexpr int kTile = 32;               // tokens per tile
 constexpr int kThreads = 512;           // 4 score waves + 4 output waves
 constexpr int kCols = 128;              // latent columns per score wave / output wave
 constexpr int kRopeW = 16;              // RoPE dims per score wave
-constexpr int kPPitch = kTile + 8;      // bf16 per row of the probability tile
+constexpr int kPPitch = kTile;          // bf16 per row of the probability tile (swizzled, p_swz)
 constexpr int kMaxPrefixBatch = 2 * kThreads;  // largest batch whose tile prefix each workgroup computes
 // A row's reference max (the value its probabilities are taken relative to) only moves
 // when a tile's max exceeds it by more than this many base-2 units, so probabilities stay
@@ -74,9 +74,14 @@ struct alignas(16) Smem {
 static_assert(kMaxInKernelPrefixBatch <= kMaxPrefixBatch, "in-kernel tile prefix does not fit");
 
 // Partial-score rows hold 8 chunks of 4 tokens; chunk c of row r is stored at c ^ sp_swz(r),
-// which keeps both the score waves' writes (16 rows, one chunk) and the softmax reads
-// (2 rows, 8 chunks) on distinct LDS banks.
-__device__ __forceinline__ int sp_swz(int row) { return (row >> 1) & 7; }
+// which keeps both the score waves' writes (8 lanes per LDS cycle: 8 rows, one chunk each)
+// and the softmax reads (16 lanes per cycle: 2 rows, 8 chunks) on distinct LDS banks.
+__device__ __forceinline__ int sp_swz(int row) { return row & 7; }
+
+// Probability rows hold 4 chunks of 8 tokens (64 bytes); chunk c of row r is stored at
+// c ^ p_swz(r), which keeps the softmax writes (16 lanes of 8 bytes: 2 rows) and the output
+// waves' operand reads (16 lanes of 16 bytes: 16 rows, one chunk each) on distinct banks.
+__device__ __forceinline__ int p_swz(int row) { return (row >> 2) & 3; }
 
 // Softmax state of one lane: row `row` of the workgroup, tokens 4 tg .. 4 tg + 3 of each tile.
 struct SoftmaxLane {
@@ -121,7 +126,8 @@ __device__ __forceinline__ void softmax_tile(Smem& sm, SoftmaxLane& st, int buf,
     for (int e = 0; e < 4; ++e) pr[e] *= t4[e];
   }
   st.l_run = st.l_run * alpha + psum;
-  *reinterpret_cast<u32x2*>(&sm.p[buf][st.row][4 * st.tg]) = u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
+  *reinterpret_cast<u32x2*>(&sm.p[buf][st.row][8 * ((st.tg >> 1) ^ p_swz(st.row)) + 4 * (st.tg & 1)]) =
+      u32x2{pack_bf16x2(pr[0], pr[1]), pack_bf16x2(pr[2], pr[3])};
   if (st.tg == 0) sm.alpha[buf][st.row] = alpha;
 }
 
@@ -518,7 +524,8 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
       for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks)
-          pb[rb2][ks] = *reinterpret_cast<const bf16x8*>(&sm.p[buf][32 * rb2 + c.n][16 * ks + 8 * c.h]);
+          pb[rb2][ks] = *reinterpret_cast<const bf16x8*>(
+              &sm.p[buf][32 * rb2 + c.n][8 * ((2 * ks + c.h) ^ p_swz(32 * rb2 + c.n))]);
       if (__any((al[0] != 1.f) | (al[1] != 1.f))) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)

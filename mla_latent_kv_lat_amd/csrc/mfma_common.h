@@ -50,10 +50,16 @@ __device__ __forceinline__ int swz256(int row) {
 }
 
 // Chunk swizzle for 256-byte-row tiles read with 32-column transposed reads (see
-// lds_operand_tr32): chunk ^ swz32(row).  Bijective on the low 4 row bits (16 rows of a
-// 16-byte-per-lane store hit distinct banks), and the 4 rows of each transposed-read pass
-// put their 64-byte column groups on distinct banks.
-__device__ __forceinline__ int swz32(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
+// lds_operand_tr32): chunk ^ swz32(row).  On gfx950 a 16-byte LDS read serves 16 lanes
+// (256 bytes) per cycle and a 16-byte write 8 lanes (128 bytes).  The swizzle is
+// bijective on the low 4 row bits (16 rows read at one chunk each hit distinct banks); its
+// low 3 bits are bijective on each aligned group of 8 rows (8 rows written at one chunk
+// each hit distinct banks); and its high 2 bits are bijective on each aligned group of 4
+// rows (the 4 rows of each transposed-read pass put their 64-byte column groups on
+// distinct banks).
+__device__ __forceinline__ int swz32(int row) {
+  return ((row & 3) << 2) | ((row >> 2) & 1) | ((((row >> 1) ^ (row >> 3)) & 1) << 1);
+}
 
 // Transposed read of 4 bf16 (see the layout note above) from LDS.
 __device__ __forceinline__ u32x2 lds_read_tr4(const uint16_t* p) {
