@@ -162,23 +162,29 @@ __global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restr
 // buffered, one barrier per tile; the next tile's loads are in flight in registers while a
 // tile is computed).  Per tile a wave forms S^T = K Q^T (keys as the A operand from LDS, its
 // queries as the B operand held in registers), the online softmax in its lanes (lane n and
-// n + 32 share query n), and O^T += V^T P^T (V read transposed from LDS).  The query lane's
-// reference max only moves when a tile exceeds it by more than kTau (base 2), so the
-// accumulators are rarely rescaled; masking is applied only to tiles that reach past the
-// wave's first query, and tiles entirely past its last query are skipped.
+// n + 32 share query n), and O^T += V^T P^T (V read transposed from LDS).  The two key
+// blocks of the score product alternate (independent accumulators) and every LDS operand is
+// read a few products ahead of its use.  The query lane's reference max only moves when a
+// tile exceeds it by more than kTau (base 2), so the accumulators are rarely rescaled;
+// masking is applied only to tiles that reach past the wave's first query, and tiles
+// entirely past its last query are skipped.  Workgroups are launched longest first (query
+// blocks from the end of the prompt), which evens out the causal imbalance.
 constexpr int kQB = 256;       // queries per workgroup
 constexpr int kAttnThreads = 512;
 constexpr int kKT = 64;        // keys per tile
-constexpr int kKPitch = kDQK;  // bf16 per staged key row (384 bytes)
+// Staged rows are padded instead of swizzled, so every operand address is a per-lane base
+// plus a constant.  Key rows: 192 bf16 + 8 (400 bytes: 16 consecutive rows read at one
+// 16-byte chunk fall on distinct banks, as 400 / 16 = 25 is odd).  Value rows: 128 bf16 +
+// 32 (320 bytes: the 4 rows of one transposed-read pass start 8 banks x 4 bytes apart... i.e.
+// at distinct 32-byte bank groups).
+constexpr int kKPitch = kDQK + 8;
+constexpr int kVPitch = kDH + 32;
 constexpr float kTau = 8.f;
 
 struct alignas(16) AttnTile {
-  uint16_t k[kKT * kKPitch];  // [key][192]: decompressed key then RoPE key, chunks swizzled
-  uint16_t v[kKT * kDH];      // [key][128], swz32 chunks (read transposed)
+  uint16_t k[kKT * kKPitch];  // [key][200]: decompressed key, RoPE key, padding
+  uint16_t v[kKT * kVPitch];  // [key][160]: value, padding (read transposed)
 };
-
-// Chunk (16 bytes) c of staged key row r sits at (c & ~7) | ((c ^ (r >> 1)) & 7).
-__device__ __forceinline__ int kswz(int r, int c) { return (c & ~7) | ((c ^ (r >> 1)) & 7); }
 
 __device__ __forceinline__ void swap32_u32(uint32_t& a, uint32_t& b) {
   float fa = __builtin_bit_cast(float, a), fb = __builtin_bit_cast(float, b);
@@ -187,12 +193,14 @@ __device__ __forceinline__ void swap32_u32(uint32_t& a, uint32_t& b) {
   b = __builtin_bit_cast(uint32_t, fb);
 }
 
+// Grid (H, query blocks, B): query block gridDim.y - 1 - blockIdx.y, so that the blocks with
+// the most keys are dispatched first.
 __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillArgs a) {
   __shared__ AttnTile sm[2];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, hh = lane >> 5;
-  const int qblk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int h = blockIdx.x, qblk = gridDim.y - 1 - blockIdx.y, b = blockIdx.z;
   const int S = a.S, H = a.H;
   const int L = min(max(a.seq_lens ? a.seq_lens[b] : a.T, 0), a.T);
   const int q0 = qblk * kQB;
@@ -238,12 +246,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillAr
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int idx = tid + kAttnThreads * i, key = idx >> 5, ch = idx & 31;
-      uint16_t* dst = (ch < 16) ? &tl.k[key * kKPitch + 8 * kswz(key, ch)]
-                                : &tl.v[key * kDH + 8 * ((ch - 16) ^ swz32(key))];
+      uint16_t* dst = (ch < 16) ? &tl.k[key * kKPitch + 8 * ch] : &tl.v[key * kVPitch + 8 * (ch - 16)];
       *reinterpret_cast<u32x4*>(dst) = pf[i];
     }
     const int key = tid >> 3, ch = tid & 7;
-    *reinterpret_cast<u32x4*>(&tl.k[key * kKPitch + 8 * kswz(key, 16 + ch)]) = pf[4];  // RoPE after the key
+    *reinterpret_cast<u32x4*>(&tl.k[key * kKPitch + 8 * (16 + ch)]) = pf[4];  // RoPE after the key
   };
 
   f32x16 oacc[kDH / 32];  // O^T: dims 32 db + 8 i + 4 hh + r, query n
@@ -254,18 +261,26 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillAr
   float m_ref = -INFINITY, l_run = 0.f;
 
   auto compute = [&](const AttnTile& tl, int t0) {
-    // S^T[key][query] for keys t0 + 32 kb + (8 i + 4 hh + r).
+    // S^T[key][query] for keys t0 + 32 kb + (8 i + 4 hh + r); product i is key block i % 2,
+    // k-step i / 2, and its operand is read kPre products ahead.
     f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) sacc[kb][e] = 0.f;
-      const int key = 32 * kb + n;
+    constexpr int kSteps = 2 * (kDQK / 16), kPre = 4;
+    const uint16_t* kbase = &tl.k[n * kKPitch + 8 * hh];
+    auto operand = [&](int i) {
+      return *reinterpret_cast<const bf16x8*>(kbase + (i & 1) * 32 * kKPitch + 16 * (i >> 1));
+    };
+    bf16x8 ring[kPre];
 #pragma unroll
-      for (int s = 0; s < kDQK / 16; ++s) {
-        const bf16x8 av = *reinterpret_cast<const bf16x8*>(&tl.k[key * kKPitch + 8 * kswz(key, 2 * s + hh)]);
-        sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[s], sacc[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < kPre; ++i) ring[i] = operand(i);
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const bf16x8 av = ring[i % kPre];
+      if (i + kPre < kSteps) ring[i % kPre] = operand(i + kPre);
+      sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[i >> 1], sacc[i & 1], 0, 0, 0);
     }
     // Scale to base 2 (masking only where the tile reaches past the wave's first query),
     // and the tile max of this query's 64 keys (half of them in the partner lane).
@@ -316,9 +331,28 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillAr
     // P^T operands: k-step ks covers keys 16 ks + 8 hh + (0..7); this lane holds keys
     // 16 (ks % 2) + 4 hh + (0..3) (register group 2 (ks % 2)) and + 8 (group 2 (ks % 2) + 1)
     // of block ks / 2; one swap with the partner lane completes the operand.
+    // V^T operands (transposed reads): lane l of 16-lane group G supplies row
+    // 8 (G >> 1) + (l >> 2) % 4 (+ 4 for the second half) and columns 16 (G & 1) + 4 (l % 4)
+    // of each 16-row x 32-column block; k-step ks adds 16 rows, column block d adds 32.
+    const int G = lane >> 4;
+    const uint16_t* vbase = &tl.v[(8 * (G >> 1) + ((lane >> 2) & 3)) * kVPitch + 16 * (G & 1) + 4 * (lane & 3)];
+    auto voperand = [&](int ks, int d) {
+      const u32x2 lo = lds_read_tr4(vbase + 16 * ks * kVPitch + 32 * d);
+      const u32x2 hi = lds_read_tr4(vbase + (16 * ks + 4) * kVPitch + 32 * d);
+      return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    bf16x8 vnext[kDH / 32];
+#pragma unroll
+    for (int d = 0; d < kDH / 32; ++d) vnext[d] = voperand(0, d);
 #pragma unroll
     for (int ks = 0; ks < kKT / 16; ++ks) {
       const int kb = ks >> 1, g = 2 * (ks & 1);
+      bf16x8 vcur[kDH / 32];
+#pragma unroll
+      for (int d = 0; d < kDH / 32; ++d) {
+        vcur[d] = vnext[d];
+        if (ks + 1 < kKT / 16) vnext[d] = voperand(ks + 1, d);
+      }
       uint32_t u0 = pack_bf16x2(sacc[kb][4 * g], sacc[kb][4 * g + 1]);
       uint32_t u1 = pack_bf16x2(sacc[kb][4 * g + 2], sacc[kb][4 * g + 3]);
       uint32_t v0 = pack_bf16x2(sacc[kb][4 * g + 4], sacc[kb][4 * g + 5]);
@@ -328,8 +362,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillAr
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{u0, u1, v0, v1});
 #pragma unroll
       for (int d = 0; d < kDH / 32; ++d)
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lds_operand_tr32(tl.v, 16 * ks, 32 * d, lane), pb,
-                                                          oacc[d], 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vcur[d], pb, oacc[d], 0, 0, 0);
     }
   };
 
@@ -389,7 +422,7 @@ int launch_prefill(PrefillArgs a, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(decompress_kernel, dim3((M + kGT - 1) / kGT, 2 * a.H), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.c_kv), wcat, kv, M, a.H);
   a.kv = kv;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3((a.S + kQB - 1) / kQB, a.H, a.B), dim3(kAttnThreads), 0, s, a);
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3(a.H, (a.S + kQB - 1) / kQB, a.B), dim3(kAttnThreads), 0, s, a);
   return int(hipGetLastError());
 }
 
