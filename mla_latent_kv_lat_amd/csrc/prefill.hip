@@ -107,6 +107,9 @@ __global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restr
   for (int st = 0; st < kStages; ++st) {
     const int buf = st & 1;
     if (st + 1 < kStages) load((st + 1) * kGK);
+    // Keep the next stage's loads here, ahead of this stage's products (the scheduler would
+    // otherwise sink them next to the stores that consume them and expose their latency).
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < kGK / 16; ++ks) {
       const int ch = 2 * ks + hh;
@@ -282,8 +285,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillAr
       if (i + kPre < kSteps) ring[i % kPre] = operand(i + kPre);
       sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, qb[i >> 1], sacc[i & 1], 0, 0, 0);
     }
-    // Scale to base 2 (masking only where the tile reaches past the wave's first query),
-    // and the tile max of this query's 64 keys (half of them in the partner lane).
+    // The tile max of this query's 64 keys (half of them in the partner lane), masking only
+    // where the tile reaches past the wave's first query; raw scores, scaled to base 2
+    // afterwards (the scale is positive, so it commutes with the max) and inside the
+    // exponent's fused multiply-add.
     float tmax = -INFINITY;
     if (t0 + kKT - 1 > pos_first_w) {
 #pragma unroll
@@ -291,22 +296,19 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillAr
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int t = t0 + 32 * kb + 8 * (e >> 2) + 4 * hh + (e & 3);
-          sacc[kb][e] = t <= pos ? sacc[kb][e] * a.scale_log2 : -INFINITY;
+          if (t > pos) sacc[kb][e] = -INFINITY;
           tmax = fmaxf(tmax, sacc[kb][e]);
         }
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          sacc[kb][e] *= a.scale_log2;
-          tmax = fmaxf(tmax, sacc[kb][e]);
-        }
+        for (int e = 0; e < 16; ++e) tmax = fmaxf(tmax, sacc[kb][e]);
     }
     {
       float x0 = tmax, x1 = tmax;
       permlane32_swap(x0, x1);
-      tmax = fmaxf(x0, x1);
+      tmax = fmaxf(x0, x1) * a.scale_log2;
     }
     // Move the reference only when the tile exceeds it by more than kTau.
     const bool grow = tmax > m_ref + kTau;  // false while nothing is visible
@@ -318,7 +320,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void prefill_attn_kernel(PrefillAr
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sacc[kb][e] + neg_m);
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][e], a.scale_log2, neg_m));
         sacc[kb][e] = p;
         psum += p;
       }
