@@ -24,6 +24,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));  // 32 fp8 codes: one f8f6f
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -120,9 +121,10 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   return r;
 }
 
+// Two floats -> two bf16 (a in the low half), round to nearest even: one packed conversion
+// (two scalar conversions plus a shift and an or when written element by element).
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(a))) |
-         (uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(b))) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
 // Cross-lane swaps of gfx950, written as single inline instructions (register operands
