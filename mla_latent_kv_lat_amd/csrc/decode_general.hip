@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void decode_general_kernel(DecodeArgs a, 
 // row, 8 consecutive columns per lane; the splits are read in batches whose loads are all
 // in flight together, merged with a running maximum so no separate max pass is needed.
 constexpr int kCombRows = 4;   // query rows (one per wave) per workgroup
-constexpr int kCombBatch = 8;  // splits per batch
+constexpr int kCombBatch = 8;  // splits per batch (4 when a row has at most 4 pieces)
 
 template <bool VEC>
 __device__ __forceinline__ void load8_f32(float (&v)[8], const float* p, int c, int dc) {
@@ -224,7 +224,7 @@ __device__ __forceinline__ void load8_f32(float (&v)[8], const uint16_t* p, int 
 // Weighted merge of np pieces of one row: piece j has base-2 log-sum-exp lse_of(j) (-inf:
 // no weight) and its dc normalised values at part_of(j).  Writes the row of o and, if
 // lse_out is set, its natural-log lse.
-template <typename OS, typename PS, bool VEC, typename LseF, typename PartF>
+template <typename OS, typename PS, bool VEC, int NB = kCombBatch, typename LseF, typename PartF>
 __device__ __forceinline__ void merge_row(const DecodeArgs& a, int np, LseF lse_of, PartF part_of,
                                           typename OS::raw* o, float* lse_out, int lane) {
   using PR = typename PS::raw;
@@ -232,10 +232,10 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int np, LseF lse_
     const int c = c0 + 8 * lane;
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float M = -INFINITY, tot = 0.f;
-    for (int s0 = 0; s0 < np; s0 += kCombBatch) {
-      float ls[kCombBatch], v[kCombBatch][8];
+    for (int s0 = 0; s0 < np; s0 += NB) {
+      float ls[NB], v[NB][8];
 #pragma unroll
-      for (int j = 0; j < kCombBatch; ++j) {
+      for (int j = 0; j < NB; ++j) {
         const int sj = min(s0 + j, np - 1);  // in range; surplus entries get weight 0
         const float lj = lse_of(sj);
         ls[j] = s0 + j < np ? lj : -INFINITY;
@@ -247,7 +247,7 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int np, LseF lse_
       }
       float bm = ls[0];
 #pragma unroll
-      for (int j = 1; j < kCombBatch; ++j) bm = fmaxf(bm, ls[j]);
+      for (int j = 1; j < NB; ++j) bm = fmaxf(bm, ls[j]);
       const float Mn = fmaxf(M, bm);
       if (Mn == -INFINITY) continue;  // nothing visible yet (uniform over the wave)
       const float r = exp2f(M - Mn);  // 0 while M is still -inf
@@ -255,7 +255,7 @@ __device__ __forceinline__ void merge_row(const DecodeArgs& a, int np, LseF lse_
 #pragma unroll
       for (int k = 0; k < 8; ++k) acc[k] *= r;
 #pragma unroll
-      for (int j = 0; j < kCombBatch; ++j) {
+      for (int j = 0; j < NB; ++j) {
         const float w = exp2f(ls[j] - Mn);
         tot += w;
 #pragma unroll
@@ -322,8 +322,16 @@ __global__ __launch_bounds__(256) void combine_ranges_kernel(DecodeArgs a, int R
     if (lane == 0 && lse_out) *lse_out = -INFINITY;
     return;
   }
-  auto range_lo = [&](int64_t w) { return total * w / R; };
-  auto range_of = [&](int64_t x) { return int(((x + 1) * R + total - 1) / total - 1); };  // holds tile x
+  // Range arithmetic in 32 bits whenever every intermediate fits: total R and
+  // (x + 1) R + total - 1 <= total (R + 1) (64-bit division is long).
+  const bool small = total * (R + 1) < (int64_t(1) << 32);
+  auto range_lo = [&](int64_t w) {
+    return small ? int64_t(uint32_t(total) * uint32_t(w) / uint32_t(R)) : total * w / R;
+  };
+  auto range_of = [&](int64_t x) {  // holds tile x
+    return small ? int((uint32_t(x + 1) * uint32_t(R) + uint32_t(total) - 1u) / uint32_t(total)) - 1
+                 : int(((x + 1) * R + total - 1) / total - 1);
+  };
   const int w0 = range_of(p0), w1 = range_of(p1 - 1);
   if (w0 == w1) return;
   const int64_t slot0 = int64_t(w0) * 2 + (range_lo(w0) == p0 ? 0 : 1);
@@ -333,10 +341,13 @@ __global__ __launch_bounds__(256) void combine_ranges_kernel(DecodeArgs a, int R
   auto has_piece = [&](int j) { return j == 0 || dense || range_lo(w0 + j) < range_lo(w0 + j + 1); };
   auto slot_of = [&](int j) { return j == 0 || !has_piece(j) ? slot0 : int64_t(w0 + j) * 2; };
   const uint16_t* po = static_cast<const uint16_t*>(a.part_o) + int64_t(row) * a.dc;
-  merge_row<BF16, BF16, true>(
-      a, w1 - w0 + 1,
-      [&](int j) { return has_piece(j) ? a.part_lse[slot_of(j) * rows + row] : -INFINITY; },
-      [&](int j) { return po + slot_of(j) * rows * a.dc; }, o, lse_out, lane);
+  auto lse_of = [&](int j) { return has_piece(j) ? a.part_lse[slot_of(j) * rows + row] : -INFINITY; };
+  auto part_of = [&](int j) { return po + slot_of(j) * rows * a.dc; };
+  const int np = w1 - w0 + 1;
+  if (np <= 4)
+    merge_row<BF16, BF16, true, 4>(a, np, lse_of, part_of, o, lse_out, lane);
+  else
+    merge_row<BF16, BF16, true>(a, np, lse_of, part_of, o, lse_out, lane);
 }
 
 // Exclusive prefix sum over the batch of each sequence's 32-token tile count (lengths
