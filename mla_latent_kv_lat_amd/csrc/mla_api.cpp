@@ -328,8 +328,10 @@ static mla_status check_prefill(const mla_dims* d, int32_t T, mla_dtype dt) {
   if (!valid_dtype(dt)) return MLA_ERR_INVALID_ARG;
   if (dt != MLA_BF16 || d->d_head != 128 || d->d_latent != 512 || d->d_rope != 64 || d->fp8_scores)
     return MLA_ERR_UNSUPPORTED;
+  // Grid limits: the decompression has 2 n_h column tiles, the attention ceil(s_q / 256)
+  // query blocks and B sequences in dimensions of at most 65535 workgroups.
   if (d->batch > kMaxGridDim || 2 * int64_t(d->n_heads) > kMaxGridDim ||
-      int64_t(d->batch) * T > INT32_MAX)
+      (int64_t(d->q_len) + 255) / 256 > kMaxGridDim || int64_t(d->batch) * T > INT32_MAX)
     return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }

@@ -316,6 +316,9 @@ def test_prefill_workspace_and_argument_errors():
     assert call(dims=v2(d_rope=32)) == U
     assert call(dims=v2(fp8_scores=1)) == U
     assert call(dims=v2(n_heads=40000)) == U      # 2 n_h column tiles exceed a grid dimension
+    # 65536 query blocks of 256 exceed a grid dimension (65535 blocks still fit)
+    assert call(dims=v2(batch=1, q_len=65536 * 256, n_heads=1), T=65536 * 256) == U
+    assert call(dims=v2(batch=1, q_len=65535 * 256, n_heads=1), T=65535 * 256, ws=None) == W
     for k in ("q_nope", "q_rope", "c_kv", "k_rope", "w_uk", "w_uv", "out"):
         assert call(**{k: None}) == E, k
         assert call(**{k: A + 8}) == E, k         # not 16-byte aligned
