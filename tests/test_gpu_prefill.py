@@ -118,3 +118,47 @@ def test_prefill_all_heads_sampled():
     rows = sorted({(0, int(i), int(h)) for i, h in zip(rng.integers(0, 512, 200), rng.integers(0, 128, 200))}
                   | {(0, 0, 0), (0, 511, 127), (0, 127, 5), (0, 128, 5)})
     check(cfg, [512], rows=rows)
+
+
+def test_prefill_bench_size_sampled():
+    """The size the prefill bench times (one 4096-token prompt, every token a query, 128
+    heads): a seeded sample of (query, head) outputs and log-sum-exps, edges included, and
+    the decompressed keys and values of three heads over every row (the full oracle would
+    take minutes)."""
+    T, H = 4096, 128
+    cfg = prefill_cfg(batch=1, q_len=T, seq_len=T, n_heads=H)
+    say("prefill bench size, sampled", T, H)
+    inp = synth.make_inputs(cfg, 5, lengths=np.array([T], np.int32))
+    dev = lambda a, k="bf16": to_device(a, k, "cuda")
+    d = capi.dims_from_config(cfg)
+    ws = torch.empty(capi.mla_prefill_workspace_bytes(d, T), dtype=torch.uint8, device="cuda")
+    out = torch.empty(1, T, H, cfg.d_head, dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(1, T, H, dtype=torch.float32, device="cuda")
+    capi.mla_prefill(d, dev(inp.q_nope), dev(inp.q_rope), dev(inp.c_kv), dev(inp.k_rope), T,
+                     dev(inp.seq_lens, "i32"), dev(inp.w_uk), dev(inp.w_uv), out, lse, ws)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = sorted({(0, int(i), int(h)) for i, h in zip(rng.integers(0, T, 96), rng.integers(0, H, 96))}
+                  | {(0, 0, 0), (0, T - 1, H - 1), (0, 255, 64), (0, 256, 64), (0, 63, 1), (0, 64, 1)})
+    ii = torch.tensor([r[1] for r in rows], device="cuda")
+    hh = torch.tensor([r[2] for r in rows], device="cuda")
+    got_o = to_host_f64(out[0, ii, hh])
+    got_l = to_host_f64(lse[0, ii, hh])
+    dd = decoded(inp)
+    ref_o, ref_l = O.mla_explicit(dd["q_nope"], dd["q_rope"], dd["c_kv"], dd["k_rope"], dd["w_uk"], dd["w_uv"],
+                                  inp.seq_lens, cfg.softmax_scale, rows=rows)
+    ref_o = np.stack([ref_o[r] for r in rows])
+    ref_l = np.array([ref_l[r] for r in rows])
+    e_o, e_l = max_rel_err(got_o, ref_o), max_rel_err(got_l, ref_l)
+    # decompressed key and value of three heads, every row (workspace: weights, then kv)
+    wbytes = (H * 256 * 512 * 2 + 255) // 256 * 256
+    kv = ws[wbytes:wbytes + T * H * 256 * 2].view(torch.bfloat16).view(T, H, 256)
+    uk, uv = O.to_page_layout(dd["w_uk"], dd["w_uv"])
+    e_kv = 0.0
+    for h in (0, 77, H - 1):
+        cols = slice(h * cfg.d_head, (h + 1) * cfg.d_head)
+        got = to_host_f64(kv[:, h])
+        e_kv = max(e_kv, max_rel_err(got[:, :cfg.d_head], dd["c_kv"][0] @ uk[:, cols]),
+                   max_rel_err(got[:, cfg.d_head:], dd["c_kv"][0] @ uv[:, cols]))
+    print(f"  {len(rows)} rows: out {e_o:.2e}  lse {e_l:.2e}  kv (3 heads) {e_kv:.2e}", flush=True)
+    assert e_o <= TOL and e_l <= TOL and e_kv <= TOL
