@@ -11,8 +11,8 @@
 //   * prefill_weights_kernel: wcat[h] = [W_UK[h] ; W_UV[h]^T] as 256 rows of d_c, so that
 //     both halves of the decompression read their weights as rows;
 //   * decompress_kernel: kv[m, h, 0:128] = c_kv[m] . W_UK[h]^T (the head's key),
-//     kv[m, h, 128:256] = c_kv[m] . W_UV[h] (its value), a 128 x 128-tiled matrix product
-//     over all B * T cache rows;
+//     kv[m, h, 128:256] = c_kv[m] . W_UV[h] (its value), a matrix product over all B * T
+//     cache rows in tiles of 256 rows by one head;
 //   * prefill_attn_kernel: 256 queries of one (sequence, head) per workgroup, 64-key tiles,
 //     scores as S^T = K Q^T and outputs as O^T += V^T P^T on the 32 x 32 x 16 bf16 matrix
 //     instruction, online softmax in base 2 per query lane.
@@ -51,34 +51,36 @@ __global__ __launch_bounds__(256) void prefill_weights_kernel(const uint16_t* __
 }
 
 // ---------------------------------------------------------------------------------------
-// kv[m, h, n0 + n] = sum_c x[m, c] * wcat[h][n0 + n][c] for a 128 (m) x 128 (n) tile.
-// Four waves, each a 64 x 64 block formed as D^T[n][m] (weights as the A operand, cache
-// rows as the B operand), in K steps of 64 staged through LDS (double buffered).  LDS
+// kv[m, h, n] = sum_c x[m, c] * wcat[h][n][c] for a tile of 256 cache rows (m) and one
+// head's 256 columns (n: key then value).  Eight waves, each a 64 (n) x 128 (m) block formed
+// as D^T[n][m] (weights as the A operand, cache rows as the B operand: 6 operand reads per 8
+// products), in K steps of 64 staged through LDS (double buffered, 64 KB per step).  LDS
 // rows are 128 bytes (8 chunks of 16 bytes); chunk c of row r sits at c ^ ((r >> 1) & 7),
 // so the 16 rows of one operand read hit distinct banks.
-constexpr int kGT = 128;   // tile edge
+constexpr int kGM = 256;   // cache rows per tile
+constexpr int kGN = kNcat; // columns per tile: one head
 constexpr int kGK = 64;    // K per stage
+constexpr int kGThreads = 512;
 
 __device__ __forceinline__ int gswz(int r) { return (r >> 1) & 7; }
 
-__global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restrict__ x,
-                                                         const uint16_t* __restrict__ wcat,
-                                                         uint16_t* __restrict__ kv, int M, int H) {
-  __shared__ __attribute__((aligned(16))) uint16_t sm[2][2][kGT * kGK];  // [buf][A = w, B = x]
+__global__ __launch_bounds__(kGThreads, 1) void decompress_kernel(const uint16_t* __restrict__ x,
+                                                                  const uint16_t* __restrict__ wcat,
+                                                                  uint16_t* __restrict__ kv, int M, int H) {
+  __shared__ __attribute__((aligned(16))) uint16_t sm[2][2][kGN * kGK];  // [buf][A = w, B = x]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int h = blockIdx.y >> 1, nt = blockIdx.y & 1;
-  const int m0 = blockIdx.x * kGT, n0 = nt * kGT;
-  const int wn = wv >> 1, wm = wv & 1;  // this wave's 64 x 64 block: n 64 wn.., m 64 wm..
+  const int m0 = blockIdx.x * kGM, h = blockIdx.y;
+  const int wn = wv & 3, wm = wv >> 2;  // this wave's block: n 64 wn.., m 128 wm..
   const int n32 = lane & 31, hh = lane >> 5;
 
-  // Global -> register loads of one stage: 128 rows x 8 chunks of each operand, 4 chunks
-  // per thread per operand.
-  const uint16_t* wrow = wcat + (int64_t(h) * kNcat + n0) * kDC;
+  // Global -> register loads of one stage: 256 rows x 8 chunks of each operand, 4 chunks per
+  // thread per operand.
+  const uint16_t* wrow = wcat + int64_t(h) * kNcat * kDC;
   u32x4 ra[4], rb[4];
   auto load = [&](int k0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, r = idx >> 3, ch = idx & 7;
+      const int idx = tid + kGThreads * i, r = idx >> 3, ch = idx & 7;
       ra[i] = ld16(wrow + int64_t(r) * kDC + k0 + 8 * ch);
       rb[i] = ld16(x + int64_t(min(m0 + r, M - 1)) * kDC + k0 + 8 * ch);
     }
@@ -86,17 +88,17 @@ __global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restr
   auto store = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int idx = tid + 256 * i, r = idx >> 3, ch = idx & 7;
+      const int idx = tid + kGThreads * i, r = idx >> 3, ch = idx & 7;
       *reinterpret_cast<u32x4*>(&sm[buf][0][r * kGK + 8 * (ch ^ gswz(r))]) = ra[i];
       *reinterpret_cast<u32x4*>(&sm[buf][1][r * kGK + 8 * (ch ^ gswz(r))]) = rb[i];
     }
   };
 
-  f32x16 acc[2][2];  // [n block][m block]
+  f32x16 acc[2][4];  // [n block][m block]
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[a][b][e] = 0.f;
 
@@ -113,17 +115,21 @@ __global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restr
 #pragma unroll
     for (int ks = 0; ks < kGK / 16; ++ks) {
       const int ch = 2 * ks + hh;
-      bf16x8 av[2], bv[2];
+      bf16x8 av[2], bv[4];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int rn = 64 * wn + 32 * j + n32, rm = 64 * wm + 32 * j + n32;
+        const int rn = 64 * wn + 32 * j + n32;
         av[j] = *reinterpret_cast<const bf16x8*>(&sm[buf][0][rn * kGK + 8 * (ch ^ gswz(rn))]);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rm = 128 * wm + 32 * j + n32;
         bv[j] = *reinterpret_cast<const bf16x8*>(&sm[buf][1][rm * kGK + 8 * (ch ^ gswz(rm))]);
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < 4; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[a], bv[b], acc[a][b], 0, 0, 0);
     }
     if (st + 1 < kStages) {
       store(buf ^ 1);
@@ -131,28 +137,29 @@ __global__ __launch_bounds__(256) void decompress_kernel(const uint16_t* __restr
     }
   }
   __syncthreads();  // every wave done with the operand buffers
-  // Stage the bf16 tile as [m][n] (reusing the operand buffers), then store whole rows.
-  uint16_t* ot = &sm[0][0][0];  // 128 x 128 bf16 = 32 KB
+  // Stage the bf16 tile as [m][n] (reusing the operand buffers: 256 x 256 bf16 = 128 KB),
+  // then store whole 512-byte rows.  Chunk c of row m sits at c ^ (m & 31).
+  uint16_t* ot = &sm[0][0][0];
 #pragma unroll
   for (int a = 0; a < 2; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int m = 64 * wm + 32 * b + n32;
+    for (int b = 0; b < 4; ++b) {
+      const int m = 128 * wm + 32 * b + n32;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int n = 64 * wn + 32 * a + 8 * i + 4 * hh;  // 4 consecutive n
         const uint32_t w0 = pack_bf16x2(acc[a][b][4 * i], acc[a][b][4 * i + 1]);
         const uint32_t w1 = pack_bf16x2(acc[a][b][4 * i + 2], acc[a][b][4 * i + 3]);
-        *reinterpret_cast<u32x2*>(&ot[m * kGT + 8 * ((n >> 3) ^ (m & 15)) + (n & 7)]) = u32x2{w0, w1};
+        *reinterpret_cast<u32x2*>(&ot[m * kGN + 8 * ((n >> 3) ^ (m & 31)) + (n & 7)]) = u32x2{w0, w1};
       }
     }
   __syncthreads();
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int idx = tid + 256 * i, m = idx >> 4, ch = idx & 15;
+  for (int i = 0; i < kGM * kGN / 8 / kGThreads; ++i) {
+    const int idx = tid + kGThreads * i, m = idx >> 5, ch = idx & 31;
     if (m0 + m < M)
-      *reinterpret_cast<u32x4*>(kv + (int64_t(m0 + m) * H + h) * kNcat + n0 + 8 * ch) =
-          *reinterpret_cast<const u32x4*>(&ot[m * kGT + 8 * (ch ^ (m & 15))]);
+      *reinterpret_cast<u32x4*>(kv + (int64_t(m0 + m) * H + h) * kNcat + 8 * ch) =
+          *reinterpret_cast<const u32x4*>(&ot[m * kGN + 8 * (ch ^ (m & 31))]);
   }
 }
 
@@ -421,7 +428,7 @@ int launch_prefill(PrefillArgs a, void* ws, hipStream_t s) {
   hipLaunchKernelGGL(prefill_weights_kernel, dim3(a.H, kNcat / 32), dim3(256), 0, s,
                      static_cast<const uint16_t*>(a.w_uk), static_cast<const uint16_t*>(a.w_uv), wcat);
   const int M = a.B * a.T;
-  hipLaunchKernelGGL(decompress_kernel, dim3((M + kGT - 1) / kGT, 2 * a.H), dim3(256), 0, s,
+  hipLaunchKernelGGL(decompress_kernel, dim3((M + kGM - 1) / kGM, a.H), dim3(kGThreads), 0, s,
                      static_cast<const uint16_t*>(a.c_kv), wcat, kv, M, a.H);
   a.kv = kv;
   hipLaunchKernelGGL(prefill_attn_kernel, dim3(a.H, (a.S + kQB - 1) / kQB, a.B), dim3(kAttnThreads), 0, s, a);
