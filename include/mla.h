@@ -31,6 +31,8 @@
  *     allocates or frees device memory, and never synchronises: each call validates
  *     its arguments on the host, enqueues its kernels on `stream` (a hipStream_t passed
  *     as void*, NULL = the null stream) and returns.  Outputs must not alias inputs.
+ *     The calls enqueue kernels only (no memset or copy), so a sequence of them can be
+ *     captured into a HIP graph and replayed with the same buffers.
  *   - Errors: a status is returned; nothing is thrown or aborted across the ABI.  On any
  *     status other than MLA_OK nothing was enqueued, except MLA_ERR_HIP (a launch
  *     failed; mla_last_hip_error() gives the hipError_t of the calling thread).
