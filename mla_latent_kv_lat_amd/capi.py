@@ -118,10 +118,18 @@ def library() -> ctypes.CDLL:
 
 
 def _ptr(x):
+    """Device address of a tensor argument (or a raw integer address, passed through).
+    Tensors must be dense and on the GPU: the library reads them as contiguous row-major
+    arrays at that address, so a strided view or a host tensor would be misread."""
     if x is None:
         return None
     if isinstance(x, int):
         return _vp(x)
+    if not x.is_cuda:
+        raise ValueError(f"libmla needs device tensors, got one on {x.device}")
+    if not x.is_contiguous():
+        raise ValueError(f"libmla needs contiguous tensors, got strides {tuple(x.stride())} "
+                         f"for shape {tuple(x.shape)}")
     return _vp(x.data_ptr())
 
 

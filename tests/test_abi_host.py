@@ -348,3 +348,15 @@ def test_linear_workspace_and_argument_errors():
         assert call(**{k: A + 8}) == E, k
     need = L.mla_linear_workspace_bytes(32, 512, 128)
     assert call(ws=None) == W and call(ws_bytes=need - 1) == W and call(ws=A + 4, ws_bytes=need) == W
+
+
+def test_binding_rejects_host_tensors():
+    # The binding passes tensor addresses to the device code: host tensors are refused
+    # before any call into the library.
+    import torch
+    d = v2()
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="device tensors"):
+        L.mla_absorb_q(d, x, A, A, dtype="bf16")
+    with pytest.raises(ValueError, match="device tensors"):
+        L.mla_linear(A, x, A, A, M=32, K=256, N=64, workspace_bytes=1 << 20, dtype="bf16")

@@ -364,3 +364,19 @@ def test_full_size_sampled_fp8_scores():
     check_all(res, oracle_full(decoded_batches(inp, batches)), TOL_FP8_PREQUANT, batches=batches,
               what=cfg.name + " fp8 scores")
     del w
+
+
+def test_binding_rejects_strided_views():
+    """A transposed or sliced view would be read as a dense array at its address; the
+    binding refuses it (a dense copy is accepted)."""
+    say("binding strided view")
+    cfg = configs.V2_DECODE.with_(batch=2, seq_len=64, cfg_id=34)
+    d = capi.dims_from_config(cfg)
+    q = torch.zeros(2, 1, 128, 256, dtype=torch.bfloat16, device="cuda")[..., :128]
+    w_uk = torch.zeros(128, 128, 512, dtype=torch.bfloat16, device="cuda")
+    q_lat = torch.empty(2, 1, 128, 512, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="contiguous"):
+        capi.mla_absorb_q(d, q, w_uk, q_lat)
+    capi.mla_absorb_q(d, q.contiguous(), w_uk, q_lat)
+    torch.cuda.synchronize()
+    assert int(q_lat.count_nonzero()) == 0
