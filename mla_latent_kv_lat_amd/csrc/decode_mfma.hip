@@ -29,8 +29,10 @@
 // The three stages are pipelined over the tiles with one barrier per step: in step n the
 // score waves stage and score tile n + 1, every wave runs the softmax of tile n, and the
 // output waves multiply tile n - 1 (whose V^T operands they read from LDS in step n - 1)
-// and read the operands of tile n.  Slices, partial scores and probabilities are double
-// buffered in LDS.  The cache is read from HBM once per workgroup.
+// and read the operands of tile n.  A score wave runs its softmax while the matrix unit
+// finishes its score products (issued first), and only then stores the partial scores and
+// refills its registers.  Slices, partial scores and probabilities are double buffered in
+// LDS.  The cache is read from HBM once per workgroup.
 //
 // Softmax runs in base-2 units (scores times softmax_scale * log2(e), exponentials by the
 // hardware base-2 exponential; results that would be denormal flush to 0) against a per-row
@@ -372,10 +374,10 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
     u32x4 av[8];  // latent score operands of the tile being scored
     bf16x8 ar;    // RoPE score operand
     // Stage tile n: write this wave's latent slice to v[n % 2] as bf16 (the output waves'
-    // V) and set the score operands.  bf16: refill the registers with tile n + 2 at once and
-    // read the slice back in operand layout (LDS operations of one wave complete in order,
-    // so no barrier is needed).  fp8: convert the codes, which are already the operands;
-    // the registers are refilled after the score product.
+    // V) and set the score operands.  bf16: read the slice back in operand layout (LDS
+    // operations of one wave complete in order, so no barrier is needed).  fp8: convert the
+    // codes, which are already the operands.  Either way the registers are refilled with
+    // tile n + 2 after the score product and the softmax (they are free meanwhile).
     auto stage = [&](TileRegs<FP8>& tr, int n) {
       const int buf = n & 1;
       uint16_t* vs = &sm.v[buf][c.w][0][0];
@@ -398,24 +400,29 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
           *reinterpret_cast<u32x4*>(vs + tok * kCols + 8 * ((c.lane & 15) ^ swz32(tok))) = tr.lat[k];
         }
         ar = __builtin_bit_cast(bf16x8, tr.rope);
-        load_tile<FP8, PK>(tr, c, a, t_lo + (n + 2) * kTile);
 #pragma unroll
         for (int s = 0; s < 8; ++s)
           av[s] = *reinterpret_cast<const u32x4*>(vs + c.n * kCols + 8 * ((kcol(s, c.h) >> 3) ^ swz32(c.n)));
       }
     };
-    // fp8: refill the registers of tile n with tile n + 2 once its score operands are used.
-    auto refill_after_score = [&](TileRegs<FP8>& tr, int n) {
-      if constexpr (FP8) load_tile<FP8, PK>(tr, c, a, t_lo + (n + 2) * kTile);
-    };
-    // Partial scores of the staged tile n into spart[n % 2].
-    auto score = [&](const TileRegs<FP8>& tr, int n) {
+    // Refill the registers of tile n with tile n + 2.
+    auto refill_after_score = [&](TileRegs<FP8>& tr, int n) { load_tile<FP8, PK>(tr, c, a, t_lo + (n + 2) * kTile); };
+    // Partial scores of the staged tile n into spart[n % 2]; `mid` runs once the latent
+    // products are issued (the previous tile's softmax in the steady state).
+    auto score = [&](const TileRegs<FP8>& tr, int n, auto mid) {
       const int buf = n & 1;
       f32x16 sacc[2];
 #pragma unroll
       for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) sacc[rb2][e] = 0.f;
+      if constexpr (!FP8) {
+        // RoPE term first: the wave can leave the products' last instruction and run `mid`
+        // (the previous tile's softmax) while the matrix unit finishes.
+#pragma unroll
+        for (int rb2 = 0; rb2 < 2; ++rb2)
+          sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qrb[rb2], sacc[rb2], 0, 0, 0);
+      }
       if constexpr (QK8) {
         // Codes times codes, 64 columns per instruction (unit block scales).
 #pragma unroll
@@ -435,6 +442,7 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
             sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av[s]), qb[rb2][s],
                                                                 sacc[rb2], 0, 0, 0);
       }
+      mid();
       if constexpr (FP8) {
         // Scale the latent part of tokens 8i + 4h + r by their per-token scales (and, for
         // the fp8 product, row n's query scale).
@@ -447,9 +455,11 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
             for (int r = 0; r < 4; ++r) sacc[rb2][4 * i + r] *= QK8 ? tsv[r] * qs[rb2] : tsv[r];
         }
       }
+      if constexpr (FP8) {
 #pragma unroll
-      for (int rb2 = 0; rb2 < 2; ++rb2)
-        sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qrb[rb2], sacc[rb2], 0, 0, 0);
+        for (int rb2 = 0; rb2 < 2; ++rb2)
+          sacc[rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar, qrb[rb2], sacc[rb2], 0, 0, 0);
+      }
 #pragma unroll
       for (int rb2 = 0; rb2 < 2; ++rb2) {
         const int row = 32 * rb2 + c.n;
@@ -462,9 +472,8 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
     // Step n (n + 1 < ntiles): stage and score tile n + 1, softmax of tile n.
     auto step = [&](TileRegs<FP8>& tr, int n) {
       stage(tr, n + 1);
-      score(tr, n + 1);
+      score(tr, n + 1, [&] { softmax_tile<FP8>(sm, st, n & 1, t_lo + n * kTile, a.scale_log2); });
       refill_after_score(tr, n + 1);
-      softmax_tile<FP8>(sm, st, n & 1, t_lo + n * kTile, a.scale_log2);
       __syncthreads();
     };
 
@@ -474,7 +483,7 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
       load_tile<FP8, PK>(ra, c, a, t_lo);
       load_tile<FP8, PK>(rb2, c, a, t_lo + kTile);
       stage(ra, 0);
-      score(ra, 0);
+      score(ra, 0, [] {});
       refill_after_score(ra, 0);
       __syncthreads();
       // Straight-line pairs: every path into the loop header has the same loads in flight.
