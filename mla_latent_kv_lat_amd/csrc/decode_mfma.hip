@@ -32,7 +32,9 @@
 // and read the operands of tile n.  A score wave runs its softmax while the matrix unit
 // finishes its score products (issued first), and only then stores the partial scores and
 // refills its registers.  Slices, partial scores and probabilities are double buffered in
-// LDS.  The cache is read from HBM once per workgroup.
+// LDS.  The cache is read from HBM once per workgroup.  At the end the output waves park
+// the normalised rows in LDS and all eight waves write them out as whole 1 KB rows (the
+// accumulator layout would scatter 8-byte pieces over 32 rows per store instruction).
 //
 // Softmax runs in base-2 units (scores times softmax_scale * log2(e), exponentials by the
 // hardware base-2 exponential; results that would be denormal flush to 0) against a per-row
@@ -566,28 +568,40 @@ __device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int 
     finish_rows(st);
     __syncthreads();  // every row sum published
 
+    // Normalised rows into LDS (the partial-score buffers are free now): row r's 16-byte
+    // chunk c is stored at chunk c ^ (r & 15), so both the 8-byte writes (16 rows per LDS
+    // cycle) and the row reads below are conflict-free.
+    uint16_t* os = reinterpret_cast<uint16_t*>(&sm.spart[0][0][0][0]);
 #pragma unroll
     for (int rb2 = 0; rb2 < 2; ++rb2) {
       const float lt = sm.lsum[32 * rb2 + c.n];
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int row = r0 + 32 * rb2 + c.n;
+      const int lrow = 32 * rb2 + c.n;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int col = kCols * q + 32 * cb + 8 * i + 4 * c.h;
+          const int chunk = 16 * q + 4 * cb + i;
           const f32x4 v = f32x4{oacc[cb][rb2][4 * i], oacc[cb][rb2][4 * i + 1], oacc[cb][rb2][4 * i + 2],
                                 oacc[cb][rb2][4 * i + 3]} * inv;
-          if (single) {
-            uint16_t* o = static_cast<uint16_t*>(a.o_lat) + (out_base + row) * kDC + col;
-            *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          } else {
-            uint16_t* o = static_cast<uint16_t*>(a.part_o) + (out_base + row) * kDC + col;
-            *reinterpret_cast<u32x2*>(o) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          }
+          *reinterpret_cast<u32x2*>(os + lrow * kDC + 8 * (chunk ^ (lrow & 15)) + 4 * c.h) =
+              u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
     }
   }
+  __syncthreads();
+  // Every wave writes 8 whole rows (1 KB each, 16 bytes per lane).
+  {
+    const uint16_t* os = reinterpret_cast<const uint16_t*>(&sm.spart[0][0][0][0]);
+    uint16_t* dst = static_cast<uint16_t*>(single ? a.o_lat : a.part_o);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int lrow = 8 * c.w + k;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(os + lrow * kDC + 8 * (c.lane ^ (lrow & 15)));
+      *reinterpret_cast<u32x4*>(dst + (out_base + r0 + lrow) * kDC + 8 * c.lane) = v;
+    }
+  }
+  __syncthreads();  // the next piece stages into these buffers
 }
 
 // Grid: one workgroup per (row block, work unit), handed out XCD-aware.  Static splits:
@@ -622,31 +636,51 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
     return;
   }
 
-  // Tile prefix of the batch: computed here for small batches (every workgroup, in LDS;
-  // unit 0 also stores it for the combine), else read from the prefix kernel's output.
-  if (a.prefix_here) {
+  // Tile prefix of the batch, computed here for small batches (unit 0 also stores it for the
+  // combine), else read from the prefix kernel's output.  Up to 64 sequences every wave
+  // scans the tile counts itself, one lane per sequence (32-bit sums: at most 64 * 2^20
+  // tiles), and finds its first sequence with a ballot: no LDS, no barrier, one load
+  // latency.  Larger batches are scanned by the workgroup in LDS.
+  const bool wave_pfx = a.prefix_here && a.B >= 1 && a.B <= 64 && a.T <= (int64_t(1) << 25);
+  int incl = 0;  // wave_pfx: inclusive tile prefix of sequence `lane`
+  if (wave_pfx) {
+    const int lane = threadIdx.x & 63;
+    const int tl = lane < a.B ? (seq_len(lane) + kTile - 1) / kTile : 0;
+    incl = tl;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += v;
+    }
+    if (unit == 0 && threadIdx.x < 64) {
+      int64_t* pg = const_cast<int64_t*>(a.prefix);
+      if (lane < a.B) pg[lane] = incl - tl;
+      if (lane == a.B - 1) pg[a.B] = incl;
+    }
+  } else if (a.prefix_here) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     auto tiles = [&](int i) { return i < a.B ? int64_t((seq_len(i) + kTile - 1) / kTile) : int64_t(0); };
     const int64_t t0 = tiles(2 * tid), t1 = tiles(2 * tid + 1);
-    int64_t incl = t0 + t1;
+    int64_t incl2 = t0 + t1;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-      const int64_t v = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += v;
+      const int64_t v = __shfl_up(incl2, off, 64);
+      if (lane >= off) incl2 += v;
     }
-    if (lane == 63) sm.wave_tot[wave] = incl;
+    if (lane == 63) sm.wave_tot[wave] = incl2;
     __syncthreads();
-    for (int k = 0; k < wave; ++k) incl += sm.wave_tot[k];
-    const int64_t excl = incl - t0 - t1;
+    for (int k = 0; k < wave; ++k) incl2 += sm.wave_tot[k];
+    const int64_t excl = incl2 - t0 - t1;
     if (2 * tid < a.B) sm.prefix[2 * tid] = excl;
     if (2 * tid + 1 < a.B) sm.prefix[2 * tid + 1] = excl + t0;
-    if (tid == kThreads - 1) sm.prefix[a.B] = incl;  // 2 kThreads >= B: the total
+    if (tid == kThreads - 1) sm.prefix[a.B] = incl2;  // 2 kThreads >= B: the total
     __syncthreads();
     if (unit == 0)
       for (int i = tid; i <= a.B; i += kThreads) const_cast<int64_t*>(a.prefix)[i] = sm.prefix[i];
   }
   // Prefix entries are the same for every lane: keep them in scalar registers.
-  auto pre = [&](int i) {
+  auto pre = [&](int i) -> int64_t {
+    if (wave_pfx) return i == 0 ? int64_t(0) : int64_t(__builtin_amdgcn_readlane(incl, i - 1));
     const int64_t v = a.prefix_here ? sm.prefix[i] : a.prefix[i];
     const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(v));
     const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(v) >> 32));
@@ -660,10 +694,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, 
   if (cur >= end) return;
   // First sequence with tiles past the range start.
   int b = 0;
-  for (int hi = a.B - 1; b < hi;) {
-    const int mid = (b + hi) / 2;
-    if (pre(mid + 1) > cur) hi = mid;
-    else b = mid + 1;
+  if (wave_pfx) {
+    // Lowest lane whose inclusive prefix passes cur (there is one: cur < total).
+    const uint64_t past = __ballot(int((threadIdx.x & 63) < a.B) & int(int64_t(incl) > cur));
+    b = __builtin_ctzll(past);
+  } else {
+    for (int hi = a.B - 1; b < hi;) {
+      const int mid = (b + hi) / 2;
+      if (pre(mid + 1) > cur) hi = mid;
+      else b = mid + 1;
+    }
   }
   for (bool first = true; cur < end; first = false) {
     const int64_t p0 = pre(b), p1 = pre(b + 1);

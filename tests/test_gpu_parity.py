@@ -297,9 +297,14 @@ def test_empty_and_short_sequences():
 # Balanced ranges (the default plan of the matrix-core path): the batch's tiles are cut into
 # equal ranges on the device, so sequences are split at data-dependent places, several
 # whole sequences can share a workgroup, ranges can be empty (fewer tiles than ranges), and
-# batches above 1024 sequences take the separate prefix kernel.
+# batches above 1024 sequences take the separate prefix kernel.  Up to 64 sequences each
+# wave scans the lengths on its own (one lane per sequence); 65 takes the workgroup scan.
+_LENS_64 = [int(x) for x in np.random.default_rng(11).integers(0, 301, size=64)]
+_LENS_64[0] = _LENS_64[63] = 0  # empty first and last sequences
 BALANCED_CASES = {
     "many_short": (dict(batch=200, seq_len=200, n_heads=128), None),
+    "wave_scan_64": (dict(batch=64, seq_len=300, n_heads=128), _LENS_64),
+    "workgroup_scan_65": (dict(batch=65, seq_len=300, n_heads=128), _LENS_64 + [300]),
     "fewer_tiles_than_ranges": (dict(batch=2, seq_len=40, n_heads=128), [1, 40]),
     "empty_sequences": (dict(batch=5, seq_len=300, n_heads=128), [0, 300, 0, 1, 65]),
     "prefix_kernel_batch": (dict(batch=1100, seq_len=64, n_heads=64), None),
