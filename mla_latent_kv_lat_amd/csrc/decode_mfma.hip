@@ -99,11 +99,11 @@ __device__ __forceinline__ int64_t any_row(const Ctx& c, int t) {
   return int64_t(c.table[int64_t(c.b) * c.max_blocks + tc / c.bs]) * c.bs + tc % c.bs;
 }
 
-// Staged tiles are triple buffered (double buffered with the fp8 score product, whose codes
-// need another 16 KB per buffer); the schedule needs two.
+// Staged tiles are double buffered: in step n the loaders write buffer (n + 1) % 2 while
+// the score and output waves read buffer n % 2.
 template <bool QK8>
 struct alignas(16) Smem {
-  static constexpr int kNB = QK8 ? 2 : 3;
+  static constexpr int kNB = 2;
   uint16_t lat[kNB][kTile][kDC];        // staged latent rows (bf16), chunk c of row t at c ^ swz32(t)
   uint16_t rope[kNB][kTile][kDR];       // staged RoPE rows, chunk c of row t at c ^ rope_swz(t)
   uint8_t lat8[QK8 ? kNB : 1][kTile][QK8 ? kDC : 16];  // fp8 score product: the codes, same swizzle
@@ -117,7 +117,11 @@ struct alignas(16) Smem {
 
 __device__ __forceinline__ int rope_swz(int row) { return (row >> 1) & 7; }
 
-// V^T operand (as lds_operand_tr32) from a staged tile with 1 KB rows.
+// A 32 x 16 (m = 32 columns, k = 16 rows) bf16 A operand of v_mfma_f32_32x32x16_bf16, read
+// transposed from a staged tile (1 KB rows, swz32): rows k0 .. k0 + 15, columns c0 .. c0 + 31
+// (c0 a multiple of 32).  Lane l receives column c0 + l % 32 and rows k0 + 8h .. k0 + 8h + 7
+// (h = l / 32): 16-lane group G reads columns c0 + 16 (G & 1) + (0..15) of rows
+// k0 + 8 (G >> 1) + (0..7).
 __device__ __forceinline__ bf16x8 lds_operand_tr512(const uint16_t* tile, int k0, int c0, int lane) {
   const int G = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
   const int col = c0 + 16 * (G & 1) + 4 * q;

@@ -31,7 +31,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Chunk swizzle for LDS tiles whose rows are 128 bytes (8 chunks of 16 bytes, two rows
 // per 64-bank cycle).  Applied as chunk ^ swz128(row): the 16 consecutive rows written by
@@ -41,17 +40,8 @@ __device__ __forceinline__ int swz128(int row) {
   return (((row >> 1) & 1) << 1) | (((row >> 3) & 1) << 2) | ((row >> 2) & 1);
 }
 
-// Chunk swizzle for LDS tiles whose rows are 256 bytes (16 chunks of 16 bytes, one row
-// per 64-bank cycle).  Applied as chunk ^ swz256(row): bijective on the low 4 row bits, so
-// the 16 rows of one 16-byte-per-lane store hit distinct banks; and (swz256 >> 1) is
-// distinct on each half of a transposed read (rows 8g + r and 8g + 4 + r, g in {0, 1} or
-// {2, 3}), so those 8 rows' 32-byte column pairs hit distinct banks as well.
-__device__ __forceinline__ int swz256(int row) {
-  return ((row & 3) << 1) | ((row >> 2) & 1) | (((row >> 3) & 1) << 3);
-}
-
-// Chunk swizzle for 256-byte-row tiles read with 32-column transposed reads (see
-// lds_operand_tr32): chunk ^ swz32(row).  On gfx950 a 16-byte LDS read serves 16 lanes
+// Chunk swizzle for tiles whose rows are a multiple of 256 bytes, read with 32-column
+// transposed reads (the decode kernel's staged rows): chunk ^ swz32(row).  On gfx950 a 16-byte LDS read serves 16 lanes
 // (256 bytes) per cycle and a 16-byte write 8 lanes (128 bytes).  The swizzle is
 // bijective on the low 4 row bits (16 rows read at one chunk each hit distinct banks); its
 // low 3 bits are bijective on each aligned group of 8 rows (8 rows written at one chunk
@@ -81,30 +71,6 @@ __device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* tile, int k0, i
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
-// As lds_operand_tr, for a tile with 256-byte rows (128 columns, swizzled by swz256).
-__device__ __forceinline__ bf16x8 lds_operand_tr256(const uint16_t* tile, int k0, int c0, int lane) {
-  const int g = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
-  const int col = c0 + 4 * q;
-  const int k_lo = k0 + 8 * g + r, k_hi = k_lo + 4;
-  const u32x2 lo = lds_read_tr4(tile + k_lo * 128 + 8 * ((col >> 3) ^ swz256(k_lo)) + (col & 7));
-  const u32x2 hi = lds_read_tr4(tile + k_hi * 128 + 8 * ((col >> 3) ^ swz256(k_hi)) + (col & 7));
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
-// A 32 x 16 (m = 32 columns, k = 16 rows) bf16 A operand of v_mfma_f32_32x32x16_bf16,
-// read transposed from a row-major LDS tile with 256-byte rows (128 columns) swizzled by
-// swz32: rows k0 .. k0 + 15, columns c0 .. c0 + 31 (c0 a multiple of 32).  Lane l receives
-// column c0 + l % 32 and rows k0 + 8h .. k0 + 8h + 7 (h = l / 32): 16-lane group G reads
-// columns c0 + 16 (G & 1) + (0..15) of rows k0 + 8 (G >> 1) + (0..7).
-__device__ __forceinline__ bf16x8 lds_operand_tr32(const uint16_t* tile, int k0, int c0, int lane) {
-  const int G = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
-  const int col = c0 + 16 * (G & 1) + 4 * q;
-  const int k_lo = k0 + 8 * (G >> 1) + r, k_hi = k_lo + 4;
-  const u32x2 lo = lds_read_tr4(tile + k_lo * 128 + 8 * ((col >> 3) ^ swz32(k_lo)) + (col & 7));
-  const u32x2 hi = lds_read_tr4(tile + k_hi * 128 + 8 * ((col >> 3) ^ swz32(k_hi)) + (col & 7));
-  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-}
-
 // Two e4m3fn codes (low or high half-word of `w`) -> two bf16, exactly.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {
@@ -127,80 +93,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
 }
 
-// Cross-lane swaps of gfx950, written as single inline instructions (register operands
-// only, no memory access).  v_permlane16_swap_b32 a, b exchanges the odd 16-lane rows of
-// a with the even rows of b, so with a = b = x every lane ends up holding {x, x from
-// lane ^ 16} in (a, b); v_permlane32_swap_b32 does the same for lane ^ 32.  The builtin
-// forms are not used: the compiler folds max(first result, second result) down to the
-// first result, dropping the partner lane.  The leading s_nop covers the two wait
-// states the instruction needs after a VALU write of its operands.
-__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-
+// Cross-lane swap of gfx950, written as a single inline instruction (register operands
+// only, no memory access).  v_permlane32_swap_b32 a, b exchanges the upper 32 lanes of a
+// with the lower 32 lanes of b, so with a = b = x every lane ends up holding {x, x from
+// lane ^ 32} in (a, b).  The builtin form is not used: the compiler folds max(first
+// result, second result) down to the first result, dropping the partner lane.  The
+// leading s_nop covers the two wait states the instruction needs after a VALU write of
+// its operands.
 __device__ __forceinline__ void permlane32_swap(float& a, float& b) {
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-
-// Reductions over lanes {l, l ^ 16, l ^ 32, l ^ 48}.
-__device__ __forceinline__ float max_xor16_32(float x) {
-  float a = x, b = x;
-  permlane16_swap(a, b);
-  x = fmaxf(a, b);
-  a = x;
-  b = x;
-  permlane32_swap(a, b);
-  return fmaxf(a, b);
-}
-
-__device__ __forceinline__ float sum_xor16_32(float x) {
-  float a = x, b = x;
-  permlane16_swap(a, b);
-  x = a + b;
-  a = x;
-  b = x;
-  permlane32_swap(a, b);
-  return a + b;
-}
-
-// Data-parallel-primitive (DPP) lane permutations of a float, applied to the source
-// operand of a register move: quad_perm [1,0,3,2] (lane ^ 1), quad_perm [2,3,0,1]
-// (lane ^ 2), row_half_mirror (lane j of each 8-lane group reads lane 7 - j) and
-// row_mirror (lane j of each 16-lane row reads lane 15 - j).
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-constexpr int kDppXor1 = 0xB1;
-constexpr int kDppXor2 = 0x4E;
-constexpr int kDppHalfMirror = 0x141;
-constexpr int kDppRowMirror = 0x140;
-
-// Reductions over the 8-lane group of a lane (lanes 8j .. 8j + 7): after the two quad
-// steps every lane holds its quad's result, and the half mirror pairs each lane of one
-// quad with a lane of the other.
-__device__ __forceinline__ float max8(float x) {
-  x = fmaxf(x, dpp_f32<kDppXor1>(x));
-  x = fmaxf(x, dpp_f32<kDppXor2>(x));
-  return fmaxf(x, dpp_f32<kDppHalfMirror>(x));
-}
-
-__device__ __forceinline__ float sum8(float x) {
-  x += dpp_f32<kDppXor1>(x);
-  x += dpp_f32<kDppXor2>(x);
-  return x + dpp_f32<kDppHalfMirror>(x);
-}
-
-// Reductions over the 16-lane row of a lane: the 8-lane result, then row_mirror (lane j
-// reads lane 15 - j) pairs the two halves.
-__device__ __forceinline__ float max16(float x) {
-  x = max8(x);
-  return fmaxf(x, dpp_f32<kDppRowMirror>(x));
-}
-
-__device__ __forceinline__ float sum16(float x) {
-  x = sum8(x);
-  return x + dpp_f32<kDppRowMirror>(x);
 }
 
 }  // namespace mla
