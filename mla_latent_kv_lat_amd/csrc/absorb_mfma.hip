@@ -6,10 +6,10 @@
 // A workgroup owns one head, 64 output columns and a group of 32 rows; it stages that K x 64
 // slice of W[h] and its rows of x in LDS and multiplies them.  The product is formed
 // transposed, y^T[n, m] = W^T[n, :] . x^T[:, m], so that the staged weights are the A operand
-// (read transposed from LDS), the activation rows the B operand, and each lane stores 4
-// consecutive output columns.  Every byte is fetched once per workgroup: the four waves
-// share the activation rows through LDS (the load path of a compute unit, not HBM, bounds
-// these small products).
+// (read transposed from LDS) and the activation rows the B operand; bf16 results go back
+// through LDS so that every output row's 128 bytes leave in one store instruction.  Every
+// byte is fetched once per workgroup: the four waves share the activation rows through LDS
+// (the load path of a compute unit, not HBM, bounds these small products).
 #include "device_common.h"
 #include "mfma_common.h"
 #include "mla_internal.h"
@@ -91,23 +91,42 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
       bv[i][s2] = *reinterpret_cast<const bf16x8*>(&xs[r * K + 8 * ((4 * s2 + g) ^ xswz(r))]);
     }
 
+  f32x4 acc[kBlocks];
 #pragma unroll
   for (int i = 0; i < kBlocks; ++i) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < K / 32; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_operand_tr(wt, 32 * s, 16 * wv, lane), bv[i][s],
-                                                    acc, 0, 0, 0);
-    const int m = m0 + 16 * i + mm;
-    if (m < M) {
-      const int64_t off = (int64_t(m) * H + h) * N + n0 + 16 * wv + 4 * g;
-      if constexpr (F32OUT) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + off) = acc;
-      } else {
-        const uint32_t w0 = uint32_t(f32_to_bf16_bits(acc[0])) | (uint32_t(f32_to_bf16_bits(acc[1])) << 16);
-        const uint32_t w1 = uint32_t(f32_to_bf16_bits(acc[2])) | (uint32_t(f32_to_bf16_bits(acc[3])) << 16);
-        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + off) = u32x2{w0, w1};
-      }
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_operand_tr(wt, 32 * s, 16 * wv, lane), bv[i][s],
+                                                       acc[i], 0, 0, 0);
+  }
+  if constexpr (F32OUT) {
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i) {
+      const int m = m0 + 16 * i + mm;
+      if (m < M)
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + (int64_t(m) * H + h) * N + n0 + 16 * wv + 4 * g) = acc[i];
+    }
+  } else {
+    // The MG x 64 bf16 result goes through LDS (in the activation buffer, once every wave is
+    // done reading it) so that each row's 128 bytes are written by 8 lanes of one store:
+    // row r's 16-byte chunk c sits at c ^ ((r >> 1) & 7).
+    __syncthreads();
+    uint16_t* ys = xs;
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i) {
+      const int r = 16 * i + mm, col = 16 * wv + 4 * g;
+      *reinterpret_cast<u32x2*>(&ys[r * kBN + 8 * ((col >> 3) ^ ((r >> 1) & 7)) + (col & 7)]) =
+          u32x2{pack_bf16x2(acc[i][0], acc[i][1]), pack_bf16x2(acc[i][2], acc[i][3])};
+    }
+    __syncthreads();
+    constexpr int kRowsPerPass = kThreads / 8;
+#pragma unroll
+    for (int r = tid >> 3; r < MG; r += kRowsPerPass) {
+      const int c = tid & 7, m = m0 + r;
+      if (m < M)
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + (int64_t(m) * H + h) * N + n0 + 8 * c) =
+            *reinterpret_cast<const u32x4*>(&ys[r * kBN + 8 * (c ^ ((r >> 1) & 7))]);
     }
   }
 }
