@@ -236,6 +236,32 @@ def test_paged_equals_contiguous_bitwise():
     check_all(res_p, oracle_full(d), TOL["bf16"], what="paged")
 
 
+# Every paged layout of the decode kernel against the contiguous one, bit for bit, for bf16
+# and fp8 caches: blocks of 64 tokens (each 32-token tile inside one block, one table entry
+# per tile) and of 48 and 16 tokens (rows looked up token by token).  Rows a sequence does not
+# own hold NaN in both layouts, so reading one would show.
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_size", [64, 48, 16])
+def test_paged_layouts_equal_contiguous_bitwise(kv, block_size):
+    base = configs.PAGED_VARLEN if kv == "bf16" else configs.SPEC_FP8
+    cfg = base.with_(batch=5, seq_len=700, len_min=1, paged=True, block_size=block_size, cfg_id=27)
+    say("paged layout vs contiguous", kv, block_size, cfg)
+    inp = synth.make_inputs(cfg, 0, poison_tail=True)
+    res_p, _ = run(inp)
+    flat = synth.Inputs(**{**inp.__dict__})
+    flat.cfg = cfg.with_(paged=False)
+    lat_fill = synth.BF16_NAN_BITS if kv == "bf16" else synth.E4M3_NAN_CODE
+    flat.c_kv = O.gather_pages(inp.c_kv, inp.block_table, inp.seq_lens, cfg.seq_len, fill=lat_fill)
+    flat.k_rope = O.gather_pages(inp.k_rope, inp.block_table, inp.seq_lens, cfg.seq_len, fill=synth.BF16_NAN_BITS)
+    if kv == "fp8":
+        flat.kv_scale = O.gather_pages(inp.kv_scale, inp.block_table, inp.seq_lens, cfg.seq_len, fill=np.nan)
+    flat.block_table = None
+    res_c, _ = run(flat)
+    for k in ("o_lat", "lse", "out"):
+        assert np.array_equal(res_p[k], res_c[k], equal_nan=True), k
+    check_all(res_p, oracle_full(decoded(inp)), TOL[kv], what=f"paged {kv} bs={block_size}")
+
+
 # ------------------------------------------------ full-size, sampled oracle ----
 
 FULL = [configs.TINY, configs.V2_DECODE, configs.PAGED_VARLEN, configs.LONG_CONTEXT, configs.SPEC_FP8]
