@@ -84,7 +84,15 @@ typedef struct {
                             with V are unchanged.  Twice the matrix rate for the score, at
                             the cost of the query rounding.  Needs an MLA_FP8_E4M3 cache on
                             the matrix-core kernel (else MLA_ERR_UNSUPPORTED); mla_decode /
-                            mla_decode_paged only. */
+                            mla_decode_paged only.
+                            Accuracy: the result is attention with that rounded query (to the
+                            fp8 kernel bar of 2e-2), which is an approximation of the exact
+                            result, outside its 6e-2 parity bar in general: each logit moves by
+                            about 2^-4 of its size, so with logits of unit standard deviation
+                            the output stays within a few 1e-2 of exact attention over long
+                            contexts but the log-sum-exp of a sequence of a few tokens moves by
+                            up to about 7e-2, and with logits 4x larger (peaked attention) the
+                            output moves by several percent. */
 } mla_dims;
 
 /* Supported kernel set (anything else returns MLA_ERR_UNSUPPORTED):

@@ -102,6 +102,7 @@ __global__ __launch_bounds__(1024) void append_finalize_kernel(const float* __re
   const int nwaves = blockDim.x >> 6;
   const int b = m / sq, i = m - b * sq;
   const int pos = seq_lens[b] - sq + i;
+  if (pos < 0) return;  // a sequence shorter than its new tokens: nothing to place (uniform per workgroup)
   const int64_t prow = int64_t(table[int64_t(b) * max_blocks + pos / bs]) * bs + pos % bs;
   const int N = dc + dr;
   float amax = 0.f;

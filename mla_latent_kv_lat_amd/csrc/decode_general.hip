@@ -27,7 +27,9 @@ __global__ __launch_bounds__(kThreads) void decode_general_kernel(DecodeArgs a, 
   const int rows = a.sq * a.H;
   const int r0 = rblk * kRB;
   const int D = a.dc + a.dr;
-  const int L = a.seq_lens ? a.seq_lens[b] : int(a.T);
+  // Lengths are clamped to [0, T] like every other kernel of the call (the combine merges
+  // only the splits below the clamped length).
+  const int L = min(max(a.seq_lens ? a.seq_lens[b] : int(a.T), 0), int(a.T));
   const int t_lo = split * chunk;
   const int t_hi = min(L, t_lo + chunk);
   // The combine reads only splits that start below the sequence length.

@@ -350,27 +350,65 @@ def cache_append_rows(x, w_dkv, w_kr, seq_lens, q_len: int, base: float, pairing
 _E4M3_MAGNITUDES = None
 
 
-def quantize_e4m3fn_rows(c):
-    """Per-row fp8 encoding: scale = max|row| / 448 (1 if the row is zero) and, for every
-    element y = c / scale, the e4m3fn code of sign(y) and of the finite magnitude nearest
-    to |y| (ties to the magnitude whose code has an even mantissa), as a sign-magnitude
-    format rounds.  Returns (codes uint8, scale float64)."""
+def _nearest_e4m3fn_codes(y):
+    """e4m3fn code of sign(y) and of the finite magnitude nearest to |y| (|y| <= 448; ties
+    to the magnitude whose code has an even mantissa), as a sign-magnitude format rounds."""
     global _E4M3_MAGNITUDES
     if _E4M3_MAGNITUDES is None:
         codes = np.arange(0x7F, dtype=np.uint8)  # 0x00 .. 0x7E: +0 .. 448 (0x7F is NaN)
         _E4M3_MAGNITUDES = (codes, decode_e4m3fn(codes))
     cand_codes, cand_vals = _E4M3_MAGNITUDES
-    c = np.asarray(c, np.float64)
-    amax = np.max(np.abs(c), axis=-1)
-    scale = np.where(amax > 0, amax / 448.0, 1.0)
-    y = c / scale[..., None]
+    y = np.asarray(y, np.float64)
     d = np.abs(np.abs(y)[..., None] - cand_vals)              # [..., n, 127]
     best = d.min(axis=-1, keepdims=True)
     # among the nearest magnitudes prefer an even mantissa (code bit 0 clear)
     pref = np.where(d <= best, (cand_codes & 1).astype(np.int64), 2)
     mag = cand_codes[np.argmin(pref * 1e9 + d, axis=-1)]
     sign = np.where(np.signbit(y), 0x80, 0x00).astype(np.uint8)
-    return (mag | sign).astype(np.uint8), scale
+    return (mag | sign).astype(np.uint8)
+
+
+def quantize_e4m3fn_rows(c):
+    """Per-row fp8 encoding: scale = max|row| / 448 (1 if the row is zero) and, for every
+    element y = c / scale, the nearest e4m3fn code (_nearest_e4m3fn_codes).
+    Returns (codes uint8, scale float64)."""
+    c = np.asarray(c, np.float64)
+    amax = np.max(np.abs(c), axis=-1)
+    scale = np.where(amax > 0, amax / 448.0, 1.0)
+    return _nearest_e4m3fn_codes(c / scale[..., None]), scale
+
+
+def round_query_slices_e4m3(q_lat, slice_width: int = 128):
+    """The query as an fp8 score product sees it: every row of q_lat cut into slices of
+    ``slice_width`` columns, each slice replaced by its fp8 encoding decoded back.  The
+    encoding is the per-slice one of quantize_e4m3fn_rows (scale max|slice| / 448, nearest
+    e4m3fn code), with its decisions taken in float32, the precision of the kernel that
+    makes them (which code a value gets is an integer decided by floating point): the
+    query is read as float32, y = q * (448 / max|slice|) with the quotient and the product
+    rounded to float32 and clamped to +-448, and the slice scale is max|slice| * (1 / 448)
+    in float32."""
+    q = np.asarray(q_lat, np.float64)
+    *lead, d_c = q.shape
+    if d_c % slice_width:
+        raise ValueError("d_c must be a multiple of the slice width")
+    q32 = q.reshape(*lead, d_c // slice_width, slice_width).astype(np.float32)
+    amax = np.max(np.abs(q32), axis=-1, keepdims=True)
+    pos = amax > 0
+    safe = np.where(pos, amax, np.float32(1))
+    inv = np.where(pos, np.float32(448) / safe, np.float32(1)).astype(np.float32)
+    y = np.clip(q32 * inv, np.float32(-448), np.float32(448)).astype(np.float32)
+    scale = np.where(pos, amax * np.float32(1.0 / 448.0), np.float32(1)).astype(np.float32)
+    return (decode_e4m3fn(_nearest_e4m3fn_codes(y)) * scale.astype(np.float64)).reshape(q.shape)
+
+
+def latent_attention_fp8_query(q_lat, q_rope, c_kv, k_rope, seq_lens, scale, slice_width: int = 128):
+    """An approximation of latent_attention that lets the latent part of the score run as an
+    fp8 matrix product against a quantized (fp8) cache, the quantized-cache direction of
+    "Multi-Head Latent Attention (MLA) Explained", section "Which Models Use MLA and What Is
+    Next": the latent score term uses the rounded query of round_query_slices_e4m3; the RoPE
+    term and the product with the latent (the value) are exact.  Returns (o_lat, lse)."""
+    return latent_attention(round_query_slices_e4m3(q_lat, slice_width), q_rope, c_kv, k_rope, seq_lens,
+                            scale)
 
 
 # ---------------------------------------------------------------------------------

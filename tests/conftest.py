@@ -58,3 +58,12 @@ def max_rel_err(got, ref):
     if denom == 0:
         return float(np.max(np.abs(got[m]))) if m.any() else 0.0
     return float(np.max(np.abs(got[m] - ref[m])) / denom)
+
+
+def max_abs_err(got, ref):
+    """max |got - ref| over the finite reference entries (used for log-sum-exp values,
+    whose size, about ln T, would make a relative bar loose)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    m = np.isfinite(ref)
+    return float(np.max(np.abs(got[m] - ref[m]))) if m.any() else 0.0

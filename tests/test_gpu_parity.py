@@ -1,6 +1,7 @@
 """GPU parity: the HIP path through the C ABI against the CPU oracle.
 
-Bars (max |gpu - ref| / max |ref| per output tensor):
+Bars (max |gpu - ref| / max |ref| per output tensor; the log-sum-exp, whose size is about
+ln T, is held to the same number as an ABSOLUTE bar, max |gpu - ref|):
   fp32 workloads 1e-4; bf16 2e-2; fp8 cache 2e-2 against the oracle on the dequantized
   cache and 6e-2 against the oracle on the latent before quantization.
 Integer work (block-table lookup, fp8 code table) is bit-exact.
@@ -14,7 +15,7 @@ import torch
 from oracle import mla_oracle as O
 from mla_latent_kv_lat_amd import capi, configs, synth
 from mla_latent_kv_lat_amd.runner import DeviceWorkload, to_device, to_host_f64
-from conftest import decoded, max_rel_err
+from conftest import decoded, max_abs_err, max_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -34,9 +35,9 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-def run(inp, split_tokens=0, stages=True):
+def run(inp, split_tokens=0, stages=True, fp8_scores=0):
     """Run the three calls; return host float64 arrays of every output."""
-    w = DeviceWorkload(inp, split_tokens=split_tokens)
+    w = DeviceWorkload(inp, split_tokens=split_tokens, fp8_scores=fp8_scores)
     w.step()
     torch.cuda.synchronize()
     res = {"q_lat": to_host_f64(w.q_lat), "o_lat": to_host_f64(w.o_lat),
@@ -55,8 +56,8 @@ def check_all(res, ref, tol, batches=None, what=""):
     errs = {k: max_rel_err(res[k][sl], ref[k]) for k in ("q_lat", "o_lat", "out")}
     fin = np.isfinite(ref["lse"])
     assert np.array_equal(np.isneginf(res["lse"][sl]), np.isneginf(ref["lse"])), what
-    errs["lse"] = max_rel_err(res["lse"][sl][fin], ref["lse"][fin]) if fin.any() else 0.0
-    print(f"  {what} max rel err: " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    errs["lse"] = max_abs_err(res["lse"][sl][fin], ref["lse"][fin]) if fin.any() else 0.0
+    print(f"  {what} max rel err (lse: abs): " + ", ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     for k, v in errs.items():
         assert v <= tol, (what, k, v)
     return errs
@@ -165,7 +166,7 @@ def test_decode_stage_bf16_ragged(split_tokens, n_heads):
     cfg = configs.V2_DECODE.with_(batch=3, seq_len=1000, cfg_id=22, n_heads=n_heads)
     say("decode bf16 ragged", split_tokens, cfg)
     o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [1000, 77, 1], split_tokens)
-    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
+    e_o, e_l = max_rel_err(o, o_ref), max_abs_err(l, l_ref)
     print(f"  o_lat {e_o:.2e} lse {e_l:.2e}")
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
 
@@ -174,7 +175,7 @@ def test_decode_stage_peaked_scores():
     cfg = configs.V2_DECODE.with_(batch=2, seq_len=700, cfg_id=23)
     say("decode peaked", cfg)
     o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [700, 333], 128, q_gain=4.0)
-    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
+    e_o, e_l = max_rel_err(o, o_ref), max_abs_err(l, l_ref)
     print(f"  o_lat {e_o:.2e} lse {e_l:.2e}")
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
 
@@ -185,7 +186,7 @@ def test_decode_stage_fp8_causal(split_tokens, n_heads):
     cfg = configs.SPEC_FP8.with_(batch=3, seq_len=700, cfg_id=24, n_heads=n_heads)
     say("decode fp8 causal", split_tokens, cfg)
     o, l, o_ref, l_ref, inp, d, _ = decode_stage_case(cfg, 0, [700, 130, 4], split_tokens)
-    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
+    e_o, e_l = max_rel_err(o, o_ref), max_abs_err(l, l_ref)
     print(f"  o_lat {e_o:.2e} lse {e_l:.2e} (dequantized cache)")
     assert e_o <= TOL["fp8"] and e_l <= TOL["fp8"]
     # Against the latent before quantization (kernel + quantization error).
@@ -240,14 +241,20 @@ def test_paged_equals_contiguous_bitwise():
 # and fp8 caches: blocks of 64 tokens (each 32-token tile inside one block, one table entry
 # per tile) and of 48 and 16 tokens (rows looked up token by token).  Rows a sequence does not
 # own hold NaN in both layouts, so reading one would show.
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-@pytest.mark.parametrize("block_size", [64, 48, 16])
-def test_paged_layouts_equal_contiguous_bitwise(kv, block_size):
+# The fp8 score product ("fp8s": the loaders also stage the stored codes) is checked the same
+# way for the tile-per-block and the token-by-token layouts.
+PAGED_LAYOUT_CASES = [(kv, bs, 0) for kv in ("bf16", "fp8") for bs in (64, 48, 16)] + \
+    [("fp8", 64, 1), ("fp8", 48, 1)]
+
+
+@pytest.mark.parametrize("kv,block_size,fp8_scores", PAGED_LAYOUT_CASES,
+                         ids=[f"{k}-{b}" + ("-fp8s" if f else "") for k, b, f in PAGED_LAYOUT_CASES])
+def test_paged_layouts_equal_contiguous_bitwise(kv, block_size, fp8_scores):
     base = configs.PAGED_VARLEN if kv == "bf16" else configs.SPEC_FP8
     cfg = base.with_(batch=5, seq_len=700, len_min=1, paged=True, block_size=block_size, cfg_id=27)
-    say("paged layout vs contiguous", kv, block_size, cfg)
+    say("paged layout vs contiguous", kv, block_size, "fp8_scores", fp8_scores, cfg)
     inp = synth.make_inputs(cfg, 0, poison_tail=True)
-    res_p, _ = run(inp)
+    res_p, _ = run(inp, fp8_scores=fp8_scores)
     flat = synth.Inputs(**{**inp.__dict__})
     flat.cfg = cfg.with_(paged=False)
     lat_fill = synth.BF16_NAN_BITS if kv == "bf16" else synth.E4M3_NAN_CODE
@@ -256,10 +263,11 @@ def test_paged_layouts_equal_contiguous_bitwise(kv, block_size):
     if kv == "fp8":
         flat.kv_scale = O.gather_pages(inp.kv_scale, inp.block_table, inp.seq_lens, cfg.seq_len, fill=np.nan)
     flat.block_table = None
-    res_c, _ = run(flat)
+    res_c, _ = run(flat, fp8_scores=fp8_scores)
     for k in ("o_lat", "lse", "out"):
         assert np.array_equal(res_p[k], res_c[k], equal_nan=True), k
-    check_all(res_p, oracle_full(decoded(inp)), TOL[kv], what=f"paged {kv} bs={block_size}")
+    check_all(res_p, oracle_full(decoded(inp)), TOL_FP8_PREQUANT if fp8_scores else TOL[kv],
+              what=f"paged {kv} bs={block_size} fp8_scores={fp8_scores}")
 
 
 # ------------------------------------------------ full-size, sampled oracle ----
@@ -282,7 +290,30 @@ def test_full_size_sampled(cfg):
     ref = oracle_full(d)
     sl = slice(None) if batches is None else batches
     errs = check_all(res, ref, TOL[cfg.kv_dtype], batches=sl, what=cfg.name)
+    if cfg.kv_dtype == "fp8":
+        # Kernel + quantization error: the same sampled sequences against the oracle on the
+        # latent before quantization.
+        pre_ref = oracle_prequant(inp, batches)
+        e_pre = {k: max_rel_err(res[k][sl], pre_ref[k]) for k in ("o_lat", "out")}
+        fin = np.isfinite(pre_ref["lse"])
+        e_pre["lse"] = max_abs_err(res["lse"][sl][fin], pre_ref["lse"][fin])
+        print("  against the pre-quantization latent: " + ", ".join(f"{k}={v:.2e}" for k, v in e_pre.items()),
+              flush=True)
+        for k, v in e_pre.items():
+            assert v <= TOL_FP8_PREQUANT, (k, v)
     del w
+
+
+def oracle_prequant(inp, batches):
+    """The oracle's whole absorbed step on the float32 latent before fp8 encoding, for the
+    sampled sequences of a contiguous fp8 workload."""
+    sub = synth.Inputs(**{**inp.__dict__})
+    sub.q_nope, sub.q_rope = inp.q_nope[batches], inp.q_rope[batches]
+    sub.seq_lens = inp.seq_lens[batches]
+    sub.c_kv, sub.k_rope, sub.kv_scale = inp.c_kv[batches], inp.k_rope[batches], inp.kv_scale[batches]
+    d = decoded(sub)
+    d["c_kv"] = np.where(np.isfinite(inp.c_kv_prequant[batches]), inp.c_kv_prequant[batches], 0).astype(np.float64)
+    return oracle_full(d)
 
 
 def decoded_batches(inp, batches):
@@ -310,6 +341,24 @@ def test_run_to_run_bitwise_deterministic():
     torch.cuda.synchronize()
     for k, t in (("o_lat", w.o_lat), ("lse", w.lse), ("out", w.out)):
         assert np.array_equal(r1[k], to_host_f64(t)), k
+
+
+@pytest.mark.parametrize("n_heads", [128, 8], ids=["mfma", "general"])
+def test_lengths_above_T_are_clamped(n_heads):
+    """Every kernel of the call clamps seq_lens[b] to [0, T]: lengths above T give the
+    result of length T (and read no row past T)."""
+    cfg = configs.V2_DECODE.with_(batch=3, seq_len=256, cfg_id=29, n_heads=n_heads)
+    say("lengths above T", cfg)
+    o_t, l_t, o_ref, _, inp, _, w = decode_stage_case(cfg, 0, [256, 256, 100], 64)
+    # The same workload on the device, with the first two stored lengths past T.
+    w.seq_lens.copy_(torch.tensor([256 + 37, 256 + 1, 100], dtype=torch.int32))
+    q_bits = synth.store(O.absorb_query(O.decode(inp.q_nope, "bf16"), O.decode(inp.w_uk, "bf16"))
+                         .astype(np.float32), "bf16")
+    w.decode(q_lat=to_device(q_bits, "bf16", "cuda"))
+    torch.cuda.synchronize()
+    o_x, l_x = to_host_f64(w.o_lat), to_host_f64(w.lse)
+    assert np.array_equal(o_t, o_x) and np.array_equal(l_t, l_x)
+    assert max_rel_err(o_x, o_ref) <= TOL["bf16"]
 
 
 def test_empty_and_short_sequences():
@@ -350,16 +399,19 @@ def test_decode_balanced_ranges(case):
     assert np.all(o[empty] == 0) and np.all(np.isneginf(l[empty]))
     fin = np.isfinite(l_ref)
     assert np.array_equal(np.isneginf(l), np.isneginf(l_ref))
-    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l[fin], l_ref[fin])
+    e_o, e_l = max_rel_err(o, o_ref), max_abs_err(l[fin], l_ref[fin])
     print(f"  o_lat {e_o:.2e} lse {e_l:.2e}", flush=True)
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
 
 
 # fp8 score product (dims.fp8_scores = 1): the kernel rounds each row's 128-column query
-# slices to e4m3 and multiplies them with the stored codes.  The oracle stays the plain
-# definition on the stored cache, so the comparison includes the query rounding; the bar is
-# the fp8 workload's 6e-2, against the dequantized cache and against the latent before
-# quantization.
+# slices to e4m3 and multiplies them with the stored codes.  Its parity reference is the
+# oracle's plain definition of that approximation (latent_attention_fp8_query: the same
+# rounding of the query, then exact attention), held to the fp8 cache's kernel bar 2e-2
+# (lse: absolute).  How far the approximation itself is from exact attention is printed as a
+# measurement: the e4m3 query rounding moves each logit by about 2^-4 of its size, so on a
+# sequence of a few tokens the log-sum-exp moves by several 1e-2, and at 4x larger logits
+# (peaked attention) the output by several percent.
 @pytest.mark.parametrize("split_tokens,q_gain", [(0, 1.0), (128, 1.0), (0, 4.0)],
                          ids=["balanced", "split128", "peaked"])
 def test_decode_fp8_scores(split_tokens, q_gain):
@@ -367,33 +419,47 @@ def test_decode_fp8_scores(split_tokens, q_gain):
     say("decode fp8 scores", split_tokens, q_gain, cfg)
     o, l, o_ref, l_ref, inp, d, _ = decode_stage_case(cfg, 0, [700, 130, 4], split_tokens,
                                                       q_gain=q_gain, fp8_scores=1)
-    e_o, e_l = max_rel_err(o, o_ref), max_rel_err(l, l_ref)
-    pre = np.where(np.isfinite(inp.c_kv_prequant), inp.c_kv_prequant, 0).astype(np.float64)
     q_dec = O.decode(synth.store(O.absorb_query(d["q_nope"], d["w_uk"]).astype(np.float32), "bf16"), "bf16")
+    o_apx, l_apx = O.latent_attention_fp8_query(q_dec, d["q_rope"], d["c_kv"], d["k_rope"], d["seq_lens"],
+                                                d["scale"])
+    e_o, e_l = max_rel_err(o, o_apx), max_abs_err(l, l_apx)
+    assert np.array_equal(np.isneginf(l), np.isneginf(l_apx))
+    pre = np.where(np.isfinite(inp.c_kv_prequant), inp.c_kv_prequant, 0).astype(np.float64)
     o_pre, _ = O.latent_attention(q_dec, d["q_rope"], pre, d["k_rope"], d["seq_lens"], d["scale"])
-    e_pre = max_rel_err(o, o_pre)
-    print(f"  o_lat {e_o:.2e} lse {e_l:.2e} (dequantized cache), {e_pre:.2e} (pre-quantization)", flush=True)
-    # The query rounding costs about 2^-4 of each logit, so the error grows with the logits:
-    # at 4x the workload's logit scale (peaked attention) it is about twice the bar, which
-    # is checked here as a characterisation, not as parity.
-    bar = TOL_FP8_PREQUANT if q_gain == 1.0 else 2.5 * TOL_FP8_PREQUANT
-    assert e_o <= bar and e_l <= bar and e_pre <= bar
+    print(f"  against the fp8-query definition: o_lat {e_o:.2e} lse {e_l:.2e}; measured distance from "
+          f"exact attention: o_lat {max_rel_err(o, o_ref):.2e} lse {max_abs_err(l, l_ref):.2e} "
+          f"(dequantized cache), o_lat {max_rel_err(o, o_pre):.2e} (pre-quantization)", flush=True)
+    assert e_o <= TOL["fp8"] and e_l <= TOL["fp8"]
 
 
 def test_full_size_sampled_fp8_scores():
+    """The speculative fp8 workload at full size with the fp8 score product: the decode call
+    on the oracle's q_lat (stored as bf16, so both sides round the same query) against the
+    fp8-query definition on sampled sequences; then the whole step, whose distance from
+    exact attention is printed as a measurement."""
     cfg = configs.SPEC_FP8
     say("full size fp8 scores", cfg.name)
     inp = synth.make_inputs(cfg, 0)
+    q_lat = O.absorb_query(O.decode(inp.q_nope, cfg.act_dtype), O.decode(inp.w_uk, cfg.act_dtype))
+    q_bits = synth.store(q_lat.astype(np.float32), cfg.act_dtype)
+    del q_lat
     w = DeviceWorkload(inp, fp8_scores=1)
+    w.decode(q_lat=to_device(q_bits, cfg.act_dtype, "cuda"))
+    torch.cuda.synchronize()
+    o, l = to_host_f64(w.o_lat), to_host_f64(w.lse)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(l))
+    batches = SAMPLE[cfg.name]
+    d = decoded_batches(inp, batches)
+    o_apx, l_apx = O.latent_attention_fp8_query(O.decode(q_bits[batches], cfg.act_dtype), d["q_rope"], d["c_kv"],
+                                                d["k_rope"], d["seq_lens"], d["scale"])
+    e_o, e_l = max_rel_err(o[batches], o_apx), max_abs_err(l[batches], l_apx)
+    print(f"  decode vs fp8-query definition: o_lat {e_o:.2e} lse {e_l:.2e}", flush=True)
+    assert e_o <= TOL["fp8"] and e_l <= TOL["fp8"]
     w.step()
     torch.cuda.synchronize()
-    res = {"q_lat": to_host_f64(w.q_lat), "o_lat": to_host_f64(w.o_lat), "lse": to_host_f64(w.lse),
-           "out": to_host_f64(w.out)}
-    for k in ("o_lat", "out", "lse"):
-        assert np.all(np.isfinite(res[k])), k
-    batches = SAMPLE[cfg.name]
-    check_all(res, oracle_full(decoded_batches(inp, batches)), TOL_FP8_PREQUANT, batches=batches,
-              what=cfg.name + " fp8 scores")
+    ref = oracle_full(d)
+    print(f"  whole step, measured distance from exact attention: out "
+          f"{max_rel_err(to_host_f64(w.out)[batches], ref['out']):.2e}", flush=True)
     del w
 
 

@@ -15,7 +15,7 @@ import torch
 from oracle import mla_oracle as O
 from mla_latent_kv_lat_amd import capi, configs, synth
 from mla_latent_kv_lat_amd.runner import to_device, to_host_f64
-from conftest import decoded, max_rel_err
+from conftest import decoded, max_abs_err, max_rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -74,7 +74,7 @@ def check(cfg, lengths, rows=None, pass_lengths=True):
     fin = done & np.isfinite(ref_l)
     assert np.array_equal(np.isneginf(lse[done]), np.isneginf(ref_l[done]))
     e_o = max_rel_err(out[done], ref_o[done])
-    e_l = max_rel_err(lse[fin], ref_l[fin])
+    e_l = max_abs_err(lse[fin], ref_l[fin])
     print(f"  kv {e_kv:.2e}  out {e_o:.2e}  lse {e_l:.2e}", flush=True)
     assert e_kv <= TOL and e_o <= TOL and e_l <= TOL
 

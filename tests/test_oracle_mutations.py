@@ -10,6 +10,7 @@ from oracle import mla_oracle as O
 import test_oracle as P
 import test_oracle_cache_write as PC
 import test_oracle_query as PQ
+import test_oracle_fp8_query as PF
 
 _orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
 
@@ -113,6 +114,22 @@ def _fold_output_wrong_slice(w_uv, w_o):
     return np.einsum("hcj,hjd->hcd", w_uv, w_o)
 
 
+def _round_query_one_scale_per_row(q_lat, slice_width=128):
+    return _orig["round_query_slices_e4m3"](q_lat, np.asarray(q_lat).shape[-1])
+
+
+def _fp8_query_unrounded(q_lat, q_rope, c_kv, k_rope, seq_lens, scale, slice_width=128):
+    return _orig["latent_attention"](q_lat, q_rope, c_kv, k_rope, seq_lens, scale)
+
+
+def _fp8_query_rounds_rope_too(q_lat, q_rope, c_kv, k_rope, seq_lens, scale, slice_width=128):
+    q_rope = np.asarray(q_rope, np.float64)
+    pad = (-q_rope.shape[-1]) % slice_width
+    r = _orig["round_query_slices_e4m3"](np.concatenate([q_rope, np.zeros(q_rope.shape[:-1] + (pad,))], -1),
+                                         slice_width)[..., :q_rope.shape[-1]]
+    return _orig["latent_attention_fp8_query"](q_lat, r, c_kv, k_rope, seq_lens, scale, slice_width)
+
+
 CASES = [
     ("latent_attention", _latent_attention_no_rope, lambda: P.pin_absorbed_vs_explicit(P.small_inputs())),
     ("latent_attention", _latent_attention_scale_on_latent_only,
@@ -138,6 +155,9 @@ CASES = [
     ("query_from_hidden", _query_rope_from_content_matrix, PQ.pin_query_brute_force),
     ("output_projection", _output_transposed_heads, PQ.pin_output_identity_and_brute_force),
     ("fold_output_weights", _fold_output_wrong_slice, PQ.pin_fold_output_brute_force),
+    ("round_query_slices_e4m3", _round_query_one_scale_per_row, PF.pin_round_query_exact_slices),
+    ("latent_attention_fp8_query", _fp8_query_unrounded, PF.pin_fp8_query_brute_force),
+    ("latent_attention_fp8_query", _fp8_query_rounds_rope_too, PF.pin_fp8_query_attention_identity),
 ]
 
 
