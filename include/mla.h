@@ -27,8 +27,9 @@
  *   - Causality: seq_lens[b] counts cache rows INCLUDING the s_q new tokens; query i of
  *     sequence b sees rows 0 .. seq_lens[b] - s_q + i.  A query that sees no row gets
  *     o_lat = 0 and lse = -inf.
- *   - Ownership: the caller owns every buffer.  The library keeps no state, never
- *     allocates or frees device memory, and never synchronises: each call validates
+ *   - Ownership: the caller owns every buffer.  The library keeps no state (besides the
+ *     static device array of mla_decode_noalloc), never allocates or frees device memory,
+ *     and never synchronises: each call validates
  *     its arguments on the host, enqueues its kernels on `stream` (a hipStream_t passed
  *     as void*, NULL = the null stream) and returns.  Outputs must not alias inputs.
  *     The calls enqueue kernels only (no memset or copy), so a sequence of them can be
@@ -170,6 +171,26 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype kv_dt, int32_t
  * block of 64 query rows and 0 tokens.  No HIP call. */
 mla_status mla_decode_plan(const mla_dims* dims, mla_dtype kv_dt, int32_t max_seq_len,
                            int32_t* num_splits, int32_t* split_tokens);
+
+/* ---- latent attention without allocation -------------------------------------------
+ * For callers that cannot allocate device memory or pass a workspace: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same arguments, result and
+ * errors as mla_decode, minus the workspace: the partial results live in a static device
+ * array of MLA_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds from the
+ * library's first kernel launch there until the process ends.  The call allocates and frees
+ * nothing; on its first call on a device it looks up that device's copy of the array.
+ *   - Plans that need more than MLA_NOALLOC_SCRATCH_BYTES of workspace
+ *     (mla_decode_workspace_bytes) return MLA_ERR_WORKSPACE before any HIP call.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ *     different streams, or from different threads without ordering) race and give
+ *     undefined results.  Calls ordered on one stream are safe.
+ *   - Nothing in the array needs to start at zero (each call writes what it reads). */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_noalloc(const mla_dims* dims, const void* q_lat, const void* q_rope,
+                              mla_dtype q_dt, const void* c_kv, mla_dtype kv_dt, const float* kv_scale,
+                              const void* k_rope, mla_dtype rope_dt, int32_t T,
+                              const int32_t* seq_lens, void* o_lat, mla_dtype o_dt, float* lse,
+                              void* stream);
 
 /* ---- output-side absorption --------------------------------------------------------
  * out[b,i,h,j] = sum_c o_lat[b,i,h,c] * w_uv[h,c,j]   (fp32 accumulation)

@@ -30,8 +30,11 @@ EXPORTED = (
     "mla_decode_plan", "mla_absorb_out", "mla_gather_pages", "mla_fp8_e4m3_table",
     "mla_status_str", "mla_last_hip_error", "mla_version", "mla_cache_append_workspace_bytes",
     "mla_cache_append", "mla_rope_query", "mla_prefill_workspace_bytes", "mla_prefill",
-    "mla_linear_workspace_bytes", "mla_linear",
+    "mla_linear_workspace_bytes", "mla_linear", "mla_decode_noalloc",
 )
+
+# Size of the static device array mla_decode_noalloc keeps its partial results in.
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MLAError(RuntimeError):
@@ -74,6 +77,8 @@ _SIGNATURES = {
                    _vp, _sz, _vp],
     "mla_decode_paged": [_dims_p, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _i32,
                          _vp, _i32, _vp, _i32, _vp, _vp, _sz, _vp],
+    "mla_decode_noalloc": [_dims_p, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _i32, _vp,
+                           _vp],
     "mla_decode_workspace_bytes": [_dims_p, _i32, _i32],
     "mla_decode_plan": [_dims_p, _i32, _i32, ctypes.POINTER(_i32), ctypes.POINTER(_i32)],
     "mla_gather_pages": [_vp, _i32, _i32, _i64, _vp, _i32, _i32, _vp, _i32, _vp, _vp],
@@ -200,6 +205,19 @@ def mla_decode(d: MlaDims, q_lat, q_rope, c_kv, k_rope, T: int, seq_lens, o_lat,
                            T, _ptr(seq_lens), _ptr(o_lat), qdt if o_lat is None else _dt(o_lat, q_dtype),
                            _ptr(lse), _ptr(workspace), workspace_bytes, _stream(stream))
     return _done(st, "mla_decode", check)
+
+
+def mla_decode_noalloc(d: MlaDims, q_lat, q_rope, c_kv, k_rope, T: int, seq_lens, o_lat, lse, *,
+                       kv_scale=None, q_dtype=None, kv_dtype=None, stream=None, check=True) -> int:
+    """mla_decode with its partial results in the library's static device array (no
+    workspace argument; argument marshalling only)."""
+    qdt = _dt(q_lat, q_dtype)
+    kvdt = _dt(c_kv, kv_dtype)
+    st = _lib().mla_decode_noalloc(ctypes.byref(d), _ptr(q_lat), _ptr(q_rope), qdt, _ptr(c_kv), kvdt,
+                                   _ptr(kv_scale), _ptr(k_rope), qdt if k_rope is None else _dt(k_rope, q_dtype),
+                                   T, _ptr(seq_lens), _ptr(o_lat), qdt if o_lat is None else _dt(o_lat, q_dtype),
+                                   _ptr(lse), _stream(stream))
+    return _done(st, "mla_decode_noalloc", check)
 
 
 def mla_decode_paged(d: MlaDims, q_lat, q_rope, c_kv_pool, k_rope_pool, block_table, seq_lens,

@@ -99,6 +99,8 @@ void fill_common(DecodeArgs* a, const mla_dims* d, const void* q_lat, const void
   a->fp8_scores = d->fp8_scores != 0;
 }
 
+}  // namespace
+
 mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t ws_bytes) {
   if (p.workspace == 0) return MLA_OK;
   if (!ws || ws_bytes < p.workspace || !aligned(ws, 256)) return MLA_ERR_WORKSPACE;
@@ -130,7 +132,24 @@ mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   return MLA_OK;
 }
 
-}  // namespace
+mla_status hip_error_status(int err) { return hip_status(err); }
+
+mla_status prepare_decode(const mla_dims* d, const void* q_lat, const void* q_rope, mla_dtype q_dt,
+                          const void* c_kv, mla_dtype kv_dt, const float* kv_scale, const void* k_rope,
+                          mla_dtype rope_dt, int32_t T, const int32_t* seq_lens, void* o_lat,
+                          mla_dtype o_dt, float* lse, DecodeArgs* a, DecodePlan* p) {
+  mla_status st = check_decode_common(d, q_lat, q_rope, q_dt, c_kv, kv_dt, kv_scale, k_rope,
+                                       rope_dt, o_lat, o_dt, lse);
+  if (st != MLA_OK) return st;
+  if (T < 1) return MLA_ERR_INVALID_ARG;
+  if (seq_lens && !aligned(seq_lens, 4)) return MLA_ERR_INVALID_ARG;
+  st = plan_decode(d, q_dt, kv_dt, T, p);
+  if (st != MLA_OK) return st;
+  fill_common(a, d, q_lat, q_rope, q_dt, c_kv, kv_dt, kv_scale, k_rope, o_lat, lse);
+  a->T = T;
+  a->seq_lens = seq_lens;
+  return MLA_OK;
+}
 
 mla_status check_dims(const mla_dims* d) {
   if (!d) return MLA_ERR_INVALID_ARG;
@@ -422,18 +441,11 @@ mla_status mla_decode(const mla_dims* d, const void* q_lat, const void* q_rope, 
                       mla_dtype rope_dt, int32_t T, const int32_t* seq_lens, void* o_lat,
                       mla_dtype o_dt, float* lse, void* workspace, size_t workspace_bytes,
                       void* stream) {
-  mla_status st = check_decode_common(d, q_lat, q_rope, q_dt, c_kv, kv_dt, kv_scale, k_rope,
-                                       rope_dt, o_lat, o_dt, lse);
-  if (st != MLA_OK) return st;
-  if (T < 1) return MLA_ERR_INVALID_ARG;
-  if (seq_lens && !aligned(seq_lens, 4)) return MLA_ERR_INVALID_ARG;
-  DecodePlan p;
-  st = plan_decode(d, q_dt, kv_dt, T, &p);
-  if (st != MLA_OK) return st;
   DecodeArgs a;
-  fill_common(&a, d, q_lat, q_rope, q_dt, c_kv, kv_dt, kv_scale, k_rope, o_lat, lse);
-  a.T = T;
-  a.seq_lens = seq_lens;
+  DecodePlan p;
+  mla_status st = prepare_decode(d, q_lat, q_rope, q_dt, c_kv, kv_dt, kv_scale, k_rope, rope_dt, T,
+                                 seq_lens, o_lat, o_dt, lse, &a, &p);
+  if (st != MLA_OK) return st;
   st = attach_workspace(&a, p, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
   return run_decode(a, p, static_cast<hipStream_t>(stream));

@@ -97,6 +97,18 @@ struct CacheAppendArgs {
 
 // Host-only validation and planning (mla_api.cpp).
 mla_status check_dims(const mla_dims* d);
+// mla_decode's argument checks and plan, and the args of its kernels without a workspace.
+mla_status prepare_decode(const mla_dims* d, const void* q_lat, const void* q_rope, mla_dtype q_dt,
+                          const void* c_kv, mla_dtype kv_dt, const float* kv_scale, const void* k_rope,
+                          mla_dtype rope_dt, int32_t T, const int32_t* seq_lens, void* o_lat,
+                          mla_dtype o_dt, float* lse, DecodeArgs* a, DecodePlan* p);
+// Points the kernels' partial results at a workspace of ws_bytes bytes (MLA_ERR_WORKSPACE
+// when it is missing, too small or not 256-byte aligned).
+mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t ws_bytes);
+// Enqueues the planned kernels of one decode call on stream s.
+mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+// MLA_OK for 0, else MLA_ERR_HIP with the hipError_t kept for mla_last_hip_error().
+mla_status hip_error_status(int err);
 mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
                        DecodePlan* plan);
 bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len);

@@ -360,3 +360,26 @@ def test_binding_rejects_host_tensors():
         L.mla_absorb_q(d, x, A, A, dtype="bf16")
     with pytest.raises(ValueError, match="device tensors"):
         L.mla_linear(A, x, A, A, M=32, K=256, N=64, workspace_bytes=1 << 20, dtype="bf16")
+
+
+def test_noalloc_decode_validates_before_any_hip_call():
+    """mla_decode_noalloc shares mla_decode's checks, and refuses plans whose partial
+    results exceed its static array, all before touching the device."""
+    bf = "bf16"
+    assert L.mla_decode_noalloc(v2(batch=0), A, A, A, A, 4096, None, A, None, q_dtype=bf, kv_dtype=bf,
+                                check=False) == L.MLA_ERR_INVALID_ARG
+    assert L.mla_decode_noalloc(v2(), A, A, A, A, 0, None, A, None, q_dtype=bf, kv_dtype=bf,
+                                check=False) == L.MLA_ERR_INVALID_ARG
+    # fp32 caches run the general kernel with fixed splits: 1024 sequences x 32 splits of
+    # 64 rows of 512 fp32 partials need 4 GiB of workspace.
+    d = L.dims(1024, 1, 64, 128, 512, 64, 0.07, split_tokens=256)
+    need = L.mla_decode_workspace_bytes(d, "f32", 8192)
+    assert need > L.NOALLOC_SCRATCH_BYTES
+    assert L.mla_decode_noalloc(d, A, A, A, A, 8192, None, A, None, q_dtype="f32", kv_dtype="f32",
+                                check=False) == L.MLA_ERR_WORKSPACE
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+MLA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == L.NOALLOC_SCRATCH_BYTES

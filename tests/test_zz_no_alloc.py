@@ -1,0 +1,60 @@
+"""mla_decode_noalloc (partial results in the library's static device array) against
+mla_decode with a caller workspace: the same plan and kernels, so the outputs must be
+equal bit for bit.  Two calls in a row, the second on a smaller batch, so a result left in
+the shared array by the first call would show in the second."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from mla_latent_kv_lat_amd import capi, configs, synth
+from mla_latent_kv_lat_amd.runner import DeviceWorkload, to_device, to_host_f64
+from conftest import decoded, max_rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def device():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    capi.library()
+    return "cuda"
+
+
+def one_call(cfg, seed, lengths):
+    inp = synth.make_inputs(cfg, seed, lengths=np.array(lengths, np.int32), poison_tail=True)
+    d = decoded(inp)
+    q_bits = synth.store(O.absorb_query(d["q_nope"], d["w_uk"]).astype(np.float32), cfg.act_dtype)
+    w = DeviceWorkload(inp)
+    q_lat = to_device(q_bits, cfg.act_dtype, "cuda")
+    w.decode(q_lat=q_lat)
+    torch.cuda.synchronize()
+    o_ws, l_ws = to_host_f64(w.o_lat), to_host_f64(w.lse)
+    # The same call without a workspace, into freshly poisoned outputs.
+    w.o_lat.fill_(float("nan"))
+    w.lse.fill_(float("nan"))
+    c = w.caches[0]
+    capi.mla_decode_noalloc(w.dims, q_lat, w.q_rope, c["c_kv"], c["k_rope"], cfg.seq_len, w.seq_lens,
+                            w.o_lat, w.lse, kv_scale=c["kv_scale"])
+    torch.cuda.synchronize()
+    o_na, l_na = to_host_f64(w.o_lat), to_host_f64(w.lse)
+    assert np.array_equal(o_ws, o_na) and np.array_equal(l_ws, l_na)
+    o_ref, _ = O.latent_attention(O.decode(q_bits, cfg.act_dtype), d["q_rope"], d["c_kv"], d["k_rope"],
+                                  d["seq_lens"], d["scale"])
+    e = max_rel_err(o_na, o_ref)
+    print(f"  noalloc == workspace bitwise; o_lat vs oracle {e:.2e}", flush=True)
+    assert e <= (2e-2 if cfg.kv_dtype == "bf16" else 2e-2)
+    return w.ws_bytes
+
+
+@pytest.mark.parametrize("kv", ["bf16", "fp8"])
+def test_noalloc_equals_workspace_call_twice(kv):
+    base = configs.V2_DECODE if kv == "bf16" else configs.SPEC_FP8
+    big = base.with_(batch=9, seq_len=1500, cfg_id=60)
+    print(f"[case] noalloc {kv} first call {big.batch}x{big.seq_len}", flush=True)
+    ws1 = one_call(big, 0, np.random.default_rng(1).integers(1, 1501, size=9))
+    small = base.with_(batch=2, seq_len=300, cfg_id=61)
+    print(f"[case] noalloc {kv} second call {small.batch}x{small.seq_len}", flush=True)
+    ws2 = one_call(small, 1, [300, 17])
+    assert 0 < ws2 <= ws1 <= capi.NOALLOC_SCRATCH_BYTES
