@@ -167,8 +167,12 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype kv_dt, int32_t
 
 /* Host-only: the split-K plan mla_decode would use.  Writes the number of context splits
  * and the tokens per split (host pointers, either may be NULL); for balanced ranges
- * (split_tokens == 0 on the matrix-core kernel) it writes the number of ranges per row
- * block of 64 query rows and 0 tokens.  No HIP call. */
+ * (split_tokens == 0 on the matrix-core kernels) it writes the number of ranges per row
+ * block and 0 tokens.  A bf16 cache takes row blocks of 128 query rows when max_seq_len is
+ * at least 8192 (or when the rows are a multiple of 32 but not of 64), else of 64; the
+ * environment variable MLA_DECODE_ROW_BLOCK=64 or =128, read on every plan, overrides the
+ * length rule where that kernel applies.  An fp8 cache takes 64.  The device's compute
+ * unit count (256 when no device is present) sets the ranges.  No kernel launch. */
 mla_status mla_decode_plan(const mla_dims* dims, mla_dtype kv_dt, int32_t max_seq_len,
                            int32_t* num_splits, int32_t* split_tokens);
 
@@ -185,7 +189,7 @@ mla_status mla_decode_plan(const mla_dims* dims, mla_dtype kv_dt, int32_t max_se
  *     different streams, or from different threads without ordering) race and give
  *     undefined results.  Calls ordered on one stream are safe.
  *   - Nothing in the array needs to start at zero (each call writes what it reads). */
-#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+#define MLA_NOALLOC_SCRATCH_BYTES (80u << 20)
 mla_status mla_decode_noalloc(const mla_dims* dims, const void* q_lat, const void* q_rope,
                               mla_dtype q_dt, const void* c_kv, mla_dtype kv_dt, const float* kv_scale,
                               const void* k_rope, mla_dtype rope_dt, int32_t T,

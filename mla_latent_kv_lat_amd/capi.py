@@ -34,7 +34,7 @@ EXPORTED = (
 )
 
 # Size of the static device array mla_decode_noalloc keeps its partial results in.
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 80 << 20
 
 
 class MLAError(RuntimeError):

@@ -3,6 +3,7 @@
 // Validation and planning are pure host logic and run before any HIP call, so every
 // error path can be exercised on a machine without a GPU.  Launch failures surface as
 // MLA_ERR_HIP with the hipError_t kept per thread.
+#include <cstdlib>
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -14,7 +15,6 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-constexpr int kNumCUs = 256;          // MI355X compute units; the plan targets a fixed count
 constexpr int kMaxLatent = 2048;      // general-kernel limits (query rows are staged in LDS)
 constexpr int kMaxRope = 512;
 constexpr int kMaxQLen = 8;
@@ -108,7 +108,7 @@ mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t
   size_t o_bytes;
   if (p.balanced) {
     a->prefix = reinterpret_cast<const int64_t*>(w);
-    a->prefix_here = a->B <= kMaxInKernelPrefixBatch;
+    a->prefix_here = a->B <= p.max_prefix_here;
     w += align_up(size_t(a->B + 1) * 8, 256);
     o_bytes = align_up(size_t(p.num_splits) * 2 * p.rows * a->dc * 2, 256);
   } else {
@@ -125,8 +125,9 @@ mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
     const int err = launch_tile_prefix(a, s);
     if (err) return hip_status(err);
   }
-  int err = p.kernel == DecodeKernel::kMfma ? launch_decode_mfma(a, p, s)
-                                            : launch_decode_general(a, p, s);
+  int err = p.kernel == DecodeKernel::kLatent ? launch_decode_latent(a, p, s)
+            : p.kernel == DecodeKernel::kMfma ? launch_decode_mfma(a, p, s)
+                                              : launch_decode_general(a, p, s);
   if (err) return hip_status(err);
   if (p.balanced || p.num_splits > 1) return hip_status(launch_combine(a, p, s));
   return MLA_OK;
@@ -164,6 +165,13 @@ mla_status check_dims(const mla_dims* d) {
   return MLA_OK;
 }
 
+bool latent_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len) {
+  // 32-bit byte offsets within one sequence's rows, as for the 64-row kernel.
+  const int64_t seq_bytes = int64_t(max_seq_len) * 512 * 2;
+  return q_dt == MLA_BF16 && kv_dt == MLA_BF16 && d->fp8_scores == 0 && d->d_latent == 512 && d->d_rope == 64 &&
+         (d->q_len * d->n_heads) % 32 == 0 && seq_bytes < (int64_t(1) << 31);
+}
+
 bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len) {
   // The matrix-core kernel addresses one sequence's cache rows with 32-bit byte offsets.
   const int64_t seq_bytes = int64_t(max_seq_len) * 512 * (kv_dt == MLA_FP8_E4M3 ? 1 : 2);
@@ -178,10 +186,29 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
   if (max_seq_len < 1) return MLA_ERR_INVALID_ARG;
   DecodePlan p{};
   p.rows = d->q_len * d->n_heads;
+  int num_cus = kDefaultCUs, n_xcd = kDefaultXcds;
+  device_topology(&num_cus, &n_xcd);
+  p.n_xcd = n_xcd;
   int tile, min_chunk;
-  if (mfma_decode_eligible(d, q_dt, kv_dt, max_seq_len)) {
+  // Kernel choice for bf16 caches: the 128-row kernel halves how often a cache row is
+  // read per sequence but splits each sequence into twice as many ranges, whose merge
+  // costs a fixed few microseconds; it wins once sequences are long.  MLA_DECODE_ROW_BLOCK
+  // (64 or 128) overrides the length rule.
+  const char* rb_env = std::getenv("MLA_DECODE_ROW_BLOCK");
+  const int rb_force = rb_env ? std::atoi(rb_env) : 0;
+  const bool old_ok = mfma_decode_eligible(d, q_dt, kv_dt, max_seq_len);
+  const bool want_latent =
+      rb_force == 128 || (rb_force != 64 && (max_seq_len >= kLatentMinSeqLen || !old_ok));
+  if (want_latent && latent_decode_eligible(d, q_dt, kv_dt, max_seq_len)) {
+    p.kernel = DecodeKernel::kLatent;
+    p.row_block = 128;
+    p.max_prefix_here = 64;
+    tile = 64;
+    min_chunk = 512;
+  } else if (old_ok) {
     p.kernel = DecodeKernel::kMfma;
     p.row_block = 64;
+    p.max_prefix_here = kMaxInKernelPrefixBatch;
     tile = 64;
     min_chunk = 512;
   } else {
@@ -193,17 +220,17 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
   if (d->fp8_scores && (p.kernel != DecodeKernel::kMfma || kv_dt != MLA_FP8_E4M3))
     return MLA_ERR_UNSUPPORTED;
   const int64_t units = int64_t(d->batch) * ceil_div(p.rows, p.row_block);
-  // The matrix-core path stores its normalised partial outputs as bf16: they are combined
+  // The matrix-core paths store their normalised partial outputs as bf16: they are combined
   // into a bf16 output, and halving them halves the extra traffic of splitting.
-  p.part_bf16 = p.kernel == DecodeKernel::kMfma;
-  if (d->split_tokens == 0 && p.kernel == DecodeKernel::kMfma) {
+  p.part_bf16 = p.kernel != DecodeKernel::kGeneral;
+  if (d->split_tokens == 0 && p.kernel != DecodeKernel::kGeneral) {
     // Balanced ranges: the 32-token tiles of the whole batch (per row block) are divided
     // into num_splits contiguous ranges of equal size on the device, from the actual
     // sequence lengths, so that ragged batches keep every compute unit busy.  Each range
     // runs on one workgroup per row block; a sequence cut by range boundaries is merged
     // afterwards.
     const int64_t rblocks = ceil_div(p.rows, p.row_block);
-    const int64_t ranges = std::max<int64_t>(1, kNumCUs / rblocks);
+    const int64_t ranges = std::max<int64_t>(1, num_cus / rblocks);
     p.balanced = true;
     p.num_splits = int32_t(ranges);
     p.split_tokens = 0;
@@ -219,7 +246,7 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
   } else {
     // Enough workgroups to give every compute unit at least one, without making a split
     // so short that its partial result costs more traffic than its share of the cache.
-    const int64_t want_splits = ceil_div(kNumCUs, units);
+    const int64_t want_splits = ceil_div(num_cus, units);
     chunk = ceil_div(ceil_div(max_seq_len, want_splits), tile) * tile;
     if (chunk < min_chunk) chunk = min_chunk;
   }

@@ -14,7 +14,8 @@ namespace mla {
 // Which decode kernel family runs a call.
 enum class DecodeKernel : int {
   kGeneral = 0,  // VALU kernel for any supported shape (one workgroup per 4 query rows)
-  kMfma = 1,     // matrix-core kernel for d_c = 512, d_r = 64, bf16 queries, bf16/fp8 cache
+  kMfma = 1,     // matrix-core kernel (64 query rows per workgroup): fp8 caches
+  kLatent = 2,   // matrix-core kernel (128 query rows per workgroup): bf16 caches
 };
 
 // Split-K plan of one decode call.
@@ -27,7 +28,16 @@ struct DecodePlan {
   bool balanced;         // num_splits ranges of equal work over the whole batch (see below)
   bool part_bf16;        // partial outputs stored as bf16 (else fp32)
   size_t workspace;      // bytes of partial results (0 when num_splits == 1)
+  int32_t n_xcd;         // XCDs of the device (work units are spread in contiguous runs)
+  int32_t max_prefix_here;  // balanced ranges: largest batch whose tile prefix the decode kernel computes
 };
+
+// Topology the plan is made for: the current device's compute units and XCDs (queried once
+// per device), or these defaults when no device is present.
+constexpr int kDefaultCUs = 256;
+constexpr int kDefaultXcds = 8;
+constexpr int kLatentMinSeqLen = 8192;  // shortest longest-sequence for the 128-row kernel
+void device_topology(int* cus, int* xcds);
 
 // Everything a decode kernel reads or writes.  Pointers are device pointers.
 struct DecodeArgs {
@@ -112,10 +122,12 @@ mla_status hip_error_status(int err);
 mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
                        DecodePlan* plan);
 bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len);
+bool latent_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len);
 
 // Launchers (one per kernel file).  Return the hipError_t of the launch as int.
 int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+int launch_decode_latent(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_tile_prefix(const DecodeArgs& a, hipStream_t s);
 constexpr int kMaxInKernelPrefixBatch = 1024;  // batches up to this size skip the prefix kernel

@@ -183,12 +183,17 @@ def test_plan_covers_the_context(cfg):
     ws = L.mla_decode_workspace_bytes(d, cfg.kv_dtype, cfg.seq_len)
     rows = cfg.q_len * cfg.n_heads
     r = lambda x: (x + 255) // 256 * 256
-    # The matrix-core path (bf16 queries, d_c 512, d_r 64, rows a multiple of 64) balances
-    # the batch's tiles over n ranges on the device (tok = 0): one range per compute unit
-    # and row block, two bf16 partial slots per range, plus the [B + 1] int64 tile prefix.
-    mfma = cfg.act_dtype == "bf16" and cfg.d_latent == 512 and cfg.d_rope == 64 and rows % 64 == 0
+    # The matrix-core paths (bf16 queries, d_c 512, d_r 64) balance the batch's tiles over n
+    # ranges on the device (tok = 0): one range per compute unit and row block (128 query
+    # rows for a bf16 cache of sequences up to at least 8192 tokens, or with rows a
+    # multiple of 32 but not of 64; otherwise 64, which needs rows a multiple of 64; 256
+    # compute units planned for when no device is present), two bf16 partial slots per
+    # range, plus the [B + 1] int64 tile prefix.
+    mfma = cfg.act_dtype == "bf16" and cfg.d_latent == 512 and cfg.d_rope == 64 and (
+        (cfg.kv_dtype == "bf16" and rows % 32 == 0) or (cfg.kv_dtype == "fp8" and rows % 64 == 0))
     if mfma:
-        assert tok == 0 and n == max(1, 256 // (rows // 64))
+        row_block = 128 if cfg.kv_dtype == "bf16" and (cfg.seq_len >= 8192 or rows % 64) else 64
+        assert tok == 0 and n == max(1, 256 // ((rows + row_block - 1) // row_block))
         assert ws == r((cfg.batch + 1) * 8) + r(n * 2 * rows * cfg.d_latent * 2) + r(n * 2 * rows * 4)
         return
     assert n >= 1 and tok >= 1
@@ -383,3 +388,16 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define\s+MLA_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == L.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("rows", ["128", "64", None])
+def test_noalloc_scratch_holds_every_full_size_plan(rows, monkeypatch):
+    """The static array of mla_decode_noalloc holds the workspace of every full-size
+    workload's plan, on either bf16 matrix-core kernel."""
+    if rows:
+        monkeypatch.setenv("MLA_DECODE_ROW_BLOCK", rows)
+    else:
+        monkeypatch.delenv("MLA_DECODE_ROW_BLOCK", raising=False)
+    for cfg in (configs.V2_DECODE, configs.PAGED_VARLEN, configs.LONG_CONTEXT, configs.SPEC_FP8):
+        ws = L.mla_decode_workspace_bytes(L.dims_from_config(cfg), cfg.kv_dtype, cfg.seq_len)
+        assert 0 < ws <= L.NOALLOC_SCRATCH_BYTES, (cfg.name, rows, ws)

@@ -35,6 +35,22 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
+# The bf16 decode has two matrix-core kernels (row blocks of 128 and of 64 query rows) and a
+# general one (any head count); the plan picks by sequence length, and the environment
+# variable MLA_DECODE_ROW_BLOCK forces one of the first two, so every small case below runs
+# on each of them.
+KERNELS = {"rows128": (128, "128"), "rows64": (128, "64"), "general": (8, None)}
+
+
+def use_kernel(kern, monkeypatch):
+    n_heads, env = KERNELS[kern]
+    if env is None:
+        monkeypatch.delenv("MLA_DECODE_ROW_BLOCK", raising=False)
+    else:
+        monkeypatch.setenv("MLA_DECODE_ROW_BLOCK", env)
+    return n_heads
+
+
 def run(inp, split_tokens=0, stages=True, fp8_scores=0):
     """Run the three calls; return host float64 arrays of every output."""
     w = DeviceWorkload(inp, split_tokens=split_tokens, fp8_scores=fp8_scores)
@@ -160,9 +176,10 @@ def decode_stage_case(cfg, seed, lengths, split_tokens, poison=True, q_gain=1.0,
     return o_got, lse_got, o_ref, lse_ref, inp, d, w
 
 
-@pytest.mark.parametrize("n_heads", [128, 8], ids=["mfma", "general"])
+@pytest.mark.parametrize("kern", list(KERNELS))
 @pytest.mark.parametrize("split_tokens", [0, 64, 192, 512])
-def test_decode_stage_bf16_ragged(split_tokens, n_heads):
+def test_decode_stage_bf16_ragged(split_tokens, kern, monkeypatch):
+    n_heads = use_kernel(kern, monkeypatch)
     cfg = configs.V2_DECODE.with_(batch=3, seq_len=1000, cfg_id=22, n_heads=n_heads)
     say("decode bf16 ragged", split_tokens, cfg)
     o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [1000, 77, 1], split_tokens)
@@ -219,7 +236,9 @@ def test_causal_equals_independent_single_query_decodes():
 
 # -------------------------------------------------------------- paged cache ----
 
-def test_paged_equals_contiguous_bitwise():
+@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+def test_paged_equals_contiguous_bitwise(kern, monkeypatch):
+    use_kernel(kern, monkeypatch)
     cfg = configs.PAGED_VARLEN.with_(batch=6, seq_len=1500, len_min=1, cfg_id=26)
     say("paged vs contiguous", cfg)
     inp = synth.make_inputs(cfg, 0, poison_tail=True)
@@ -249,7 +268,11 @@ PAGED_LAYOUT_CASES = [(kv, bs, 0) for kv in ("bf16", "fp8") for bs in (64, 48, 1
 
 @pytest.mark.parametrize("kv,block_size,fp8_scores", PAGED_LAYOUT_CASES,
                          ids=[f"{k}-{b}" + ("-fp8s" if f else "") for k, b, f in PAGED_LAYOUT_CASES])
-def test_paged_layouts_equal_contiguous_bitwise(kv, block_size, fp8_scores):
+@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+def test_paged_layouts_equal_contiguous_bitwise(kv, block_size, fp8_scores, kern, monkeypatch):
+    if kv != "bf16" and kern == "rows128":
+        pytest.skip("the 128-row kernel reads bf16 caches only")
+    use_kernel(kern, monkeypatch)
     base = configs.PAGED_VARLEN if kv == "bf16" else configs.SPEC_FP8
     cfg = base.with_(batch=5, seq_len=700, len_min=1, paged=True, block_size=block_size, cfg_id=27)
     say("paged layout vs contiguous", kv, block_size, "fp8_scores", fp8_scores, cfg)
@@ -277,9 +300,16 @@ SAMPLE = {configs.V2_DECODE.name: [0, 17, 31], configs.PAGED_VARLEN.name: [0, 33
           configs.LONG_CONTEXT.name: [2], configs.SPEC_FP8.name: [5, 127]}
 
 
-@pytest.mark.parametrize("cfg", FULL, ids=lambda c: c.name)
-def test_full_size_sampled(cfg):
-    say("full size", cfg.name)
+# Each workload at full size with the plan's own kernel choice, plus the bf16 decode and the
+# paged workload forced onto the other matrix-core kernel.
+FULL_CASES = [(c, None) for c in FULL] + [(configs.V2_DECODE, "rows128"), (configs.PAGED_VARLEN, "rows64")]
+
+
+@pytest.mark.parametrize("cfg,kern", FULL_CASES, ids=[c.name + (f"-{k}" if k else "") for c, k in FULL_CASES])
+def test_full_size_sampled(cfg, kern, monkeypatch):
+    if kern is not None:
+        use_kernel(kern, monkeypatch)
+    say("full size", cfg.name, kern or "planned kernel")
     inp = synth.make_inputs(cfg, 0)
     res, w = run(inp)
     print(f"  plan (splits, tokens) = {res['plan']}", flush=True)
@@ -332,7 +362,9 @@ def decoded_batches(inp, batches):
     return decoded(sub)
 
 
-def test_run_to_run_bitwise_deterministic():
+@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+def test_run_to_run_bitwise_deterministic(kern, monkeypatch):
+    use_kernel(kern, monkeypatch)
     cfg = configs.V2_DECODE.with_(batch=4, seq_len=2048, cfg_id=27)
     say("determinism", cfg)
     inp = synth.make_inputs(cfg, 0)
@@ -343,10 +375,11 @@ def test_run_to_run_bitwise_deterministic():
         assert np.array_equal(r1[k], to_host_f64(t)), k
 
 
-@pytest.mark.parametrize("n_heads", [128, 8], ids=["mfma", "general"])
-def test_lengths_above_T_are_clamped(n_heads):
+@pytest.mark.parametrize("kern", list(KERNELS))
+def test_lengths_above_T_are_clamped(kern, monkeypatch):
     """Every kernel of the call clamps seq_lens[b] to [0, T]: lengths above T give the
     result of length T (and read no row past T)."""
+    n_heads = use_kernel(kern, monkeypatch)
     cfg = configs.V2_DECODE.with_(batch=3, seq_len=256, cfg_id=29, n_heads=n_heads)
     say("lengths above T", cfg)
     o_t, l_t, o_ref, _, inp, _, w = decode_stage_case(cfg, 0, [256, 256, 100], 64)
@@ -361,8 +394,10 @@ def test_lengths_above_T_are_clamped(n_heads):
     assert max_rel_err(o_x, o_ref) <= TOL["bf16"]
 
 
-def test_empty_and_short_sequences():
-    cfg = configs.V2_DECODE.with_(batch=3, seq_len=256, cfg_id=28)
+@pytest.mark.parametrize("kern", list(KERNELS))
+def test_empty_and_short_sequences(kern, monkeypatch):
+    n_heads = use_kernel(kern, monkeypatch)
+    cfg = configs.V2_DECODE.with_(batch=3, seq_len=256, cfg_id=28, n_heads=n_heads)
     say("empty sequence", cfg)
     o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [0, 1, 256], 64)
     assert np.all(o[0] == 0) and np.all(np.isneginf(l[0]))
@@ -386,8 +421,10 @@ BALANCED_CASES = {
 }
 
 
+@pytest.mark.parametrize("kern", ["rows128", "rows64"])
 @pytest.mark.parametrize("case", list(BALANCED_CASES))
-def test_decode_balanced_ranges(case):
+def test_decode_balanced_ranges(case, kern, monkeypatch):
+    use_kernel(kern, monkeypatch)
     kw, lengths = BALANCED_CASES[case]
     cfg = configs.V2_DECODE.with_(cfg_id=30, **kw)
     if lengths is None:

@@ -48,8 +48,11 @@ def one_call(cfg, seed, lengths):
     return w.ws_bytes
 
 
-@pytest.mark.parametrize("kv", ["bf16", "fp8"])
-def test_noalloc_equals_workspace_call_twice(kv):
+@pytest.mark.parametrize("kv,rows", [("bf16", "128"), ("bf16", "64"), ("fp8", None)])
+def test_noalloc_equals_workspace_call_twice(kv, rows, monkeypatch):
+    # A bf16 cache runs on either matrix-core kernel (row blocks of 128 or 64 query rows).
+    if rows:
+        monkeypatch.setenv("MLA_DECODE_ROW_BLOCK", rows)
     base = configs.V2_DECODE if kv == "bf16" else configs.SPEC_FP8
     big = base.with_(batch=9, seq_len=1500, cfg_id=60)
     print(f"[case] noalloc {kv} first call {big.batch}x{big.seq_len}", flush=True)
