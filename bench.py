@@ -13,8 +13,11 @@ Prints one JSON line:
   value        latent-cache GB/s of the whole step (cache bytes / step time)
   roofline     the decode call (its kernels) against the 8 TB/s HBM peak, timed with HIP
                events around each call inside the timed loop
+  configs      the decode call alone on the other full-size workloads (paged variable-length,
+               long context, speculative fp8), each with its own roofline, plus the headline's
+               decode call with its cache left warm in the last-level cache (labelled)
   cpu_baseline the CPU oracle (fp64 numpy, absorbed form) on a bounded sample of the
-               same workload, on this host's cores
+               same workload, on this host's cores, and on one core
 """
 from __future__ import annotations
 
@@ -79,9 +82,89 @@ def measured_traffic(workload: str):
     return float(m_val.group(1))
 
 
-def cpu_baseline(inp, budget_s: float) -> dict:
+def metric_name(cfg) -> str:
+    lens = f"T={cfg.seq_len}" if not cfg.paged else f"T<={cfg.seq_len}, paged"
+    sq = f", s_q={cfg.q_len}" if cfg.q_len > 1 else ""
+    return f"MLA decode latent-cache GB/s + TFLOP/s and % roofline ({cfg.kv_dtype}, B={cfg.batch}, {lens}{sq})"
+
+
+def decode_roofline(cfg, wc, call_ms: float) -> dict:
+    """The decode call against HBM for the streaming workloads, against the bf16 matrix peak
+    where the arithmetic intensity is past the ridge (speculative multi-token fp8)."""
+    mfma_bound = wc["attn_flops"] / wc["decode_bytes"] > BF16_MFMA_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if mfma_bound:
+        achieved = wc["attn_flops"] / (call_ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFS, 4), "traffic": None}
+    achieved = wc["decode_bytes"] / (call_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name)}
+
+
+def time_decode_calls(w, calls: int, warmup: int, ramp_ms: float = 200.0) -> list:
+    """Milliseconds of each of `calls` decode calls (HIP events on the stream the library
+    launches on), cycling over the workload's cache replicas, after `ramp_ms` of untimed
+    calls (the clock drops while the host prepares inputs) and `warmup` more."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ramp_ms:
+        for k in range(10):
+            w.decode(w.caches[k % len(w.caches)])
+        torch.cuda.synchronize()
+    for k in range(warmup):
+        w.decode(w.caches[k % len(w.caches)])
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for k in range(calls):
+        ev[k][0].record()
+        w.decode(w.caches[k % len(w.caches)])
+        ev[k][1].record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def side_workload(cfg, calls: int, warmup: int) -> dict:
+    """The decode call alone on one full-size workload (queries absorbed once beforehand),
+    its cache bigger than the last-level cache, so every call streams it from HBM."""
+    import torch
+    from mla_latent_kv_lat_amd import synth
+    from mla_latent_kv_lat_amd.runner import DeviceWorkload
+    t0 = time.perf_counter()
+    inp = synth.make_inputs(cfg, 0)
+    wc = work_counts(cfg, inp.seq_lens)
+    w = DeviceWorkload(inp, replicas=1)
+    w.absorb_q()
+    gen_s = time.perf_counter() - t0
+    ms = time_decode_calls(w, calls, warmup)
+    avg = float(np.mean(ms))
+    out = {"metric": metric_name(cfg), "workload": cfg.name, "decode_call_us": round(avg * 1e3, 2),
+           "decode_call_us_p10_p90": [round(float(np.percentile(ms, 10)) * 1e3, 2),
+                                      round(float(np.percentile(ms, 90)) * 1e3, 2)],
+           "value": round(wc["cache_bytes"] / (avg * 1e-3) / 1e9, 2), "unit": "GB/s",
+           "tflops": round(wc["attn_flops"] / (avg * 1e-3) / 1e12, 2),
+           "decode_tokens_per_s": round(cfg.batch * cfg.q_len / (avg * 1e-3), 1),
+           "dtype": cfg.kv_dtype, "cache_bytes": wc["cache_bytes"], "splits": w.plan[0], "calls": calls,
+           "roofline": decode_roofline(cfg, wc, avg)}
+    print(f"[bench] {cfg.name}: decode call {avg * 1e3:.1f} us over {calls} calls (inputs {gen_s:.1f} s)",
+          file=sys.stderr, flush=True)
+    del w
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def host_cores() -> int:
+    """Cores this process may run on (its CPU affinity), not the machine's count."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(inp, budget_s: float, single_core_budget_s: float = 0.0) -> dict:
     """Time the CPU oracle's absorbed form on whole sequences until the time budget is spent
-    (cycling over the batch again when it is done sooner)."""
+    (cycling over the batch again when it is done sooner); then, with a budget, the same on
+    one core (its BLAS limited to one thread)."""
     from oracle import mla_oracle as O
     cfg = inp.cfg
     act = cfg.act_dtype
@@ -103,27 +186,40 @@ def cpu_baseline(inp, budget_s: float) -> dict:
         return q_nope, q_rope, lat, rope
 
     w_uk, w_uv = O.decode(inp.w_uk, act), O.decode(inp.w_uv, act)
-    done, secs = [], 0.0
-    b = 0
-    while secs < budget_s:
-        # Grow the sample in whole sequences until the time budget is spent.
-        q_nope, q_rope, lat, rope = dec_seq([b])
-        t0 = time.perf_counter()
-        O.mla_absorbed(q_nope, q_rope, lat, rope, w_uk, w_uv, inp.seq_lens[[b]], cfg.softmax_scale)
-        secs += time.perf_counter() - t0
-        done.append(b)
-        b = (b + 1) % cfg.batch
+
+    def run(budget):
+        done, secs = [], 0.0
+        b = 0
+        while secs < budget:
+            # Grow the sample in whole sequences until the time budget is spent.
+            q_nope, q_rope, lat, rope = dec_seq([b])
+            t0 = time.perf_counter()
+            O.mla_absorbed(q_nope, q_rope, lat, rope, w_uk, w_uv, inp.seq_lens[[b]], cfg.softmax_scale)
+            secs += time.perf_counter() - t0
+            done.append(b)
+            b = (b + 1) % cfg.batch
+        return done, secs
+
+    def sample(done, secs):
+        return (f"{len(done)} sequence passes over the {cfg.batch} sequences of {cfg.name}, whole absorbed "
+                f"decode (q absorption, attention, output absorption) in fp64, {secs:.2f} s wall")
+
+    done, secs = run(budget_s)
     wc = work_counts(cfg, inp.seq_lens[done])
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    return {"value": wc["cache_bytes"] / secs / 1e9, "unit": "GB/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{len(done)} sequence passes over the {cfg.batch} sequences of {cfg.name}, "
-                      f"whole absorbed decode (q absorption, attention, output absorption) in "
-                      f"fp64, {secs:.2f} s wall"}
+    res = {"value": wc["cache_bytes"] / secs / 1e9, "unit": "GB/s", "cores": int(min(threads, host_cores())),
+           "kind": "oracle", "sample": sample(done, secs)}
+    if single_core_budget_s > 0:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            done1, secs1 = run(single_core_budget_s)
+        res["single_core"] = {"value": work_counts(cfg, inp.seq_lens[done1])["cache_bytes"] / secs1 / 1e9,
+                              "unit": "GB/s", "cores": 1, "sample": sample(done1, secs1)}
+    return res
 
 
 def bench_cache_append(args, cfg) -> int:
@@ -361,6 +457,13 @@ def main() -> int:
     ap.add_argument("--fp8-scores", type=int, choices=(0, 1), default=0,
                     help="1: latent score term as an fp8 matrix product (fp8-cache workloads)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--cpu-single-core-budget", type=float, default=8.0,
+                    help="seconds of the oracle on one core (0: skip)")
+    ap.add_argument("--side-workloads", default="paged_varlen_bf16_b64,long_bf16_b4_t131072,spec4_fp8_b128_t8192",
+                    help="comma-separated workloads whose decode call is also timed (empty: none)")
+    ap.add_argument("--side-calls", type=int, default=40, help="timed decode calls per side workload")
+    ap.add_argument("--warm-calls", type=int, default=100,
+                    help="decode calls timed with the cache left in the last-level cache (0: skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one plain device copy of this size (for counter calibration)")
@@ -455,19 +558,32 @@ def main() -> int:
           f"(p10 {np.percentile(dec_ms, 10) * 1e3:.1f}, p90 {np.percentile(dec_ms, 90) * 1e3:.1f})",
           file=sys.stderr, flush=True)
 
-    # The decode call's roofline: HBM for the streaming configurations, the bf16 matrix
-    # peak where the arithmetic intensity is past the ridge (speculative multi-token fp8).
-    mfma_bound = wc["attn_flops"] / wc["decode_bytes"] > BF16_MFMA_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if mfma_bound:
-        achieved = wc["attn_flops"] / (dec_avg * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFS, 4), "traffic": None}
-    else:
-        achieved = wc["decode_bytes"] / (dec_avg * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name)}
+    roof = decode_roofline(cfg, wc, dec_avg)
+
+    # The same decode call with one cache copy, called back to back: the 151 MB cache stays in
+    # the 256 MB last-level cache between calls (not a cold-HBM figure; labelled as such).
+    side = {}
+    if args.warm_calls > 0:
+        w1 = DeviceWorkload(inp, split_tokens=args.split_tokens, replicas=1, fp8_scores=args.fp8_scores)
+        w1.absorb_q()
+        warm_ms = time_decode_calls(w1, args.warm_calls, 20)
+        warm_avg = float(np.mean(warm_ms))
+        del w1
+        side["last_level_cache_warm"] = {
+            "workload": cfg.name, "note": "one cache copy, calls back to back: served largely from the 256 MB "
+                                          "last-level cache, not from HBM",
+            "decode_call_us": round(warm_avg * 1e3, 2),
+            "value": round(wc["cache_bytes"] / (warm_avg * 1e-3) / 1e9, 2), "unit": "GB/s"}
+    plan, n_replicas = w.plan, len(w.caches)
+    names = [n for n in args.side_workloads.split(",") if n and n != cfg.name]
+    if names:
+        del w
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        for n in names:
+            side[n] = side_workload(configs.BY_NAME[n], args.side_calls, 5)
     result = {
-        "metric": "MLA decode latent-cache GB/s + TFLOP/s and % roofline (bf16, B=32, T=4096)",
+        "metric": metric_name(cfg),
         "value": round(wc["cache_bytes"] / (ms_step * 1e-3) / 1e9, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -483,9 +599,9 @@ def main() -> int:
         "config": {"workload": cfg.name, "batch": cfg.batch, "q_len": cfg.q_len,
                    "n_heads": cfg.n_heads, "d_head": cfg.d_head, "d_latent": cfg.d_latent,
                    "d_rope": cfg.d_rope, "seq_len": cfg.seq_len, "kv_dtype": cfg.kv_dtype,
-                   "paged": cfg.paged, "splits": w.plan[0], "split_tokens": w.plan[1],
+                   "paged": cfg.paged, "splits": plan[0], "split_tokens": plan[1],
                    "fp8_scores": args.fp8_scores,
-                   "cache_replicas": len(w.caches)},
+                   "cache_replicas": n_replicas},
         "tflops": round(wc["attn_flops"] / (ms_step * 1e-3) / 1e12, 2),
         "decode_tokens_per_s": round(cfg.batch * cfg.q_len / (ms_step * 1e-3), 1),
         "decode_call_us": round(dec_avg * 1e3, 2),
@@ -493,10 +609,11 @@ def main() -> int:
         "decode_call_tflops": round(wc["attn_flops"] / (dec_avg * 1e-3) / 1e12, 2),
         "decode_call_mfma_frac": round(wc["attn_flops"] / (dec_avg * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS, 4),
         "roofline": roof,
+        "configs": side,
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget)
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_budget, args.cpu_single_core_budget)
     print(json.dumps(result), flush=True)
     return 0
 

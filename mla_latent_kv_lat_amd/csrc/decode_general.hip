@@ -197,6 +197,7 @@ __global__ __launch_bounds__(kThreads) void decode_general_kernel(DecodeArgs a, 
 // in flight together, merged with a running maximum so no separate max pass is needed.
 constexpr int kCombRows = 4;   // query rows (one per wave) per workgroup
 constexpr int kCombBatch = 8;  // splits per batch (4 when a row has at most 4 pieces)
+constexpr int kCombWaves = 4;  // waves sharing one row in the merge of balanced ranges
 
 template <bool VEC>
 __device__ __forceinline__ void load8_f32(float (&v)[8], const float* p, int c, int dc) {
@@ -311,17 +312,67 @@ __global__ __launch_bounds__(256) void combine_kernel(DecodeArgs a, int S, int c
 // boundaries is merged from the partial of its first range (slot 1 when that range began
 // in an earlier sequence, else slot 0) and slot 0 of each later range it reaches.  A
 // sequence without tiles gets zeros and lse = -inf.
+// Running merge, for the 8 columns c .. c + 7 of this lane, of the pieces first, first + step,
+// ... below np of one row: base-2 max M of their log-sum-exps, the sum tot of their weights
+// 2^(lse - M) and the weighted sum acc of their values.
+template <int NB, typename LseF, typename PartF>
+__device__ __forceinline__ void merge_state(int np, int first, int step, LseF lse_of, PartF part_of, int c, int dc,
+                                            float& M, float& tot, float (&acc)[8]) {
+  M = -INFINITY;
+  tot = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) acc[k] = 0.f;
+  for (int s0 = first; s0 < np; s0 += NB * step) {
+    float ls[NB], v[NB][8];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int sj = min(s0 + j * step, np - 1);  // in range; surplus entries get weight 0
+      const float lj = lse_of(sj);
+      ls[j] = s0 + j * step < np ? lj : -INFINITY;
+      load8_f32(v[j], part_of(sj) + c, c, dc);
+    }
+    float bm = ls[0];
+#pragma unroll
+    for (int j = 1; j < NB; ++j) bm = fmaxf(bm, ls[j]);
+    const float Mn = fmaxf(M, bm);
+    if (Mn == -INFINITY) continue;  // nothing visible yet (uniform over the wave)
+    const float r = exp2f(M - Mn);  // 0 while M is still -inf
+    tot *= r;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] *= r;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const float w = exp2f(ls[j] - Mn);
+      tot += w;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[k] = fmaf(w, v[j][k], acc[k]);
+    }
+    M = Mn;
+  }
+}
+
+// Workgroups of 4 waves over (row group, sequence).  WPR waves share one row: wave g of a
+// row merges pieces g, g + WPR, g + 2 WPR, ..., then (WPR > 1) the row's first wave merges
+// their states from LDS.  WPR = 4 keeps four chains of loads in flight per row for
+// sequences cut into many pieces; WPR = 1 (a whole row per wave) suits few pieces.
+template <int WPR>
 __global__ __launch_bounds__(256) void combine_ranges_kernel(DecodeArgs a, int R) {
+  static_assert(WPR == 1 || WPR == kCombWaves, "one row per wave, or per workgroup");
+  __shared__ float sh_acc[WPR > 1 ? WPR : 1][8][64];
+  __shared__ float sh_m[WPR], sh_t[WPR];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rows = a.sq * a.H;
-  const int row = blockIdx.x * kCombRows + wave, b = blockIdx.y;
-  if (row >= rows) return;
+  const int g = wave % WPR;  // chain of this wave within its row
+  const int row = blockIdx.x * (kCombWaves / WPR) + wave / WPR, b = blockIdx.y;
+  if (row >= rows) return;  // WPR = 1 only (WPR = 4: one row per workgroup, all valid)
   const int64_t total = a.prefix[a.B], p0 = a.prefix[b], p1 = a.prefix[b + 1];
   uint16_t* o = static_cast<uint16_t*>(a.o_lat) + (int64_t(b) * rows + row) * a.dc;
   float* lse_out = a.lse ? a.lse + int64_t(b) * rows + row : nullptr;
   if (p1 == p0) {
-    for (int c = 8 * lane; c < a.dc; c += 512) *reinterpret_cast<uint4*>(o + c) = uint4{0u, 0u, 0u, 0u};
-    if (lane == 0 && lse_out) *lse_out = -INFINITY;
+    if (g == 0) {
+      for (int c = 8 * lane; c < a.dc; c += 512) *reinterpret_cast<uint4*>(o + c) = uint4{0u, 0u, 0u, 0u};
+      if (lane == 0 && lse_out) *lse_out = -INFINITY;
+    }
     return;
   }
   // Range arithmetic in 32 bits whenever every intermediate fits: total R and
@@ -346,10 +397,51 @@ __global__ __launch_bounds__(256) void combine_ranges_kernel(DecodeArgs a, int R
   auto lse_of = [&](int j) { return has_piece(j) ? a.part_lse[slot_of(j) * rows + row] : -INFINITY; };
   auto part_of = [&](int j) { return po + slot_of(j) * rows * a.dc; };
   const int np = w1 - w0 + 1;
-  if (np <= 4)
-    merge_row<BF16, BF16, true, 4>(a, np, lse_of, part_of, o, lse_out, lane);
-  else
-    merge_row<BF16, BF16, true>(a, np, lse_of, part_of, o, lse_out, lane);
+  for (int c0 = 0; c0 < a.dc; c0 += 512) {
+    const int c = c0 + 8 * lane;
+    float M, tot, acc[8];
+    if (np <= 4 * WPR)
+      merge_state<4>(np, g, WPR, lse_of, part_of, c, a.dc, M, tot, acc);
+    else
+      merge_state<kCombBatch>(np, g, WPR, lse_of, part_of, c, a.dc, M, tot, acc);
+    if constexpr (WPR > 1) {
+      if (g > 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sh_acc[g][k][lane] = acc[k];
+        if (lane == 0) {
+          sh_m[g] = M;
+          sh_t[g] = tot;
+        }
+      }
+      __syncthreads();
+    }
+    if (g == 0) {
+      float Mn = M;
+#pragma unroll
+      for (int q = 1; q < WPR; ++q) Mn = fmaxf(Mn, sh_m[q]);
+      float t = 0.f, x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+      if (Mn != -INFINITY) {
+#pragma unroll
+        for (int q = 0; q < WPR; ++q) {
+          const float mq = q == 0 ? M : sh_m[q];
+          const float wq = mq == -INFINITY ? 0.f : exp2f(mq - Mn);
+          t = fmaf(wq, q == 0 ? tot : sh_t[q], t);
+#pragma unroll
+          for (int k = 0; k < 8; ++k) x[k] = fmaf(wq, q == 0 ? acc[k] : sh_acc[q][k][lane], x[k]);
+        }
+      }
+      const float inv = t > 0.f ? 1.f / t : 0.f;
+      if (c < a.dc) {
+        uint32_t pk[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          pk[k] = uint32_t(f32_to_bf16_bits(x[2 * k] * inv)) | (uint32_t(f32_to_bf16_bits(x[2 * k + 1] * inv)) << 16);
+        *reinterpret_cast<uint4*>(o + c) = uint4{pk[0], pk[1], pk[2], pk[3]};
+      }
+      if (c0 == 0 && lane == 0 && lse_out) *lse_out = t > 0.f ? (Mn + log2f(t)) * kLn2 : -INFINITY;
+    }
+    if constexpr (WPR > 1) __syncthreads();  // the states are reused by the next 512 columns
+  }
 }
 
 // Exclusive prefix sum over the batch of each sequence's 32-token tile count (lengths
@@ -416,7 +508,12 @@ int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const bool vec = a.dc % 8 == 0;
   if (p.balanced) {
     if (!a.part_bf16 || a.q_dt != MLA_BF16 || !vec) return int(hipErrorInvalidValue);
-    hipLaunchKernelGGL(combine_ranges_kernel, grid, dim3(256), 0, s, a, p.num_splits);
+    // Four waves per row when the ranges cut the average sequence into 8 or more pieces.
+    if (p.num_splits >= 8 * a.B)
+      hipLaunchKernelGGL(combine_ranges_kernel<kCombWaves>, dim3(p.rows, a.B), dim3(64 * kCombWaves), 0, s, a,
+                         p.num_splits);
+    else
+      hipLaunchKernelGGL(combine_ranges_kernel<1>, grid, dim3(64 * kCombWaves), 0, s, a, p.num_splits);
     return int(hipGetLastError());
   }
   if (a.part_bf16) {

@@ -51,7 +51,6 @@ constexpr int kSlots = 4;                      // LDS ring of staged tiles
 constexpr int kAhead = 2;                      // tiles loaded ahead of the one being computed
 constexpr int kVPre = 5;                       // value-product operands read ahead of their product
 constexpr bool kLoadsInValue = true;           // tile loads issued between the value products
-constexpr bool kPingPong = false;              // waves 2, 3 run half a step behind waves 0, 1
 constexpr int kLatPitch = kDC * 2 + 64;        // bytes per staged latent row (1 KB + 64 B)
 constexpr int kLatSlot = kTile * kLatPitch;    // 34 KB of latent rows per slot
 constexpr int kRopeSlot = kTile * kDR * 2;     // 4 KB of RoPE rows per slot
@@ -392,9 +391,7 @@ __device__ __forceinline__ void decode_piece(SmemL& sm, const DecodeArgs& a, int
     else wait_vm<0>();
     barrier_lds();  // tile k staged by every wave; tile k - 1's slot is free
   };
-  // Trailing waves still read tile k - 1 in step k: the loads issued in step k must not reuse
-  // its slot.
-  static_assert(kAhead >= 1 && kAhead <= 3 && kAhead + (kPingPong ? 1 : 0) < kSlots, "tile pipeline depth");
+  static_assert(kAhead >= 1 && kAhead < kSlots, "tile pipeline depth");
   auto start = [&]() {
 #pragma unroll
     for (int k = 0; k < kAhead; ++k)
@@ -450,10 +447,10 @@ __device__ __forceinline__ void decode_piece(SmemL& sm, const DecodeArgs& a, int
     l_run = 0.f;
     rise = false;
     if (pass == 1) start();
-    if (active && (!kPingPong || w < 2)) {
-      // Leading waves: score, softmax and value product of tile k in step k.  Steps that
-      // still issue loads, then the last kAhead steps (separate loops, so that no branch
-      // inside the step merges two versions of the accumulators).
+    if (active) {
+      // Score, softmax and value product of tile k in step k.  Steps that still issue loads,
+      // then the last kAhead steps (separate loops, so that no branch inside the step merges
+      // two versions of the accumulators).
       int k = 0;
       for (; k + kAhead < ntiles; ++k) {
         step_sync(k);
@@ -468,27 +465,6 @@ __device__ __forceinline__ void decode_piece(SmemL& sm, const DecodeArgs& a, int
         softmax(k, score(k), pb);
         value(k, pb, -1);
       }
-    } else if (active) {
-      // Trailing waves (waves 2, 3): the value product of tile k - 1 first, then score and
-      // softmax of tile k, so that at any time two waves read score operands while two read
-      // value operands, and their loads are issued half a step apart from the leading waves'.
-      bf16x8 pb[2];
-      step_sync(0);
-      if (kAhead < ntiles) issue(kAhead);
-      softmax(0, score(0), pb);
-      int k = 1;
-      for (; k + kAhead < ntiles; ++k) {
-        step_sync(k);
-        if (!kLoadsInValue) issue(k + kAhead);
-        value(k - 1, pb, kLoadsInValue ? k + kAhead : -1);
-        softmax(k, score(k), pb);
-      }
-      for (; k < ntiles; ++k) {
-        step_sync(k);
-        value(k - 1, pb, -1);
-        softmax(k, score(k), pb);
-      }
-      value(ntiles - 1, pb, -1);
     } else {
       for (int k = 0; k < ntiles; ++k) {
         step_sync(k);

@@ -158,11 +158,14 @@ def test_absorb_q_and_out_v2_shapes():
     assert e_q <= TOL["bf16"] and e_o <= TOL["bf16"]
 
 
-def decode_stage_case(cfg, seed, lengths, split_tokens, poison=True, q_gain=1.0, fp8_scores=0):
+def decode_stage_case(cfg, seed, lengths, split_tokens, poison=True, q_gain=1.0, fp8_scores=0, edit=None):
     """mla_decode alone: both sides read the same stored q_lat (the oracle's q_lat rounded
-    to the stored dtype), so only the attention stage is compared."""
+    to the stored dtype), so only the attention stage is compared.  edit(inp), if given,
+    changes the stored inputs before either side reads them."""
     inp = synth.make_inputs(cfg, seed, lengths=np.array(lengths, np.int32), poison_tail=poison,
                             q_gain=q_gain)
+    if edit is not None:
+        edit(inp)
     d = decoded(inp)
     q_lat = O.absorb_query(d["q_nope"], d["w_uk"])
     q_bits = synth.store(q_lat.astype(np.float32), cfg.act_dtype)
@@ -188,10 +191,43 @@ def test_decode_stage_bf16_ragged(split_tokens, kern, monkeypatch):
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
 
 
-def test_decode_stage_peaked_scores():
+@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+def test_decode_stage_peaked_scores(kern, monkeypatch):
+    use_kernel(kern, monkeypatch)
     cfg = configs.V2_DECODE.with_(batch=2, seq_len=700, cfg_id=23)
     say("decode peaked", cfg)
     o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [700, 333], 128, q_gain=4.0)
+    e_o, e_l = max_rel_err(o, o_ref), max_abs_err(l, l_ref)
+    print(f"  o_lat {e_o:.2e} lse {e_l:.2e}")
+    assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kern", list(KERNELS))
+@pytest.mark.parametrize("split_tokens", [0, 2048])
+@pytest.mark.parametrize("gain", [8.0, 24.0])
+def test_decode_rising_scores(gain, split_tokens, kern, monkeypatch):
+    """Latent rows scaled up along the sequence (x1 at token 0 to x gain at the last), so
+    every row's scores rise far above the max of its first tile.  The 128-row kernel fixes
+    each row's reference at its first visible tile and reruns a piece against the true
+    maxima once a score rises more than 64 (base 2) above it: gain 24 takes that second
+    pass (rises of 49 to 125 on the single-piece split), gain 8 stays in the first pass with
+    probabilities up to 2^40.  Both must match the oracle."""
+    n_heads = use_kernel(kern, monkeypatch)
+    cfg = configs.V2_DECODE.with_(batch=2, seq_len=1500, cfg_id=31, n_heads=n_heads)
+    lengths = [1500, 900]
+
+    def scale_up(inp):
+        g = 1.0 + (gain - 1.0) * np.arange(cfg.seq_len) / (cfg.seq_len - 1)
+        inp.c_kv = synth.store((O.decode(inp.c_kv, "bf16") * g[None, :, None]).astype(np.float32), "bf16")
+
+    say("decode rising scores", gain, split_tokens, cfg)
+    o, l, o_ref, l_ref, inp, d, _ = decode_stage_case(cfg, 0, lengths, split_tokens, edit=scale_up)
+    # The rise the case is built for (first sequence, whole-sequence piece), in base 2.
+    q = O.absorb_query(d["q_nope"], d["w_uk"])[0].reshape(-1, cfg.d_latent)
+    s = (q @ d["c_kv"][0].T + d["q_rope"][0].reshape(-1, cfg.d_rope) @ d["k_rope"][0].T) * d["scale"] / np.log(2)
+    rise = (s.max(1) - s[:, :32].max(1)).max()
+    print(f"  largest rise above the first tile: {rise:.1f} (base 2)")
+    assert (rise > 64) == (gain > 10)
     e_o, e_l = max_rel_err(o, o_ref), max_abs_err(l, l_ref)
     print(f"  o_lat {e_o:.2e} lse {e_l:.2e}")
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
