@@ -372,6 +372,12 @@ def bench_projections(args, cfg) -> int:
              "uv": rnd(H, dc, dh, std=dc ** -0.5), "o": rnd(H * dh, dm, std=(H * dh) ** -0.5)}
         w["uqk"] = torch.empty(dcq, H * dc, dtype=torch.bfloat16, device="cuda")
         capi.mla_absorb_q(capi.dims(dcq, 1, H, dh, dc, dr, 1.0), w["uq"].view(dcq, 1, H, dh), w["uk"], w["uqk"])
+        w["uvo"] = torch.empty(H * dc, dm, dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        t_f = time.perf_counter()
+        capi.mla_fold_output_weights(w["uv"], w["o"], w["uvo"])
+        torch.cuda.synchronize()
+        fold_ms = (time.perf_counter() - t_f) * 1e3
         reps.append(w)
     c_q = torch.empty(M, dcq, dtype=torch.bfloat16, device="cuda")
     q_nope = torch.empty(M, H * dh, dtype=torch.bfloat16, device="cuda")
@@ -381,7 +387,7 @@ def bench_projections(args, cfg) -> int:
     heads = torch.empty(M, H * dh, dtype=torch.bfloat16, device="cuda")
     y = torch.empty(M, dm, dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(max(capi.mla_linear_workspace_bytes(M, K, N) for K, N in
-                         ((dm, dcq), (dcq, H * dh), (dcq, H * dr), (dcq, H * dc), (H * dh, dm))),
+                         ((dm, dcq), (dcq, H * dh), (dcq, H * dr), (dcq, H * dc), (H * dh, dm), (H * dc, dm))),
                      dtype=torch.uint8, device="cuda")
     dq = capi.dims(M, 1, H, dh, dc, dr, 1.0)
 
@@ -400,6 +406,9 @@ def bench_projections(args, cfg) -> int:
         capi.mla_absorb_out(dq, o_lat.view(M, 1, H, dc), w["uv"], heads.view(M, 1, H, dh))
         capi.mla_linear(heads, w["o"], y, ws)
 
+    def output_folded(w):
+        capi.mla_linear(o_lat, w["uvo"], y, ws)
+
     def timed(fn):
         for k in range(args.warmup):
             fn(reps[k % len(reps)])
@@ -416,14 +425,15 @@ def bench_projections(args, cfg) -> int:
     while (time.perf_counter() - t0) * 1e3 < args.ramp_ms:
         query_unfolded(reps[0])
         torch.cuda.synchronize()
-    ms_u, ms_f, ms_o = timed(query_unfolded), timed(query_folded), timed(output)
+    ms_u, ms_f, ms_o, ms_of = timed(query_unfolded), timed(query_folded), timed(output), timed(output_folded)
     b = lambda n: 2 * n
     bytes_u = b(dm * dcq + dcq * H * dh + dcq * H * dr + H * dh * dc)
     bytes_f = b(dm * dcq + dcq * H * dr + dcq * H * dc)
     bytes_o = b(H * dc * dh + H * dh * dm)
+    bytes_of = b(H * dc * dm)
     gbs = lambda nb, ms: nb / (ms * 1e-3) / 1e9
-    print(f"[bench] query unfolded {ms_u * 1e3:.1f} us, folded {ms_f * 1e3:.1f} us, output {ms_o * 1e3:.1f} us",
-          file=sys.stderr, flush=True)
+    print(f"[bench] query unfolded {ms_u * 1e3:.1f} us, folded {ms_f * 1e3:.1f} us, output {ms_o * 1e3:.1f} us, "
+          f"output folded {ms_of * 1e3:.1f} us (fold {fold_ms:.2f} ms, once per weight set)", file=sys.stderr, flush=True)
     ach = gbs(bytes_u, ms_u)
     print(json.dumps({
         "metric": "MLA query path from hidden states (unfolded), weight GB/s", "value": round(ach, 1),
@@ -437,6 +447,8 @@ def bench_projections(args, cfg) -> int:
         "query_folded_us": round(ms_f * 1e3, 2), "query_folded_weight_MB": round(bytes_f / 1e6, 1),
         "output_us": round(ms_o * 1e3, 2), "output_weight_MB": round(bytes_o / 1e6, 1),
         "output_GBs": round(gbs(bytes_o, ms_o), 1), "query_folded_GBs": round(gbs(bytes_f, ms_f), 1),
+        "output_folded_us": round(ms_of * 1e3, 2), "output_folded_weight_MB": round(bytes_of / 1e6, 1),
+        "output_folded_GBs": round(gbs(bytes_of, ms_of), 1), "output_fold_ms_once": round(fold_ms, 3),
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
     }), flush=True)

@@ -100,8 +100,10 @@ typedef struct {
  *   - every shape with all tensors MLA_F32, and with activations / weights in MLA_BF16
  *     and the latent cache in MLA_BF16 or MLA_FP8_E4M3 (general kernels);
  *   - d_c = 512, d_r = 64, activations MLA_BF16, cache MLA_BF16 or MLA_FP8_E4M3,
- *     s_q * n_h a multiple of 64, and one sequence's cache rows spanning less than 2 GiB
- *     (max_seq_len * 512 * bytes per code < 2^31): the matrix-core (MFMA) decode kernel.
+ *     s_q * n_h a multiple of 64 (for a bf16 cache, of 32), and one sequence's cache rows
+ *     spanning less than 2 GiB (max_seq_len * 512 * bytes per code < 2^31): the
+ *     matrix-core (MFMA) decode kernels, with row blocks of 64 query rows, or for a bf16
+ *     cache of 128 (see mla_decode_plan for which).
  * Limits of every kernel: d_c <= 2048, d_r <= 512, s_q * n_h <= 65536, batch <= 65535,
  * n_heads <= 65535; a decode call uses at most 8192 context splits (an explicit
  * split_tokens that would need more returns MLA_ERR_UNSUPPORTED). */
@@ -280,6 +282,20 @@ mla_status mla_prefill(const mla_dims* dims, const void* q_nope, const void* q_r
  * workspace (at least mla_linear_workspace_bytes(M, K, N) bytes, 16-byte aligned) holds
  * the fp32 partial sums of the 256-wide slices of K; contents irrelevant on entry. */
 size_t mla_linear_workspace_bytes(int32_t M, int32_t K, int32_t N);
+
+/* ---- output-side fold ----------------------------------------------------------------
+ * w_uvo[h, c, :] = sum_j w_uv[h, c, j] * w_o[h * d_h + j, :]   (fp32 accumulation, bf16 out)
+ *   w_uv  [n_h, d_c, d_h]       MLA_BF16 (the per-head layout mla_absorb_out takes)
+ *   w_o   [n_h * d_h, d_model]  MLA_BF16 (the output projection W_O, row-major)
+ *   w_uvo [n_h, d_c, d_model]   MLA_BF16
+ * The value up-projection merged into the output projection ("Operator Notes (1): MLA",
+ * sections 2 and 4; the glossary's paragraph on the decoupled RoPE key): afterwards
+ * mla_linear(o_lat viewed as [M, n_h * d_c], w_uvo viewed as [n_h * d_c, d_model]) gives the
+ * layer output O W_O without forming the per-head outputs O.  Run once per weight set.
+ * d_h must be 128 or 512, d_model a multiple of 64, d_c <= 32 * 65535, dt MLA_BF16 (else
+ * MLA_ERR_UNSUPPORTED); pointers 16-byte aligned (else MLA_ERR_INVALID_ARG). */
+mla_status mla_fold_output_weights(const void* w_uv, const void* w_o, void* w_uvo, int32_t n_h, int32_t d_c,
+                                   int32_t d_h, int32_t d_model, mla_dtype dt, void* stream);
 mla_status mla_linear(const void* x, const void* w, void* y, int32_t M, int32_t K, int32_t N, mla_dtype dt,
                       void* workspace, size_t workspace_bytes, void* stream);
 

@@ -30,7 +30,7 @@ EXPORTED = (
     "mla_decode_plan", "mla_absorb_out", "mla_gather_pages", "mla_fp8_e4m3_table",
     "mla_status_str", "mla_last_hip_error", "mla_version", "mla_cache_append_workspace_bytes",
     "mla_cache_append", "mla_rope_query", "mla_prefill_workspace_bytes", "mla_prefill",
-    "mla_linear_workspace_bytes", "mla_linear", "mla_decode_noalloc",
+    "mla_linear_workspace_bytes", "mla_linear", "mla_decode_noalloc", "mla_fold_output_weights",
 )
 
 # Size of the static device array mla_decode_noalloc keeps its partial results in.
@@ -90,6 +90,7 @@ _SIGNATURES = {
     "mla_prefill_workspace_bytes": [_dims_p, _i32],
     "mla_linear_workspace_bytes": [_i32, _i32, _i32],
     "mla_linear": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp],
+    "mla_fold_output_weights": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
     "mla_prefill": [_dims_p, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
     "mla_status_str": [_i32],
     "mla_last_hip_error": [],
@@ -335,6 +336,19 @@ def mla_linear(x, w, y, workspace, *, M=None, K=None, N=None, workspace_bytes=No
     st = _lib().mla_linear(_ptr(x), _ptr(w), _ptr(y), M, K, N, _dt(x, dtype), _ptr(workspace),
                            workspace_bytes, _stream(stream))
     return _done(st, "mla_linear", check)
+
+
+def mla_fold_output_weights(w_uv, w_o, w_uvo, *, n_h=None, d_c=None, d_h=None, d_model=None, dtype=None,
+                            stream=None, check=True) -> int:
+    """w_uvo[h] = w_uv[h] . w_o[h d_h : (h + 1) d_h] for w_uv [n_h, d_c, d_h], w_o [n_h d_h,
+    d_model], w_uvo [n_h, d_c, d_model] (argument marshalling only)."""
+    if n_h is None:
+        n_h, d_c, d_h = w_uv.shape
+    if d_model is None:
+        d_model = w_o.shape[1]
+    st = _lib().mla_fold_output_weights(_ptr(w_uv), _ptr(w_o), _ptr(w_uvo), n_h, d_c, d_h, d_model,
+                                        _dt(w_uv, dtype), _stream(stream))
+    return _done(st, "mla_fold_output_weights", check)
 
 
 def mla_fp8_e4m3_table(out, *, stream=None, check=True) -> int:

@@ -20,16 +20,26 @@ namespace {
 constexpr int kBN = 64;      // output columns per workgroup (one 16-column block per wave)
 constexpr int kThreads = 256;
 
+struct Strides {
+  int64_t m, h;
+};
+constexpr Strides kPacked{-1, 0};
+
 // Activation rows in LDS: row r's 8-column chunk c is stored at chunk c ^ (r & 15), so the
 // 16 rows of one B-operand read hit distinct banks.
 __device__ __forceinline__ int xswz(int r) { return r & 15; }
 
 // Grid (H, N / 64, ceil(M / MG)): one workgroup per (head, 64-column tile, MG-row group).
 // Every load of the workgroup (its MG activation rows and the K x 64 weight slice) is issued
-// before the first wait, so a workgroup costs one memory latency.  Workgroup ids are dealt
-// to the 8 XCDs round-robin, and the head is the fastest grid dimension: with H a multiple
-// of 8, all column tiles (and row groups) of one head run on one XCD and share its
-// activation rows (and weight slice) through that XCD's L2.
+// before the first wait, so a workgroup costs one memory latency.  Workgroups are dealt to
+// the n_xcd XCDs round-robin in launch order; when H is a multiple of n_xcd the launch index
+// is remapped so that XCD x takes the heads h = x (mod n_xcd) and runs, head after head and
+// column tile after column tile, all row groups of one (head, tile) back to back: the tile's
+// weight slice and the head's activation rows are then read from HBM once and reused from
+// that XCD's L2 (with the head as the fastest index instead, the row groups of one weight
+// slice are spread over the whole launch and each refetches it).
+// Element strides: x[m, h, :] starts at m x_st.m + h x_st.h and y[m, h, :] at m y_st.m +
+// h y_st.h (a negative .m selects the packed layouts [M, H, K] / [M, H, N]).
 // F32OUT: y holds fp32 sums (the split-K partials of the cache-write projection) instead of
 // bf16 results.  Column tiles from N / 64 on take a second weight matrix w2 [H, K, N2] and
 // output y2 [M, H, N2] (N2 a multiple of 64; the grid then has N / 64 + N2 / 64 column tiles).
@@ -38,18 +48,29 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
                                                                const uint16_t* __restrict__ w,
                                                                void* __restrict__ y, int M,
                                                                int H, int N,
+                                                               int n_xcd, Strides x_st, Strides y_st,
                                                                const uint16_t* __restrict__ w2 = nullptr,
                                                                void* __restrict__ y2 = nullptr, int N2 = 0) {
   constexpr int kBlocks = MG / 16;
   __shared__ __attribute__((aligned(16))) uint16_t wt[K * kBN];  // [k][64], chunks swizzled
   __shared__ __attribute__((aligned(16))) uint16_t xs[MG * K];   // [row][k], chunks swizzled
   int h = blockIdx.x, n0 = blockIdx.y * kBN, m0 = blockIdx.z * MG;
+  if (n_xcd > 1 && int(gridDim.x) % n_xcd == 0) {
+    const int ncol = int(gridDim.y), nrg = int(gridDim.z);
+    const int id = int(blockIdx.x) + int(gridDim.x) * (int(blockIdx.y) + ncol * int(blockIdx.z));
+    const int j = id / n_xcd;  // position within this XCD's share
+    h = (j / (ncol * nrg)) * n_xcd + id % n_xcd;
+    n0 = ((j / nrg) % ncol) * kBN;
+    m0 = (j % nrg) * MG;
+  }
   if (n0 >= N) {  // a tile of the second matrix (workgroup-uniform)
     n0 -= N;
     w = w2;
     y = y2;
     N = N2;
   }
+  const int64_t x_m = x_st.m >= 0 ? x_st.m : int64_t(H) * K, x_h = x_st.m >= 0 ? x_st.h : K;
+  const int64_t y_m = y_st.m >= 0 ? y_st.m : int64_t(H) * N, y_h = y_st.m >= 0 ? y_st.h : N;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane >> 4, mm = lane & 15;
 
@@ -61,7 +82,7 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
 #pragma unroll
   for (int i = 0; i < kXPer; ++i) {
     const int idx = tid + i * kThreads, r = idx / (K / 8), ch = idx % (K / 8);
-    xr[i] = ld16(x + (int64_t(min(m0 + r, M - 1)) * H + h) * K + 8 * ch);
+    xr[i] = ld16(x + int64_t(min(m0 + r, M - 1)) * x_m + h * x_h + 8 * ch);
   }
   const uint16_t* wh = w + int64_t(h) * K * N + n0;
   u32x4 wr[kPer];
@@ -105,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
     for (int i = 0; i < kBlocks; ++i) {
       const int m = m0 + 16 * i + mm;
       if (m < M)
-        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + (int64_t(m) * H + h) * N + n0 + 16 * wv + 4 * g) = acc[i];
+        *reinterpret_cast<f32x4*>(static_cast<float*>(y) + int64_t(m) * y_m + h * y_h + n0 + 16 * wv + 4 * g) = acc[i];
     }
   } else {
     // The MG x 64 bf16 result goes through LDS (in the activation buffer, once every wave is
@@ -125,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
     for (int r = tid >> 3; r < MG; r += kRowsPerPass) {
       const int c = tid & 7, m = m0 + r;
       if (m < M)
-        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + (int64_t(m) * H + h) * N + n0 + 8 * c) =
+        *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + int64_t(m) * y_m + h * y_h + n0 + 8 * c) =
             *reinterpret_cast<const u32x4*>(&ys[r * kBN + 8 * (c ^ ((r >> 1) & 7))]);
     }
   }
@@ -143,9 +164,11 @@ bool proj_mfma_supported(int32_t M, int32_t K_total, int32_t N) {
 int launch_proj_mfma(const void* x, const void* w, float* part, int32_t N, const void* w2, float* part2,
                      int32_t N2, int32_t M, int32_t K_total, hipStream_t s) {
   const int KC = K_total / 256;
+  int cus = kDefaultCUs, n_xcd = kDefaultXcds;
+  device_topology(&cus, &n_xcd);
   hipLaunchKernelGGL((absorb_mfma_kernel<256, 32, true>), dim3(KC, (N + N2) / kBN, (M + 31) / 32), dim3(kThreads),
-                     0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), part, M, KC, N,
-                     static_cast<const uint16_t*>(w2), part2, N2);
+                     0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), part, M, KC, N, n_xcd,
+                     kPacked, kPacked, static_cast<const uint16_t*>(w2), part2, N2);
   return int(hipGetLastError());
 }
 
@@ -154,18 +177,36 @@ bool absorb_mfma_supported(mla_dtype dt, int32_t M, int32_t K, int32_t N) {
   return dt == MLA_BF16 && (K == 128 || K == 512) && N % kBN == 0 && M <= 32 * 65535;
 }
 
-int launch_absorb_mfma(const void* x, const void* w, void* y, int32_t M, int32_t H, int32_t K,
-                       int32_t N, hipStream_t s) {
+namespace {
+int launch_absorb_t(const void* x, const void* w, void* y, int32_t M, int32_t H, int32_t K, int32_t N, Strides x_st,
+                    Strides y_st, hipStream_t s) {
   const auto* xp = static_cast<const uint16_t*>(x);
   const auto* wp = static_cast<const uint16_t*>(w);
   auto* yp = static_cast<uint16_t*>(y);
+  int cus = kDefaultCUs, n_xcd = kDefaultXcds;
+  device_topology(&cus, &n_xcd);
   if (K == 128)
     hipLaunchKernelGGL((absorb_mfma_kernel<128, 32>), dim3(H, N / kBN, (M + 31) / 32), dim3(kThreads), 0, s,
-                       xp, wp, yp, M, H, N);
+                       xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
   else
     hipLaunchKernelGGL((absorb_mfma_kernel<512, 32>), dim3(H, N / kBN, (M + 31) / 32), dim3(kThreads), 0, s,
-                       xp, wp, yp, M, H, N);
+                       xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
   return int(hipGetLastError());
+}
+}  // namespace
+
+int launch_absorb_mfma(const void* x, const void* w, void* y, int32_t M, int32_t H, int32_t K,
+                       int32_t N, hipStream_t s) {
+  return launch_absorb_t(x, w, y, M, H, K, N, kPacked, kPacked, s);
+}
+
+// w_uvo[h, c, :] = w_uv[h, c, :] . w_o[h d_h .. h d_h + d_h, :]: the per-head product with the
+// d_c rows c of w_uv[h] as its rows (x[c, h, :] at c d_h + h d_c d_h), w_o viewed as
+// [n_h, d_h, d_model], and the result stored head-major (y[c, h, :] at c d_model + h d_c d_model).
+int launch_fold_output(const void* w_uv, const void* w_o, void* w_uvo, int32_t n_h, int32_t d_c, int32_t d_h,
+                       int32_t d_model, hipStream_t s) {
+  return launch_absorb_t(w_uv, w_o, w_uvo, d_c, n_h, d_h, d_model, Strides{d_h, int64_t(d_c) * d_h},
+                         Strides{d_model, int64_t(d_c) * d_model}, s);
 }
 
 }  // namespace mla

@@ -585,15 +585,18 @@ __device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a,
 // sequence that lies wholly inside the range is a final piece, the range's cut first and
 // last sequences write partials to the range's slots 0 and 1 (slot 0 when one sequence
 // covers the whole range).
+// Launch bounds: 512 threads and at least 2 waves per SIMD (HIP's second argument counts
+// waves per SIMD), i.e. one 8-wave workgroup per compute unit, which is what the kernel's
+// 124 KB of LDS allows; each wave may then hold up to 256 registers.
 template <bool FP8, int PK, bool QK8>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, int num_splits,
-                                                                  int chunk, int rblocks, int n_units) {
+                                                                  int chunk, int rblocks, int n_units, int n_xcd) {
   __shared__ Smem<QK8> sm;
 
-  // Workgroups are handed to the 8 XCDs round-robin by id; give each XCD a contiguous
+  // Workgroups are handed to the n_xcd XCDs round-robin by id; give each XCD a contiguous
   // range of work units so that the row blocks of one piece share an L2.
-  const int per_xcd = gridDim.x / 8;
-  const int unit = (blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  const int per_xcd = int(gridDim.x) / n_xcd;
+  const int unit = (int(blockIdx.x) % n_xcd) * per_xcd + int(blockIdx.x) / n_xcd;
   if (unit >= n_units) return;
   const int rb = unit % rblocks;
   const int rows = a.sq * a.H;
@@ -696,9 +699,10 @@ template <bool FP8, int PK, bool QK8 = false>
 int launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const int rblocks = p.rows / kRows;
   const int n_units = p.balanced ? p.num_splits * rblocks : a.B * p.num_splits * rblocks;
-  const int grid = (n_units + 7) / 8 * 8;
+  const int n_xcd = p.n_xcd > 0 ? p.n_xcd : 1;
+  const int grid = (n_units + n_xcd - 1) / n_xcd * n_xcd;
   hipLaunchKernelGGL((decode_mfma_kernel<FP8, PK, QK8>), dim3(grid), dim3(kThreads), 0, s, a,
-                     p.num_splits, p.split_tokens, rblocks, n_units);
+                     p.num_splits, p.split_tokens, rblocks, n_units, n_xcd);
   return int(hipGetLastError());
 }
 

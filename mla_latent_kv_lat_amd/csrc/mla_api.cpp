@@ -408,6 +408,15 @@ mla_status mla_linear(const void* x, const void* w, void* y, int32_t M, int32_t 
                                   static_cast<hipStream_t>(stream)));
 }
 
+mla_status mla_fold_output_weights(const void* w_uv, const void* w_o, void* w_uvo, int32_t n_h, int32_t d_c,
+                                   int32_t d_h, int32_t d_model, mla_dtype dt, void* stream) {
+  if (n_h < 1 || d_c < 1 || d_h < 1 || d_model < 1) return MLA_ERR_INVALID_ARG;
+  if (dt != MLA_BF16 || !absorb_mfma_supported(dt, d_c, d_h, d_model)) return MLA_ERR_UNSUPPORTED;
+  if (!w_uv || !w_o || !w_uvo) return MLA_ERR_INVALID_ARG;
+  if (!aligned(w_uv, 16) || !aligned(w_o, 16) || !aligned(w_uvo, 16)) return MLA_ERR_INVALID_ARG;
+  return hip_status(launch_fold_output(w_uv, w_o, w_uvo, n_h, d_c, d_h, d_model, static_cast<hipStream_t>(stream)));
+}
+
 size_t mla_prefill_workspace_bytes(const mla_dims* d, int32_t T) {
   if (check_prefill(d, T, MLA_BF16) != MLA_OK) return 0;
   return prefill_workspace_bytes(d->batch, T, d->n_heads);

@@ -134,6 +134,8 @@ constexpr int kMaxInKernelPrefixBatch = 1024;  // batches up to this size skip t
 int launch_absorb(const void* x, const void* w, void* y, mla_dtype dt, int32_t M, int32_t H,
                   int32_t K, int32_t N, hipStream_t s);
 bool absorb_mfma_supported(mla_dtype dt, int32_t M, int32_t K, int32_t N);
+int launch_fold_output(const void* w_uv, const void* w_o, void* w_uvo, int32_t n_h, int32_t d_c, int32_t d_h,
+                       int32_t d_model, hipStream_t s);
 int launch_absorb_mfma(const void* x, const void* w, void* y, int32_t M, int32_t H, int32_t K,
                        int32_t N, hipStream_t s);
 int launch_gather_pages(const void* pool, int32_t block_size, int64_t row_bytes,

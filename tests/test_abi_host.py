@@ -401,3 +401,16 @@ def test_noalloc_scratch_holds_every_full_size_plan(rows, monkeypatch):
     for cfg in (configs.V2_DECODE, configs.PAGED_VARLEN, configs.LONG_CONTEXT, configs.SPEC_FP8):
         ws = L.mla_decode_workspace_bytes(L.dims_from_config(cfg), cfg.kv_dtype, cfg.seq_len)
         assert 0 < ws <= L.NOALLOC_SCRATCH_BYTES, (cfg.name, rows, ws)
+
+
+def test_fold_output_weights_validates_before_any_hip_call():
+    """mla_fold_output_weights rejects unsupported shapes and dtypes, null and misaligned
+    pointers without touching the device."""
+    f = L._lib().mla_fold_output_weights
+    bf, f32 = L.MLA_BF16, L.MLA_F32
+    assert f(A, A, A, 128, 512, 128, 5120, f32, None) == L.MLA_ERR_UNSUPPORTED
+    assert f(A, A, A, 128, 512, 64, 5120, bf, None) == L.MLA_ERR_UNSUPPORTED   # d_h not 128 / 512
+    assert f(A, A, A, 128, 512, 128, 5000, bf, None) == L.MLA_ERR_UNSUPPORTED  # d_model % 64
+    assert f(None, A, A, 128, 512, 128, 5120, bf, None) == L.MLA_ERR_INVALID_ARG
+    assert f(A + 2, A, A, 128, 512, 128, 5120, bf, None) == L.MLA_ERR_INVALID_ARG
+    assert f(A, A, A, 0, 512, 128, 5120, bf, None) == L.MLA_ERR_INVALID_ARG

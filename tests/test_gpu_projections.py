@@ -133,3 +133,27 @@ def test_output_projection():
     err = max_rel_err(to_host_f64(y), ref)
     print(f"  max rel err {err:.2e}", flush=True)
     assert err <= TOL
+
+
+def test_output_path_folded():
+    """out = o_lat (viewed as [M, n_h d_c]) . W_UVO, where W_UVO[h] = W_UV[h] . W_O[h d_h :
+    (h + 1) d_h] is formed on the device by mla_fold_output_weights: the fold against the
+    oracle's (sampled heads), and the folded output path against the oracle's unfolded
+    one (value absorption, then O W_O, in fp64)."""
+    s = DS
+    say("output path, folded", s)
+    M, n_h, d_h, d_c, d_model = s["M"], s["n_h"], s["d_h"], s["d_c"], s["d_model"]
+    o_lat = bf16(gaussian(10, (M, n_h, d_c)))
+    w_uv = bf16(gaussian(11, (n_h, d_c, d_h), d_c ** -0.5))
+    w_o = bf16(gaussian(12, (n_h * d_h, d_model), (n_h * d_h) ** -0.5))
+    w_uvo = torch.empty(n_h, d_c, d_model, dtype=torch.bfloat16, device="cuda")
+    capi.mla_fold_output_weights(dev(w_uv), dev(w_o), w_uvo)
+    y = linear(dev(o_lat).view(M, n_h * d_c), w_uvo.view(n_h * d_c, d_model))
+    torch.cuda.synchronize()
+    hs = [0, 77, 127]  # the fold is checked on sampled heads (the oracle's product is slow)
+    ref_fold = O.fold_output_weights(w_uv[hs], w_o.reshape(n_h, d_h, d_model)[hs].reshape(-1, d_model))
+    errs = {"w_uvo": max_rel_err(to_host_f64(w_uvo[hs]), ref_fold),
+            "out": max_rel_err(to_host_f64(y), O.output_projection(O.absorb_output(o_lat[:, None], w_uv)[:, 0], w_o))}
+    print("  " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()), flush=True)
+    for k, v in errs.items():
+        assert v <= TOL, k
