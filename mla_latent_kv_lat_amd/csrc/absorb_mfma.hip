@@ -20,6 +20,8 @@ namespace {
 constexpr int kBN = 64;      // output columns per workgroup (one 16-column block per wave)
 constexpr int kThreads = 256;
 
+constexpr int kTallRows = 128;  // rows per workgroup of the K = 128 product when M >= 128 (64 for K = 512)
+
 struct Strides {
   int64_t m, h;
 };
@@ -102,24 +104,20 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
     *reinterpret_cast<u32x4*>(&wt[k * kBN + 8 * (ch ^ swz128(k))]) = wr[i];
   }
   __syncthreads();
-  // B operands: rows 16 i + mm, columns 32 s + 8 g + (0..7).
-  bf16x8 bv[kBlocks][K / 32];
-#pragma unroll
-  for (int i = 0; i < kBlocks; ++i)
-#pragma unroll
-    for (int s2 = 0; s2 < K / 32; ++s2) {
-      const int r = 16 * i + mm;
-      bv[i][s2] = *reinterpret_cast<const bf16x8*>(&xs[r * K + 8 * ((4 * s2 + g) ^ xswz(r))]);
-    }
-
+  // Per k-step s: the weight operand (A, read transposed) once, then the B operands of every
+  // row block (rows 16 i + mm, columns 32 s + 8 g + (0..7)).
   f32x4 acc[kBlocks];
 #pragma unroll
-  for (int i = 0; i < kBlocks; ++i) {
-    acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kBlocks; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < K / 32; ++s)
-      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lds_operand_tr(wt, 32 * s, 16 * wv, lane), bv[i][s],
-                                                       acc[i], 0, 0, 0);
+  for (int s = 0; s < K / 32; ++s) {
+    const bf16x8 av = lds_operand_tr(wt, 32 * s, 16 * wv, lane);
+#pragma unroll
+    for (int i = 0; i < kBlocks; ++i) {
+      const int r = 16 * i + mm;
+      const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&xs[r * K + 8 * ((4 * s + g) ^ xswz(r))]);
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+    }
   }
   if constexpr (F32OUT) {
 #pragma unroll
@@ -185,8 +183,14 @@ int launch_absorb_t(const void* x, const void* w, void* y, int32_t M, int32_t H,
   auto* yp = static_cast<uint16_t*>(y);
   int cus = kDefaultCUs, n_xcd = kDefaultXcds;
   device_topology(&cus, &n_xcd);
-  if (K == 128)
+  if (K == 128 && M >= kTallRows)
+    hipLaunchKernelGGL((absorb_mfma_kernel<128, kTallRows>), dim3(H, N / kBN, (M + kTallRows - 1) / kTallRows),
+                       dim3(kThreads), 0, s, xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
+  else if (K == 128)
     hipLaunchKernelGGL((absorb_mfma_kernel<128, 32>), dim3(H, N / kBN, (M + 31) / 32), dim3(kThreads), 0, s,
+                       xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
+  else if (M >= 64)
+    hipLaunchKernelGGL((absorb_mfma_kernel<512, 64>), dim3(H, N / kBN, (M + 63) / 64), dim3(kThreads), 0, s,
                        xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
   else
     hipLaunchKernelGGL((absorb_mfma_kernel<512, 32>), dim3(H, N / kBN, (M + 31) / 32), dim3(kThreads), 0, s,
