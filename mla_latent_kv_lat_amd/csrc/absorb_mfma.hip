@@ -152,21 +152,28 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
 
 }  // namespace
 
-bool proj_mfma_supported(int32_t M, int32_t K_total, int32_t N) {
-  return K_total % 256 == 0 && N % kBN == 0 && M <= 32 * 65535;
+bool proj_mfma_supported(int32_t M, int32_t K_total, int32_t N, int32_t kchunk) {
+  return (kchunk == 128 || kchunk == 256) && K_total % kchunk == 0 && N % kBN == 0 && M <= 32 * 65535;
 }
 
-// part[m, kc, n] = sum_{k < 256} x[m, 256 kc + k] * w[256 kc + k, n] (and part2 likewise
-// with w2, N2 columns; N2 may be 0): the per-head kernel with the K chunks of x and w taken
-// as the heads, fp32 out, both matrices in one launch.
+// part[m, kc, n] = sum_{k < kchunk} x[m, kchunk kc + k] * w[kchunk kc + k, n] (and part2
+// likewise with w2, N2 columns; N2 may be 0): the per-head kernel with the K chunks of x and w
+// taken as the heads, fp32 out, both matrices in one launch.
 int launch_proj_mfma(const void* x, const void* w, float* part, int32_t N, const void* w2, float* part2,
-                     int32_t N2, int32_t M, int32_t K_total, hipStream_t s) {
-  const int KC = K_total / 256;
+                     int32_t N2, int32_t M, int32_t K_total, int32_t kchunk, hipStream_t s) {
+  const int KC = K_total / kchunk;
   int cus = kDefaultCUs, n_xcd = kDefaultXcds;
   device_topology(&cus, &n_xcd);
-  hipLaunchKernelGGL((absorb_mfma_kernel<256, 32, true>), dim3(KC, (N + N2) / kBN, (M + 31) / 32), dim3(kThreads),
-                     0, s, static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(w), part, M, KC, N, n_xcd,
-                     kPacked, kPacked, static_cast<const uint16_t*>(w2), part2, N2);
+  const dim3 grid(KC, (N + N2) / kBN, (M + 31) / 32);
+  const auto* xp = static_cast<const uint16_t*>(x);
+  const auto* wp = static_cast<const uint16_t*>(w);
+  const auto* w2p = static_cast<const uint16_t*>(w2);
+  if (kchunk == 128)
+    hipLaunchKernelGGL((absorb_mfma_kernel<128, 32, true>), grid, dim3(kThreads), 0, s, xp, wp, part, M, KC, N,
+                       n_xcd, kPacked, kPacked, w2p, part2, N2);
+  else
+    hipLaunchKernelGGL((absorb_mfma_kernel<256, 32, true>), grid, dim3(kThreads), 0, s, xp, wp, part, M, KC, N,
+                       n_xcd, kPacked, kPacked, w2p, part2, N2);
   return int(hipGetLastError());
 }
 

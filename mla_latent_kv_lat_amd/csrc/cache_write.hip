@@ -84,10 +84,23 @@ __device__ __forceinline__ void rope_pair(int j, int dr, int pairing, int& ia, i
   }
 }
 
-// One workgroup per new token, one thread per output column: sum the split-K partials
-// (loaded 16 chunks at a time, so the loads of a batch are in flight together), rotate the
-// key, encode the latent and write both to the token's pool row.
-constexpr int kFinBatch = 16;
+// Two workgroups per new token (grid y): y = 0 sums the latent's split-K partials (one
+// thread per column, every chunk's load in flight at once), encodes the row and writes it
+// to the token's pool row; y = 1 does the same for the RoPE key and rotates it, its angle
+// (double-precision arithmetic) computed while its partial loads are in flight.
+constexpr int kFinBatch = 32;  // split-K chunks summed per batch of loads (d_model 5120: 20 chunks)
+
+__device__ __forceinline__ float sum_chunks(const float* src, int stride, int KC) {
+  float s = 0.f;
+  for (int k0 = 0; k0 < KC; k0 += kFinBatch) {
+    float v[kFinBatch];
+#pragma unroll
+    for (int k = 0; k < kFinBatch; ++k) v[k] = k0 + k < KC ? src[int64_t(k0 + k) * stride] : 0.f;
+#pragma unroll
+    for (int k = 0; k < kFinBatch; ++k) s += v[k];
+  }
+  return s;
+}
 
 template <typename XS, typename KVS>
 __global__ __launch_bounds__(1024) void append_finalize_kernel(const float* __restrict__ part_c,
@@ -96,62 +109,115 @@ __global__ __launch_bounds__(1024) void append_finalize_kernel(const float* __re
                                                                void* c_pool, float* scale_pool, void* rope_pool,
                                                                int bs, const int32_t* __restrict__ table,
                                                                int max_blocks, const int32_t* __restrict__ seq_lens) {
-  extern __shared__ float rowv[];  // [d_c + d_r], then one slot per wave for the max
-  float* red = rowv + dc + dr;
+  extern __shared__ float rowv[];  // latent: one slot per wave for the max; key: its d_r sums
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nwaves = blockDim.x >> 6;
   const int b = m / sq, i = m - b * sq;
-  const int pos = seq_lens[b] - sq + i;
-  if (pos < 0) return;  // a sequence shorter than its new tokens: nothing to place (uniform per workgroup)
-  const int64_t prow = int64_t(table[int64_t(b) * max_blocks + pos / bs]) * bs + pos % bs;
-  const int N = dc + dr;
-  float amax = 0.f;
-  for (int n = tid; n < N; n += blockDim.x) {
-    const float* src = n < dc ? part_c + int64_t(m) * KC * dc + n : part_r + int64_t(m) * KC * dr + (n - dc);
-    const int stride = n < dc ? dc : dr;
-    float s = 0.f;
-    for (int k0 = 0; k0 < KC; k0 += kFinBatch) {
-      float v[kFinBatch];
+  // The token's pool row (a length load, then a block-table load) is looked up while the
+  // partial sums' loads are in flight; a sequence shorter than its new tokens (pos < 0) is
+  // skipped after them (uniform per workgroup, before any barrier or store).
+  auto pool_row = [&](int& pos) {
+    pos = seq_lens[b] - sq + i;
+    return pos < 0 ? int64_t(-1) : int64_t(table[int64_t(b) * max_blocks + pos / bs]) * bs + pos % bs;
+  };
+  if (blockIdx.y == 1) {
+    // RoPE key: thread n owns column n (threads past d_r only take part in the barrier).
+    const bool own = tid < dr;
+    const int n = own ? tid : 0;
+    float c = 1.f, sn = 0.f;
+    int partner = n;
+    bool first = true;
+    const float* src = part_r + int64_t(m) * KC * dr + n;
+    float v[kFinBatch];
+    const bool one_batch = KC <= kFinBatch;
+    if (one_batch) {
 #pragma unroll
-      for (int k = 0; k < kFinBatch; ++k) v[k] = k0 + k < KC ? src[int64_t(min(k0 + k, KC - 1)) * stride] : 0.f;
+      for (int k = 0; k < kFinBatch; ++k) v[k] = own && k < KC ? src[int64_t(k) * dr] : 0.f;
+    }
+    int pos;
+    const int64_t prow = pool_row(pos);
+    if (pos < 0) return;
+    if (own) {
+      // Pair j of the rotation holds elements ia, ib; this column is one of them.
+      const int j = pairing == MLA_ROPE_INTERLEAVED ? n / 2 : (n < dr / 2 ? n : n - dr / 2);
+      int ia, ib;
+      rope_pair(j, dr, pairing, ia, ib);
+      first = n == ia;
+      partner = first ? ib : ia;
+      rope_angle(pos, j, dr, base, c, sn);
+    }
+    float s = 0.f;
+    if (one_batch) {
 #pragma unroll
       for (int k = 0; k < kFinBatch; ++k) s += v[k];
+    } else if (own) {
+      s = sum_chunks(src, dr, KC);
     }
-    rowv[n] = s;
-    if (n < dc) amax = fmaxf(amax, fabsf(s));
+    if (own) rowv[n] = s;
+    __syncthreads();
+    if (own) {
+      const float xp = rowv[partner];
+      const float r = first ? s * c - xp * sn : xp * sn + s * c;
+      using XR = typename XS::raw;
+      store_from_f32<XS>(static_cast<XR*>(rope_pool) + prow * dr, n, r);
+    }
+    return;
   }
-  amax = wave_max(amax);
-  if (lane == 0) red[wave] = amax;
-  __syncthreads();
-  for (int j = tid; j < dr / 2; j += blockDim.x) {
-    int ia, ib;
-    rope_pair(j, dr, pairing, ia, ib);
-    float c, s;
-    rope_angle(pos, j, dr, base, c, s);
-    const float xa = rowv[dc + ia], xb = rowv[dc + ib];
-    rowv[dc + ia] = xa * c - xb * s;
-    rowv[dc + ib] = xa * s + xb * c;
+  // Latent row: thread n owns columns n, n + blockDim.x, ...
+  float* red = rowv;
+  float amax = 0.f;
+  constexpr int kCols = 2;  // columns per thread kept in registers (d_c <= 2 blockDim.x)
+  float sv[kCols];
+  int pos;
+  int64_t prow = -1;
+#pragma unroll
+  for (int q = 0; q < kCols; ++q) {
+    const int n = tid + q * int(blockDim.x);
+    if (q == 0 && KC <= kFinBatch) {
+      // One batch: issue the loads, then look up the row while they are in flight.
+      float v[kFinBatch];
+#pragma unroll
+      for (int k = 0; k < kFinBatch; ++k)
+        v[k] = n < dc && k < KC ? part_c[(int64_t(m) * KC + k) * dc + n] : 0.f;
+      prow = pool_row(pos);
+      float t = 0.f;
+#pragma unroll
+      for (int k = 0; k < kFinBatch; ++k) t += v[k];
+      sv[q] = t;
+    } else {
+      sv[q] = n < dc ? sum_chunks(part_c + int64_t(m) * KC * dc + n, dc, KC) : 0.f;
+    }
+    if (n < dc) amax = fmaxf(amax, fabsf(sv[q]));
   }
-  __syncthreads();
-  using XR = typename XS::raw;
-  XR* rp = static_cast<XR*>(rope_pool) + prow * dr;
-  for (int n = tid; n < dr; n += blockDim.x) store_from_f32<XS>(rp, n, rowv[dc + n]);
+  if (KC > kFinBatch) prow = pool_row(pos);
+  if (pos < 0) return;
   if constexpr (sizeof(typename KVS::raw) == 1) {
+    amax = wave_max(amax);
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
     amax = red[0];
     for (int w = 1; w < nwaves; ++w) amax = fmaxf(amax, red[w]);
     const float scale = amax > 0.f ? amax / 448.f : 1.f;
     if (tid == 0) scale_pool[prow] = scale;
     uint8_t* cp = static_cast<uint8_t*>(c_pool) + prow * dc;
-    for (int n = tid; n < dc; n += blockDim.x) {
-      // Nearest-even e4m3fn (OCP) conversion of the gfx950 instruction; |y| <= 448 up to
-      // the rounding of the division, clamped so that no code saturates to NaN.
-      const float y = fminf(fmaxf(rowv[n] / scale, -448.f), 448.f);
-      cp[n] = uint8_t(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFF);
+#pragma unroll
+    for (int q = 0; q < kCols; ++q) {
+      const int n = tid + q * int(blockDim.x);
+      if (n < dc) {
+        // Nearest-even e4m3fn (OCP) conversion of the gfx950 instruction; |y| <= 448 up to
+        // the rounding of the division, clamped so that no code saturates to NaN.
+        const float y = fminf(fmaxf(sv[q] / scale, -448.f), 448.f);
+        cp[n] = uint8_t(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false) & 0xFF);
+      }
     }
   } else {
     using KR = typename KVS::raw;
     KR* cp = static_cast<KR*>(c_pool) + prow * dc;
-    for (int n = tid; n < dc; n += blockDim.x) store_from_f32<KVS>(cp, n, rowv[n]);
+#pragma unroll
+    for (int q = 0; q < kCols; ++q) {
+      const int n = tid + q * int(blockDim.x);
+      if (n < dc) store_from_f32<KVS>(cp, n, sv[q]);
+    }
   }
 }
 
@@ -183,10 +249,11 @@ int launch_cache_append(const CacheAppendArgs& a, hipStream_t s) {
   const int KC = int(cache_append_chunks(a.d_model));
   float* part_c = a.part;
   float* part_r = a.part + int64_t(a.M) * KC * a.dc;
-  const bool mfma = a.x_dt == MLA_BF16 && proj_mfma_supported(a.M, a.d_model, a.dc) &&
-                    (a.dr == 0 || proj_mfma_supported(a.M, a.d_model, a.dr));
+  const bool mfma = a.x_dt == MLA_BF16 && proj_mfma_supported(a.M, a.d_model, a.dc, kPK) &&
+                    (a.dr == 0 || proj_mfma_supported(a.M, a.d_model, a.dr, kPK));
   if (mfma) {
-    if (int e = launch_proj_mfma(a.x, a.w_dkv, part_c, a.dc, a.w_kr, part_r, a.dr, a.M, a.d_model, s)) return e;
+    if (int e = launch_proj_mfma(a.x, a.w_dkv, part_c, a.dc, a.w_kr, part_r, a.dr, a.M, a.d_model, kPK, s))
+      return e;
   } else {
     const dim3 grid((N + kPN - 1) / kPN, KC, (a.M + kPM - 1) / kPM);
     if (a.x_dt == MLA_F32)
@@ -199,10 +266,12 @@ int launch_cache_append(const CacheAppendArgs& a, hipStream_t s) {
                          a.d_model, a.dc, a.dr, part_c, part_r);
     if (int e = int(hipGetLastError())) return e;
   }
-  const int fin_threads = std::min(1024, (N + 63) / 64 * 64);
-  const size_t lds = sizeof(float) * (N + 16);
+  // One thread per latent column (up to 1024; d_c <= 2048 takes two per thread), and at
+  // least d_r threads for the key's workgroup.
+  const int fin_threads = std::min(1024, (std::max(a.dc, a.dr) + 63) / 64 * 64);
+  const size_t lds = sizeof(float) * std::max(a.dr, 16);
 #define MLA_FIN(XS, KVS)                                                                                    \
-  hipLaunchKernelGGL((append_finalize_kernel<XS, KVS>), dim3(a.M), dim3(fin_threads), lds, s, part_c, part_r, KC, a.M, a.sq, \
+  hipLaunchKernelGGL((append_finalize_kernel<XS, KVS>), dim3(a.M, a.dr > 0 ? 2 : 1), dim3(fin_threads), lds, s, part_c, part_r, KC, a.M, a.sq, \
                      a.dc, a.dr, a.base, a.pairing, a.c_pool, a.scale_pool, a.rope_pool, a.bs, a.table,      \
                      a.max_blocks, a.seq_lens)
   if (a.x_dt == MLA_F32)

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void linear_reduce_kernel(const float* __restr
 
 int launch_linear(const void* x, const void* w, void* y, int32_t M, int32_t K, int32_t N, float* part,
                   hipStream_t s) {
-  int err = launch_proj_mfma(x, w, part, N, nullptr, nullptr, 0, M, K, s);
+  int err = launch_proj_mfma(x, w, part, N, nullptr, nullptr, 0, M, K, 256, s);
   if (err) return err;
   const int64_t threads = int64_t(M) * (N / 8);
   hipLaunchKernelGGL(linear_reduce_kernel, dim3(unsigned((threads + 255) / 256)), dim3(256), 0, s, part,
