@@ -208,6 +208,24 @@ mla_status mla_absorb_out(const mla_dims* dims, const void* o_lat, mla_dtype in_
                           const void* w_uv, mla_dtype w_dt, void* out, mla_dtype out_dt,
                           void* stream);
 
+/* ---- latent attention and output absorption in one call ------------------------------
+ * mla_decode (same arguments, o_dt = q_dt) followed by mla_absorb_out(dims, o_lat, q_dt,
+ * w_uv, q_dt, out, q_dt, stream), with the same results bit for bit: o_lat, lse (if not
+ * NULL) and out[B, s_q, n_h, d_h] are all written.  w_uv [n_h, d_c, d_h] as for
+ * mla_absorb_out.  On the matrix-core kernels' default plan (balanced ranges, bf16, d_c =
+ * 512, d_h a multiple of 64, fewer than 8 ranges per sequence on average) the merge of the
+ * sequences cut by range boundaries runs inside the output absorption: one launch and one
+ * round trip of the merged rows fewer (the output side of "Operator Notes (1): MLA",
+ * section 2, o = attn . V then O; the split-K merge of the decode as in mla_decode).
+ * Otherwise the two calls run one after the other.  workspace: as for mla_decode.  Errors
+ * as for mla_decode, plus MLA_ERR_INVALID_ARG for a NULL or misaligned w_uv or out, all
+ * before any launch. */
+mla_status mla_decode_absorb_out(const mla_dims* dims, const void* q_lat, const void* q_rope, mla_dtype q_dt,
+                                 const void* c_kv, mla_dtype kv_dt, const float* kv_scale, const void* k_rope,
+                                 mla_dtype rope_dt, int32_t T, const int32_t* seq_lens, const void* w_uv,
+                                 void* o_lat, float* lse, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* ---- cache write of the new tokens (the step before decode) ------------------------
  * The latent is the only KV state cached ("Operator Notes (1): MLA", section 2:
  * c_kv = x . W_DKV); next to it sits the small decoupled key that carries the rotary

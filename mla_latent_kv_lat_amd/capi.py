@@ -31,6 +31,7 @@ EXPORTED = (
     "mla_status_str", "mla_last_hip_error", "mla_version", "mla_cache_append_workspace_bytes",
     "mla_cache_append", "mla_rope_query", "mla_prefill_workspace_bytes", "mla_prefill",
     "mla_linear_workspace_bytes", "mla_linear", "mla_decode_noalloc", "mla_fold_output_weights",
+    "mla_decode_absorb_out",
 )
 
 # Size of the static device array mla_decode_noalloc keeps its partial results in.
@@ -91,6 +92,8 @@ _SIGNATURES = {
     "mla_linear_workspace_bytes": [_i32, _i32, _i32],
     "mla_linear": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _sz, _vp],
     "mla_fold_output_weights": [_vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp],
+    "mla_decode_absorb_out": [_dims_p, _vp, _vp, _i32, _vp, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                              _vp, _sz, _vp],
     "mla_prefill": [_dims_p, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz, _vp],
     "mla_status_str": [_i32],
     "mla_last_hip_error": [],
@@ -206,6 +209,21 @@ def mla_decode(d: MlaDims, q_lat, q_rope, c_kv, k_rope, T: int, seq_lens, o_lat,
                            T, _ptr(seq_lens), _ptr(o_lat), qdt if o_lat is None else _dt(o_lat, q_dtype),
                            _ptr(lse), _ptr(workspace), workspace_bytes, _stream(stream))
     return _done(st, "mla_decode", check)
+
+
+def mla_decode_absorb_out(d: MlaDims, q_lat, q_rope, c_kv, k_rope, T: int, seq_lens, w_uv, o_lat, lse, out,
+                          workspace, workspace_bytes: Optional[int] = None, *, kv_scale=None, q_dtype=None,
+                          kv_dtype=None, stream=None, check=True) -> int:
+    """mla_decode followed by mla_absorb_out in one call (argument marshalling only)."""
+    qdt = _dt(q_lat, q_dtype)
+    kvdt = _dt(c_kv, kv_dtype)
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = _lib().mla_decode_absorb_out(ctypes.byref(d), _ptr(q_lat), _ptr(q_rope), qdt, _ptr(c_kv), kvdt,
+                                      _ptr(kv_scale), _ptr(k_rope), qdt if k_rope is None else _dt(k_rope, q_dtype),
+                                      T, _ptr(seq_lens), _ptr(w_uv), _ptr(o_lat), _ptr(lse), _ptr(out),
+                                      _ptr(workspace), workspace_bytes, _stream(stream))
+    return _done(st, "mla_decode_absorb_out", check)
 
 
 def mla_decode_noalloc(d: MlaDims, q_lat, q_rope, c_kv, k_rope, T: int, seq_lens, o_lat, lse, *,

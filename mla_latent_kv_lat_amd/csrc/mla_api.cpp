@@ -120,7 +120,7 @@ mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t
   return MLA_OK;
 }
 
-mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
+mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s, bool combine) {
   if (p.balanced && !a.prefix_here) {
     const int err = launch_tile_prefix(a, s);
     if (err) return hip_status(err);
@@ -129,7 +129,7 @@ mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
             : p.kernel == DecodeKernel::kMfma ? launch_decode_mfma(a, p, s)
                                               : launch_decode_general(a, p, s);
   if (err) return hip_status(err);
-  if (p.balanced || p.num_splits > 1) return hip_status(launch_combine(a, p, s));
+  if (combine && (p.balanced || p.num_splits > 1)) return hip_status(launch_combine(a, p, s));
   return MLA_OK;
 }
 
@@ -485,6 +485,30 @@ mla_status mla_decode(const mla_dims* d, const void* q_lat, const void* q_rope, 
   st = attach_workspace(&a, p, workspace, workspace_bytes);
   if (st != MLA_OK) return st;
   return run_decode(a, p, static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_decode_absorb_out(const mla_dims* d, const void* q_lat, const void* q_rope, mla_dtype q_dt,
+                                 const void* c_kv, mla_dtype kv_dt, const float* kv_scale, const void* k_rope,
+                                 mla_dtype rope_dt, int32_t T, const int32_t* seq_lens, const void* w_uv,
+                                 void* o_lat, float* lse, void* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  DecodeArgs a;
+  DecodePlan p;
+  mla_status st = prepare_decode(d, q_lat, q_rope, q_dt, c_kv, kv_dt, kv_scale, k_rope, rope_dt, T, seq_lens,
+                                 o_lat, q_dt, lse, &a, &p);
+  if (st != MLA_OK) return st;
+  if (!w_uv || !out || !aligned(w_uv, 16) || !aligned(out, 16)) return MLA_ERR_INVALID_ARG;
+  st = attach_workspace(&a, p, workspace, workspace_bytes);
+  if (st != MLA_OK) return st;
+  const auto s = static_cast<hipStream_t>(stream);
+  if (merge_absorb_fits(a, p, d->d_head)) {
+    st = run_decode(a, p, s, false);
+    if (st != MLA_OK) return st;
+    return hip_status(launch_merge_absorb(a, p, w_uv, out, d->d_head, s));
+  }
+  st = run_decode(a, p, s, true);
+  if (st != MLA_OK) return st;
+  return mla_absorb_out(d, o_lat, q_dt, w_uv, q_dt, out, q_dt, stream);
 }
 
 mla_status mla_decode_paged(const mla_dims* d, const void* q_lat, const void* q_rope,

@@ -116,7 +116,7 @@ mla_status prepare_decode(const mla_dims* d, const void* q_lat, const void* q_ro
 // when it is missing, too small or not 256-byte aligned).
 mla_status attach_workspace(DecodeArgs* a, const DecodePlan& p, void* ws, size_t ws_bytes);
 // Enqueues the planned kernels of one decode call on stream s.
-mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s, bool combine = true);
 // MLA_OK for 0, else MLA_ERR_HIP with the hipError_t kept for mla_last_hip_error().
 mla_status hip_error_status(int err);
 mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
@@ -129,6 +129,10 @@ int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t 
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_decode_latent(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+// The balanced ranges' merge inside the output absorption (decode_general.hip).
+bool merge_absorb_fits(const DecodeArgs& a, const DecodePlan& p, int32_t d_h);
+int launch_merge_absorb(const DecodeArgs& a, const DecodePlan& p, const void* w_uv, void* out, int32_t d_h,
+                        hipStream_t s);
 int launch_tile_prefix(const DecodeArgs& a, hipStream_t s);
 constexpr int kMaxInKernelPrefixBatch = 1024;  // batches up to this size skip the prefix kernel
 int launch_absorb(const void* x, const void* w, void* y, mla_dtype dt, int32_t M, int32_t H,

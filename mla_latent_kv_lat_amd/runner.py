@@ -96,6 +96,20 @@ class DeviceWorkload:
         c = c or self.caches[0]
         libmla.mla_absorb_out(self.dims, self.o_lat if o_lat is None else o_lat, c["w_uv"], self.out)
 
+    def decode_absorb_out(self, c: Optional[dict] = None, q_lat=None):
+        """Latent attention and output absorption in one library call (contiguous caches;
+        a paged cache takes the two calls)."""
+        c = c or self.caches[0]
+        q_lat = self.q_lat if q_lat is None else q_lat
+        cfg = self.cfg
+        if cfg.paged:
+            self.decode(c, q_lat)
+            self.absorb_out(c)
+            return
+        libmla.mla_decode_absorb_out(self.dims, q_lat, self.q_rope, c["c_kv"], c["k_rope"], cfg.seq_len,
+                                     self.seq_lens, c["w_uv"], self.o_lat, self.lse, self.out, self.workspace,
+                                     kv_scale=c["kv_scale"])
+
     def step(self):
         """One whole decode step over the next replica."""
         c = self.caches[self._k % len(self.caches)]

@@ -414,3 +414,20 @@ def test_fold_output_weights_validates_before_any_hip_call():
     assert f(None, A, A, 128, 512, 128, 5120, bf, None) == L.MLA_ERR_INVALID_ARG
     assert f(A + 2, A, A, 128, 512, 128, 5120, bf, None) == L.MLA_ERR_INVALID_ARG
     assert f(A, A, A, 0, 512, 128, 5120, bf, None) == L.MLA_ERR_INVALID_ARG
+
+
+def test_decode_absorb_out_validates_before_any_hip_call():
+    """mla_decode_absorb_out shares mla_decode's checks and rejects a NULL or misaligned
+    w_uv or out, all before touching the device."""
+    f = L._lib().mla_decode_absorb_out
+    bf = L.MLA_BF16
+    d = v2()
+    ws = 1 << 30
+
+    def call(w_uv=A, out=A, dims=d):
+        return f(ctypes.byref(dims), A, A, bf, A, bf, None, A, bf, 4096, None, w_uv, A, None, out, A, ws, None)
+    assert call(w_uv=None) == L.MLA_ERR_INVALID_ARG
+    assert call(out=None) == L.MLA_ERR_INVALID_ARG
+    assert call(w_uv=A + 2) == L.MLA_ERR_INVALID_ARG
+    assert call(out=A + 8) == L.MLA_ERR_INVALID_ARG
+    assert call(dims=v2(batch=0)) == L.MLA_ERR_INVALID_ARG
