@@ -150,6 +150,202 @@ __global__ __launch_bounds__(kThreads) void absorb_mfma_kernel(const uint16_t* _
   }
 }
 
+// The K = 512 product at large M, with K streamed: a workgroup (head, 64 columns, MG rows)
+// walks K in chunks of 128, the weight and activation slices of chunk c + 1 loaded into
+// registers while chunk c is multiplied from one of two LDS stages (2 x 32 KB for MG = 64,
+// so two workgroups share a compute unit and their memory phases overlap).  The products of
+// every output element run in the same k order as in absorb_mfma_kernel, so the results are
+// the same bit for bit.
+template <int MG>
+__global__ __launch_bounds__(kThreads) void absorb_stream_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ w,
+                                                                 uint16_t* __restrict__ y, int M, int H, int N,
+                                                                 int n_xcd) {
+  constexpr int K = 512, KC = 128, NC = K / KC, kBlocks = MG / 16;
+  constexpr int kWPer = KC * 8 / kThreads;         // 16-byte weight chunks per thread and K chunk
+  constexpr int kXPer = MG * (KC / 8) / kThreads;  // 16-byte activation chunks per thread and K chunk
+  __shared__ __attribute__((aligned(16))) uint16_t wt[2][KC * kBN];  // [k][64], chunks swizzled by swz128(k)
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MG * KC];   // [row][k], chunk c at c ^ xswz(row)
+  int h = blockIdx.x, n0 = blockIdx.y * kBN, m0 = blockIdx.z * MG;
+  if (n_xcd > 1 && int(gridDim.x) % n_xcd == 0) {
+    const int ncol = int(gridDim.y), nrg = int(gridDim.z);
+    const int id = int(blockIdx.x) + int(gridDim.x) * (int(blockIdx.y) + ncol * int(blockIdx.z));
+    const int j = id / n_xcd;
+    h = (j / (ncol * nrg)) * n_xcd + id % n_xcd;
+    n0 = ((j / nrg) % ncol) * kBN;
+    m0 = (j % nrg) * MG;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, mm = lane & 15;
+  const uint16_t* wh = w + int64_t(h) * K * N + n0;
+  u32x4 wr[kWPer], xr[kXPer];
+  auto load = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int idx = tid + i * kThreads, k = idx >> 3, ch = idx & 7;
+      wr[i] = ld16(wh + int64_t(c * KC + k) * N + 8 * ch);
+    }
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int idx = tid + i * kThreads, r = idx / (KC / 8), ch = idx % (KC / 8);
+      xr[i] = ld16(x + (int64_t(min(m0 + r, M - 1)) * H + h) * K + c * KC + 8 * ch);
+    }
+  };
+  auto stage = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int idx = tid + i * kThreads, k = idx >> 3, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(&wt[st][k * kBN + 8 * (ch ^ swz128(k))]) = wr[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int idx = tid + i * kThreads, r = idx / (KC / 8), ch = idx % (KC / 8);
+      *reinterpret_cast<u32x4*>(&xs[st][r * KC + 8 * (ch ^ xswz(r))]) = xr[i];
+    }
+  };
+  f32x4 acc[kBlocks];
+#pragma unroll
+  for (int i = 0; i < kBlocks; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load(0);
+  stage(0);
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int st = c & 1;
+    if (c + 1 < NC) load(c + 1);
+#pragma unroll
+    for (int s = 0; s < KC / 32; ++s) {
+      const bf16x8 av = lds_operand_tr(wt[st], 32 * s, 16 * wv, lane);
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) {
+        const int r = 16 * i + mm;
+        const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&xs[st][r * KC + 8 * ((4 * s + g) ^ xswz(r))]);
+        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[i], 0, 0, 0);
+      }
+    }
+    if (c + 1 < NC) stage(st ^ 1);
+    __syncthreads();  // stage st ^ 1 written; every wave done reading stage st
+  }
+  // bf16 results through LDS (stage 0's activation buffer), so that each output row's 128
+  // bytes leave in one store: row r's 16-byte chunk c sits at c ^ ((r >> 1) & 7).
+  uint16_t* ys = xs[0];
+#pragma unroll
+  for (int i = 0; i < kBlocks; ++i) {
+    const int r = 16 * i + mm, col = 16 * wv + 4 * g;
+    *reinterpret_cast<u32x2*>(&ys[r * kBN + 8 * ((col >> 3) ^ ((r >> 1) & 7)) + (col & 7)]) =
+        u32x2{pack_bf16x2(acc[i][0], acc[i][1]), pack_bf16x2(acc[i][2], acc[i][3])};
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = tid >> 3; r < MG; r += kThreads / 8) {
+    const int c = tid & 7, m = m0 + r;
+    if (m < M)
+      *reinterpret_cast<u32x4*>(y + (int64_t(m) * H + h) * N + n0 + 8 * c) =
+          *reinterpret_cast<const u32x4*>(&ys[r * kBN + 8 * (c ^ ((r >> 1) & 7))]);
+  }
+}
+
+// The K = 128 product at large M, persistent over rows: a workgroup (head, 128 columns as
+// two 64-column halves) keeps its 32 KB weight slice in LDS and walks the rows in groups of
+// 64, group g + 1's activation rows loaded into registers while group g is multiplied from
+// one of two LDS stages; group g's bf16 results are staged in the stage it was read from
+// (once every wave is done with it) and leave as whole 128-byte row pieces.  The products of
+// every output element run in the same k order as in absorb_mfma_kernel.
+__global__ __launch_bounds__(kThreads) void absorb_rows_kernel(const uint16_t* __restrict__ x,
+                                                               const uint16_t* __restrict__ w,
+                                                               uint16_t* __restrict__ y, int M, int H, int N,
+                                                               int n_xcd) {
+  constexpr int K = 128, RG = 64, NH = 2, kBlocks = RG / 16;
+  constexpr int kWPer = NH * K * 8 / kThreads;     // 16-byte weight chunks per thread
+  constexpr int kXPer = RG * (K / 8) / kThreads;   // 16-byte activation chunks per thread and group
+  __shared__ __attribute__((aligned(16))) uint16_t wt[NH][K * kBN];  // [k][64], chunks swizzled by swz128(k)
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][RG * K];    // [row][k], chunk c at c ^ xswz(row)
+  int h = blockIdx.x, n0 = blockIdx.y * NH * kBN;
+  if (n_xcd > 1 && int(gridDim.x) % n_xcd == 0) {
+    const int ncol = int(gridDim.y);
+    const int id = int(blockIdx.x) + int(gridDim.x) * int(blockIdx.y);
+    const int j = id / n_xcd;
+    h = (j / ncol) * n_xcd + id % n_xcd;
+    n0 = (j % ncol) * NH * kBN;
+  }
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane >> 4, mm = lane & 15;
+  const int ngroups = (M + RG - 1) / RG;
+  u32x4 xr[kXPer];
+  auto load = [&](int grp) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int idx = tid + i * kThreads, r = idx / (K / 8), ch = idx % (K / 8);
+      xr[i] = ld16(x + (int64_t(min(grp * RG + r, M - 1)) * H + h) * K + 8 * ch);
+    }
+  };
+  auto stage = [&](int st) {
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int idx = tid + i * kThreads, r = idx / (K / 8), ch = idx % (K / 8);
+      *reinterpret_cast<u32x4*>(&xs[st][r * K + 8 * (ch ^ xswz(r))]) = xr[i];
+    }
+  };
+  {
+    u32x4 wr[kWPer];
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int idx = tid + i * kThreads, hh = idx / (K * 8), k = (idx >> 3) % K, ch = idx & 7;
+      wr[i] = ld16(w + int64_t(h) * K * N + int64_t(k) * N + n0 + 64 * hh + 8 * ch);
+    }
+    load(0);
+#pragma unroll
+    for (int i = 0; i < kWPer; ++i) {
+      const int idx = tid + i * kThreads, hh = idx / (K * 8), k = (idx >> 3) % K, ch = idx & 7;
+      *reinterpret_cast<u32x4*>(&wt[hh][k * kBN + 8 * (ch ^ swz128(k))]) = wr[i];
+    }
+    stage(0);
+  }
+  __syncthreads();
+  for (int grp = 0; grp < ngroups; ++grp) {
+    const int st = grp & 1;
+    if (grp + 1 < ngroups) load(grp + 1);
+    f32x4 acc[NH][kBlocks];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) acc[hh][i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s2 = 0; s2 < K / 32; ++s2) {
+#pragma unroll
+      for (int hh = 0; hh < NH; ++hh) {
+        const bf16x8 av = lds_operand_tr(wt[hh], 32 * s2, 16 * wv, lane);
+#pragma unroll
+        for (int i = 0; i < kBlocks; ++i) {
+          const int r = 16 * i + mm;
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&xs[st][r * K + 8 * ((4 * s2 + g) ^ xswz(r))]);
+          acc[hh][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[hh][i], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done reading stage st
+    // Results into stage st: 128-byte piece rp = 2 r + hh of row r, chunk c at c ^ ((rp >> 1) & 7).
+    uint16_t* ys = xs[st];
+#pragma unroll
+    for (int hh = 0; hh < NH; ++hh)
+#pragma unroll
+      for (int i = 0; i < kBlocks; ++i) {
+        const int rp = NH * (16 * i + mm) + hh, col = 16 * wv + 4 * g;
+        *reinterpret_cast<u32x2*>(&ys[rp * kBN + 8 * ((col >> 3) ^ ((rp >> 1) & 7)) + (col & 7)]) =
+            u32x2{pack_bf16x2(acc[hh][i][0], acc[hh][i][1]), pack_bf16x2(acc[hh][i][2], acc[hh][i][3])};
+      }
+    if (grp + 1 < ngroups) stage(st ^ 1);
+    __syncthreads();  // results staged, next group's rows staged
+#pragma unroll
+    for (int rp = tid >> 3; rp < RG * NH; rp += kThreads / 8) {
+      const int c = tid & 7, r = rp / NH, hh = rp % NH, m = grp * RG + r;
+      if (m < M)
+        *reinterpret_cast<u32x4*>(y + (int64_t(m) * H + h) * N + n0 + 64 * hh + 8 * c) =
+            *reinterpret_cast<const u32x4*>(&ys[rp * kBN + 8 * (c ^ ((rp >> 1) & 7))]);
+    }
+  }
+}
+
 }  // namespace
 
 bool proj_mfma_supported(int32_t M, int32_t K_total, int32_t N, int32_t kchunk) {
@@ -190,15 +386,17 @@ int launch_absorb_t(const void* x, const void* w, void* y, int32_t M, int32_t H,
   auto* yp = static_cast<uint16_t*>(y);
   int cus = kDefaultCUs, n_xcd = kDefaultXcds;
   device_topology(&cus, &n_xcd);
-  if (K == 128 && M >= kTallRows)
+  if (K == 128 && M >= kTallRows && N % 128 == 0 && x_st.m < 0 && y_st.m < 0)
+    hipLaunchKernelGGL(absorb_rows_kernel, dim3(H, N / 128), dim3(kThreads), 0, s, xp, wp, yp, M, H, N, n_xcd);
+  else if (K == 128 && M >= kTallRows)
     hipLaunchKernelGGL((absorb_mfma_kernel<128, kTallRows>), dim3(H, N / kBN, (M + kTallRows - 1) / kTallRows),
                        dim3(kThreads), 0, s, xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
   else if (K == 128)
     hipLaunchKernelGGL((absorb_mfma_kernel<128, 32>), dim3(H, N / kBN, (M + 31) / 32), dim3(kThreads), 0, s,
                        xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
-  else if (M >= 64)
-    hipLaunchKernelGGL((absorb_mfma_kernel<512, 64>), dim3(H, N / kBN, (M + 63) / 64), dim3(kThreads), 0, s,
-                       xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
+  else if (M >= 64 && x_st.m < 0 && y_st.m < 0)
+    hipLaunchKernelGGL((absorb_stream_kernel<64>), dim3(H, N / kBN, (M + 63) / 64), dim3(kThreads), 0, s, xp, wp,
+                       yp, M, H, N, n_xcd);
   else
     hipLaunchKernelGGL((absorb_mfma_kernel<512, 32>), dim3(H, N / kBN, (M + 31) / 32), dim3(kThreads), 0, s,
                        xp, wp, yp, M, H, N, n_xcd, x_st, y_st);
