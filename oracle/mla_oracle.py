@@ -30,7 +30,7 @@ Readings of points the pages leave open (stated once here, used throughout):
   sequence of length L sees rows t <= L - s_q + i (causal among the new tokens).
 * A query row that sees no key returns zeros and lse = -inf.
 
-Parity pins for every function live in tests/test_oracle.py.
+Parity pins for every function live in tests/test_oracle*.py.
 """
 from __future__ import annotations
 
@@ -409,6 +409,59 @@ def latent_attention_fp8_query(q_lat, q_rope, c_kv, k_rope, seq_lens, scale, sli
     term and the product with the latent (the value) are exact.  Returns (o_lat, lse)."""
     return latent_attention(round_query_slices_e4m3(q_lat, slice_width), q_rope, c_kv, k_rope, seq_lens,
                             scale)
+
+
+def round_significand(x, bits: int = 4):
+    """x rounded to ``bits`` significant binary digits, ties to the even one.  With bits = 4
+    this is the precision of an e4m3 number in its normal range (an implicit leading one and
+    three stored mantissa bits), without the format's bounds on the exponent."""
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)  # x = m * 2^e with 0.5 <= |m| < 1 (m = 0 for x = 0)
+    return np.ldexp(np.round(m * 2.0 ** bits), e - bits)
+
+
+def latent_attention_fp8(q_lat, q_rope, codes, kv_scale, k_rope, seq_lens, scale, slice_width: int = 128):
+    """Both products of the absorbed decode on fp8 operands (the quantized-cache direction
+    of "Multi-Head Latent Attention (MLA) Explained", section "Which Models Use MLA and What
+    Is Next").  The score is latent_attention_fp8_query's: the latent query rounded slice by
+    slice (round_query_slices_e4m3), times the stored codes (decode_e4m3fn) and the token's
+    scale, plus the exact RoPE term.  The softmax weights are exact; the value product runs on
+    the stored codes, with each weight times its token's scale rounded to e4m3 precision
+    (round_significand).  The normaliser sums the unrounded weights.
+
+    Reading: the weight of token t is taken as 2^(x_t - k), with x_t the base-2 logit
+    (scale * log2(e) * score) and k an integer (here the ceiling of the row's largest logit);
+    since rounding to a number of significant bits commutes with multiplying by a power of
+    two, the rounded products do not depend on which integer it is.
+
+    codes [B, T, d_c] uint8 e4m3fn, kv_scale [B, T]; the rest as latent_attention.
+    Returns (o_lat, lse), lse in natural-log units."""
+    q = round_query_slices_e4m3(q_lat, slice_width)
+    q_rope = np.asarray(q_rope, np.float64)
+    k_rope = np.asarray(k_rope, np.float64)
+    B, sq, n_h, d_c = q.shape
+    o_lat = np.zeros((B, sq, n_h, d_c))
+    lse = np.full((B, sq, n_h), -np.inf)
+    for b in range(B):
+        L = int(seq_lens[b])
+        C = decode_e4m3fn(np.asarray(codes)[b, :L])
+        ts = np.asarray(kv_scale, np.float64)[b, :L]
+        s = scale * ((q[b] @ C.T) * ts + q_rope[b] @ k_rope[b, :L].T)     # [s_q, n_h, L]
+        x = (s * np.log2(np.e)).reshape(sq * n_h, L)
+        n_vis = np.repeat([visible_keys(L, sq, i) for i in range(sq)], n_h)
+        vis = np.arange(L)[None, :] < n_vis[:, None]
+        x = np.where(vis, x, -np.inf)
+        top = np.max(x, axis=1, initial=-np.inf)
+        k = np.where(np.isfinite(top), np.ceil(top), 0.0)
+        w = np.where(vis, np.exp2(x - k[:, None]), 0.0)
+        tot = w.sum(axis=1)
+        pw = round_significand(w * ts[None, :])
+        with np.errstate(divide="ignore", invalid="ignore"):
+            o = np.where(tot[:, None] > 0, (pw @ C) / tot[:, None], 0.0)
+            l = np.where(tot > 0, (k + np.log2(tot)) * np.log(2.0), -np.inf)
+        o_lat[b] = o.reshape(sq, n_h, d_c)
+        lse[b] = l.reshape(sq, n_h)
+    return o_lat, lse
 
 
 # ---------------------------------------------------------------------------------

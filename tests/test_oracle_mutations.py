@@ -11,6 +11,7 @@ import test_oracle as P
 import test_oracle_cache_write as PC
 import test_oracle_query as PQ
 import test_oracle_fp8_query as PF
+import test_oracle_fp8_values as PV
 
 _orig = {name: getattr(O, name) for name in dir(O) if callable(getattr(O, name))}
 
@@ -130,6 +131,50 @@ def _fp8_query_rounds_rope_too(q_lat, q_rope, c_kv, k_rope, seq_lens, scale, sli
     return _orig["latent_attention_fp8_query"](q_lat, r, c_kv, k_rope, seq_lens, scale, slice_width)
 
 
+def _round_significand_truncates(x, bits=4):
+    x = np.asarray(x, np.float64)
+    m, e = np.frexp(x)
+    return np.ldexp(np.trunc(m * 2.0 ** bits), e - bits)
+
+
+def _fp8_values_with(**change):
+    """latent_attention_fp8 with one step changed (its own code, re-written per mutation)."""
+    def f(q_lat, q_rope, codes, kv_scale, k_rope, seq_lens, scale, slice_width=128):
+        q = O.round_query_slices_e4m3(q_lat, slice_width)
+        B, sq, n_h, d_c = q.shape
+        o_lat = np.zeros((B, sq, n_h, d_c))
+        lse = np.full((B, sq, n_h), -np.inf)
+        for b in range(B):
+            L = int(seq_lens[b])
+            C = O.decode_e4m3fn(np.asarray(codes)[b, :L])
+            ts = np.asarray(kv_scale, np.float64)[b, :L]
+            s = scale * ((q[b] @ C.T) * ts + np.asarray(q_rope)[b] @ np.asarray(k_rope)[b, :L].T)
+            x = (s * np.log2(np.e)).reshape(sq * n_h, L)
+            n_vis = np.repeat([O.visible_keys(L, sq, i) for i in range(sq)], n_h)
+            vis = np.arange(L)[None, :] < n_vis[:, None]
+            x = np.where(vis, x, -np.inf)
+            top = np.max(x, axis=1, initial=-np.inf)
+            k = np.where(np.isfinite(top), top if change.get("real_reference") else np.ceil(top), 0.0)
+            w = np.where(vis, np.exp2(x - k[:, None]), 0.0)
+            if change.get("round_before_scale"):
+                pw = O.round_significand(w) * ts[None, :]
+            else:
+                pw = O.round_significand(w * ts[None, :])
+            tot = (pw / ts[None, :]).sum(axis=1) if change.get("rounded_normaliser") else w.sum(axis=1)
+            with np.errstate(divide="ignore", invalid="ignore"):
+                o = np.where(tot[:, None] > 0, (pw @ C) / tot[:, None], 0.0)
+                l = np.where(tot > 0, (k + np.log2(tot)) * np.log(2.0), -np.inf)
+            o_lat[b] = o.reshape(sq, n_h, d_c)
+            lse[b] = l.reshape(sq, n_h)
+        return o_lat, lse
+    return f
+
+
+def _fp8_values_unrounded(q_lat, q_rope, codes, kv_scale, k_rope, seq_lens, scale, slice_width=128):
+    return _orig["latent_attention_fp8_query"](q_lat, q_rope, O.dequantize_cache(codes, kv_scale), k_rope,
+                                               seq_lens, scale, slice_width)
+
+
 CASES = [
     ("latent_attention", _latent_attention_no_rope, lambda: P.pin_absorbed_vs_explicit(P.small_inputs())),
     ("latent_attention", _latent_attention_scale_on_latent_only,
@@ -158,6 +203,12 @@ CASES = [
     ("round_query_slices_e4m3", _round_query_one_scale_per_row, PF.pin_round_query_exact_slices),
     ("latent_attention_fp8_query", _fp8_query_unrounded, PF.pin_fp8_query_brute_force),
     ("latent_attention_fp8_query", _fp8_query_rounds_rope_too, PF.pin_fp8_query_attention_identity),
+    ("round_significand", _round_significand_truncates, PV.pin_round_significand_vs_torch),
+    ("latent_attention_fp8", _fp8_values_with(real_reference=True), PV.pin_fp8_values_brute_force),
+    ("latent_attention_fp8", _fp8_values_with(round_before_scale=True), PV.pin_fp8_values_brute_force),
+    ("latent_attention_fp8", _fp8_values_with(rounded_normaliser=True), PV.pin_fp8_values_brute_force),
+    ("latent_attention_fp8", _fp8_values_unrounded, PV.pin_fp8_values_bound),
+    ("latent_attention_fp8", _fp8_values_unrounded, PV.pin_fp8_values_hand_case),
 ]
 
 
