@@ -466,7 +466,7 @@ def main() -> int:
     ap.add_argument("--workload", default=None, help="workload name (default: the headline)")
     ap.add_argument("--replicas", type=int, default=4)
     ap.add_argument("--split-tokens", type=int, default=0)
-    ap.add_argument("--fp8-scores", type=int, choices=(0, 1), default=0,
+    ap.add_argument("--fp8-scores", type=int, choices=(0, 1, 2), default=0,
                     help="1: latent score term as an fp8 matrix product (fp8-cache workloads)")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--cpu-single-core-budget", type=float, default=8.0,

@@ -78,7 +78,7 @@ typedef struct {
                             from max_seq_len.  Any value gives the same result up to
                             rounding; every plan is bitwise reproducible run to run for
                             the same lengths. */
-  int32_t fp8_scores;    /* 0 or 1.  1: the latent part of the score is an fp8 matrix
+  int32_t fp8_scores;    /* 0, 1 or 2.  1: the latent part of the score is an fp8 matrix
                             product: each row's 128-column slices of q_lat are rounded to
                             e4m3 with their own scale (max|x| / 448) and multiplied with the
                             cache codes as stored; the RoPE term, the softmax and the product
@@ -93,7 +93,15 @@ typedef struct {
                             the output stays within a few 1e-2 of exact attention over long
                             contexts but the log-sum-exp of a sequence of a few tokens moves by
                             up to about 7e-2, and with logits 4x larger (peaked attention) the
-                            output moves by several percent. */
+                            output moves by several percent.
+                            2: the score as with 1, and the product with V also an fp8 matrix
+                            product on the cache codes as stored: each softmax weight times its
+                            token's scale is rounded to e4m3 precision (4 significant bits,
+                            nearest even; a power-of-two scale per row and 32 tokens keeps
+                            every weight above 2^-13 of that block's largest in e4m3's normal
+                            range), the normaliser sums the unrounded weights.  Same kernel
+                            set and accuracy statement as 1, plus the weight rounding (about
+                            2^-5 of each weight, averaging out over long contexts). */
 } mla_dims;
 
 /* Supported kernel set (anything else returns MLA_ERR_UNSUPPORTED):

@@ -7,6 +7,11 @@
 //   v_mfma_f32_32x32x16_bf16 (h = l / 32):
 //     A[m][k]: lane holds A[l % 32][8h .. 8h + 7];  B[k][n]: B[8h .. 8h + 7][l % 32];
 //     D[m][n]: element 4i + r of lane l is D[8i + 4h + r][l % 32]   (i, r in 0..3).
+//   v_mfma_scale_f32_32x32x64_f8f6f4 (8-bit formats, h = l / 32): lane l holds row (A) or
+//     column (B) l % 32, K values 16h .. 16h + 15 in bytes 0 .. 15 and 32 + 16h .. 32 + 16h + 15
+//     in bytes 16 .. 31; its E8M0 scale operand applies to K block h (K 32h .. 32h + 31) of
+//     that row or column.  D as for the bf16 form.  A product whose two operands follow any
+//     one K order is unaffected by it; the block scales are not.
 // On gfx950 the 32x32x16 form runs at twice the 16x16x32 form's throughput (the latter
 // takes as long per instruction for half the work), so dense loops use 32x32x16.
 // ds_read_b64_tr_b16: within each 16-lane group, lane 4r + q supplies the address of

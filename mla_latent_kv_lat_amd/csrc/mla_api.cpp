@@ -96,7 +96,7 @@ void fill_common(DecodeArgs* a, const mla_dims* d, const void* q_lat, const void
   a->part_lse = nullptr;
   a->prefix = nullptr;
   a->prefix_here = false;
-  a->fp8_scores = d->fp8_scores != 0;
+  a->fp8_scores = d->fp8_scores;
 }
 
 }  // namespace
@@ -126,7 +126,8 @@ mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s, b
     if (err) return hip_status(err);
   }
   int err = p.kernel == DecodeKernel::kLatent ? launch_decode_latent(a, p, s)
-            : p.kernel == DecodeKernel::kMfma ? launch_decode_mfma(a, p, s)
+            : p.kernel == DecodeKernel::kMfma ? (a.fp8_scores == 2 ? launch_decode_fp8(a, p, s)
+                                                                   : launch_decode_mfma(a, p, s))
                                               : launch_decode_general(a, p, s);
   if (err) return hip_status(err);
   if (combine && (p.balanced || p.num_splits > 1)) return hip_status(launch_combine(a, p, s));
@@ -156,7 +157,7 @@ mla_status check_dims(const mla_dims* d) {
   if (!d) return MLA_ERR_INVALID_ARG;
   if (d->batch < 1 || d->q_len < 1 || d->q_len > kMaxQLen || d->n_heads < 1 || d->d_head < 1 ||
       d->d_latent < 1 || d->d_rope < 0 || d->split_tokens < 0 || d->fp8_scores < 0 ||
-      d->fp8_scores > 1)
+      d->fp8_scores > 2)
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;
   if (int64_t(d->q_len) * d->n_heads > kMaxRows) return MLA_ERR_UNSUPPORTED;
@@ -367,7 +368,7 @@ mla_status mla_rope_query(const mla_dims* d, void* q_rope, mla_dtype q_dt, const
 static mla_status check_prefill(const mla_dims* d, int32_t T, mla_dtype dt) {
   if (!d) return MLA_ERR_INVALID_ARG;
   if (d->batch < 1 || d->q_len < 1 || d->n_heads < 1 || d->d_head < 1 || d->d_latent < 1 ||
-      d->d_rope < 0 || d->split_tokens < 0 || d->fp8_scores < 0 || d->fp8_scores > 1 || T < 1 ||
+      d->d_rope < 0 || d->split_tokens < 0 || d->fp8_scores < 0 || d->fp8_scores > 2 || T < 1 ||
       d->q_len > T)
     return MLA_ERR_INVALID_ARG;
   if (!std::isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_INVALID_ARG;

@@ -65,7 +65,8 @@ struct DecodeArgs {
   const int64_t* prefix; // balanced ranges: [B + 1] exclusive prefix sum of 32-token tiles per
                          // sequence (lengths clamped to [0, T]); nullptr for static splits
   bool prefix_here;      // the decode kernel computes and stores prefix itself (small batches)
-  bool fp8_scores;       // latent score term as an fp8 product (fp8 cache, matrix-core kernel)
+  int32_t fp8_scores;    // fp8 cache, matrix-core kernel: 1 = latent score term as an fp8
+                         // product; 2 = both products fp8 (decode_fp8.hip)
   float* part_lse;       // [B, S, rows] base-2 log-sum-exp of each split (S > 1)
 };
 
@@ -127,6 +128,7 @@ bool latent_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, 
 // Launchers (one per kernel file).  Return the hipError_t of the launch as int.
 int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+int launch_decode_fp8(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_decode_latent(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 // The balanced ranges' merge inside the output absorption (decode_general.hip).

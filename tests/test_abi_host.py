@@ -281,18 +281,21 @@ def test_rope_query_argument_errors(kw, status):
 
 
 def test_fp8_scores_argument():
-    """fp8_scores must be 0 or 1, and needs the fp8 cache on the matrix-core kernel."""
+    """fp8_scores must be 0, 1 or 2, and 1 and 2 need the fp8 cache on the matrix-core kernel
+    (same plan as without)."""
     cfg = configs.SPEC_FP8
-    assert L.mla_decode_plan(L.dims_from_config(cfg, fp8_scores=2), "fp8", cfg.seq_len,
-                             check=False)[0] == L.MLA_ERR_INVALID_ARG
-    assert L.mla_decode_plan(L.dims_from_config(cfg, fp8_scores=1), "fp8", cfg.seq_len) == \
-        L.mla_decode_plan(L.dims_from_config(cfg), "fp8", cfg.seq_len)
-    v2 = configs.V2_DECODE
-    assert L.mla_decode_plan(L.dims_from_config(v2, fp8_scores=1), "bf16", v2.seq_len,
-                             check=False)[0] == L.MLA_ERR_UNSUPPORTED
-    small = cfg.with_(n_heads=8)  # general kernel
-    assert L.mla_decode_plan(L.dims_from_config(small, fp8_scores=1), "fp8", small.seq_len,
-                             check=False)[0] == L.MLA_ERR_UNSUPPORTED
+    for bad in (3, -1):
+        assert L.mla_decode_plan(L.dims_from_config(cfg, fp8_scores=bad), "fp8", cfg.seq_len,
+                                 check=False)[0] == L.MLA_ERR_INVALID_ARG
+    for mode in (1, 2):
+        assert L.mla_decode_plan(L.dims_from_config(cfg, fp8_scores=mode), "fp8", cfg.seq_len) == \
+            L.mla_decode_plan(L.dims_from_config(cfg), "fp8", cfg.seq_len)
+        v2 = configs.V2_DECODE
+        assert L.mla_decode_plan(L.dims_from_config(v2, fp8_scores=mode), "bf16", v2.seq_len,
+                                 check=False)[0] == L.MLA_ERR_UNSUPPORTED
+        small = cfg.with_(n_heads=8)  # general kernel
+        assert L.mla_decode_plan(L.dims_from_config(small, fp8_scores=mode), "fp8", small.seq_len,
+                                 check=False)[0] == L.MLA_ERR_UNSUPPORTED
 
 
 def test_prefill_workspace_and_argument_errors():
