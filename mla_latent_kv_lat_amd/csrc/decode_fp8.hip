@@ -21,20 +21,21 @@
 // rounding to 4 significant bits).
 //
 // The value product's K (64 tokens) sets the step: a workgroup owns 64 query rows of one
-// sequence and walks its piece of the context in 64-token steps.  Eight waves, three roles:
-//   * loader waves 4, 5 (SIMDs 0, 1): wave 4 + l loads tokens 32 l .. 32 l + 31 of every
-//     step (512-byte code rows, 128-byte RoPE rows, the scales; 16 bytes per lane, two steps
-//     ahead in registers) and stages them in LDS as they are;
-//   * score waves 0, 1 (SIMDs 0, 1): wave w owns rows 32 w .. 32 w + 31 and scores the
-//     step's two 32-token halves one after the other (eight fp8 and four bf16 products
-//     each), runs the online softmax on each in registers and publishes the rounded
-//     probabilities with their block scales;
-//   * output waves 2, 3, 6, 7 (SIMDs 2, 3): 128 columns each, eight fp8 products per step;
-//     the V^T operands come from the staged codes by 8-bit transposed LDS reads
-//     (ds_read_b64_tr_b8) one step ahead.
-// One barrier per step, as in the bf16-value kernel: in step n the loaders stage step n + 1
-// (and load step n + 3), the score waves score step n, the output waves multiply step n - 1
-// and read the V^T operands of step n.
+// sequence and walks its piece of the context in 64-token steps.  Eight waves, one score
+// wave and one output wave on each SIMD:
+//   * score waves 0 .. 3 (SIMD w): wave w owns rows 32 (w & 1) .. + 31 and half w >> 1 (tokens
+//     32 (w >> 1) .. + 31) of every step: eight fp8 and four bf16 products, then the online
+//     softmax of its rows over its half-stream (its own integer reference and sum), then the
+//     rounded probabilities with their block scales and the stream's reference;
+//   * output waves 4 .. 7 (SIMD w - 4): 128 columns each, eight fp8 products per step on V^T
+//     operands read from the staged codes by 8-bit transposed LDS reads (ds_read_b64_tr_b8);
+//     the two half-streams of a row meet here: the accumulator's reference is the larger of
+//     the two, and each half's block scale is lowered by its distance to it (powers of two).
+//     They also stage the cache: each wave copies 16 rows of every step straight from memory
+//     into LDS (direct-to-LDS loads, two steps ahead, three buffers).
+// One barrier per step: in step n the output waves issue the loads of step n + 2, multiply
+// step n - 1 and read the V^T operands of step n, and wait for step n + 1's loads; the score
+// waves score step n.
 #include "device_common.h"
 #include "mfma_common.h"
 #include "mla_internal.h"
@@ -48,27 +49,17 @@ constexpr int kDR = 64;
 constexpr int kRows = 64;      // query rows per workgroup
 constexpr int kStep = 64;      // tokens per step (K of the fp8 value product)
 constexpr int kHalf = 32;      // tokens per score product (and per block scale)
-constexpr int kThreads = 512;  // 2 score, 2 loader and 4 output waves
+constexpr int kThreads = 512;  // 4 score and 4 output waves
 constexpr int kCols = 128;     // latent columns per output wave
+constexpr int kStages = 3;     // staged steps in LDS (loads run two steps ahead)
+constexpr int kLoadsPerStep = 11;  // direct-to-LDS loads per output wave and step
 constexpr int kMaxPrefixBatch = 2 * kThreads;
-// The reference max only moves when a half's max exceeds it by more than this many base-2
-// units (it then moves to the ceiling of that max).
+// A half-stream's reference max only moves when a half's max exceeds it by more than this
+// many base-2 units (it then moves to the ceiling of that max).
 constexpr float kTau = 8.f;
 static_assert(kMaxInKernelPrefixBatch <= kMaxPrefixBatch, "in-kernel tile prefix does not fit");
 
 enum : int { kContig = 0, kPagedTile = 1, kPagedAny = 2 };
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
-}
-
-__device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-__device__ __forceinline__ float buf_ld4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
 
 __device__ __forceinline__ int rope_swz(int row) { return (row >> 1) & 7; }
 
@@ -84,146 +75,89 @@ __device__ __forceinline__ u32x2 lds_read_tr8(const uint8_t* p) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) v2i*)(p)));
 }
 
-struct Ctx {
-  int b, lane, n, h, w;
-  int t_hi;
-  const int32_t* table;
-  int max_blocks, bs;
-  int64_t T;
-};
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return uint32_t(reinterpret_cast<uintptr_t>(p)); }
 
-__device__ __forceinline__ int64_t any_row(const Ctx& c, int t) {
-  const int tc = min(t, c.t_hi - 1);
-  return int64_t(c.table[int64_t(c.b) * c.max_blocks + tc / c.bs]) * c.bs + tc % c.bs;
+// Direct-to-LDS loads (lane i writes LDS bytes [lds + size i, lds + size (i + 1)) from its
+// own address, or from a wave-uniform base plus its 32-bit offset), written as inline assembly so that the compiler does not treat later LDS
+// reads as dependent on them; completion is awaited explicitly (wait_vm) before the barrier
+// that publishes the step.  The LDS address is made wave-uniform; the block carries the wait
+// states the hardware needs between the read-first-lane, the M0 write and the load.
+__device__ __forceinline__ void dma16(const void* addr, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(addr), "s"(m0) : "memory");
 }
+__device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
+  const uint64_t ps = (uint64_t(hi) << 32) | uint64_t(lo);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ps), "s"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void dma4_s(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
+  const uint64_t ps = (uint64_t(hi) << 32) | uint64_t(lo);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(ps), "s"(m0)
+               : "memory");
+}
+__device__ __forceinline__ void dma4(const void* addr, uint32_t lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(m0) : "memory");
+}
+// Scalar load of one int (a wave-uniform address) and its wait, in one block: a vector load
+// would make the compiler wait for every outstanding vector-memory operation, the staged loads
+// in flight included.  (The general paged layout does look its rows up with vector loads: its
+// loads then wait for the previous step's, which have had a step to arrive.)
+__device__ __forceinline__ int sload_i32(const int32_t* p) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(a));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(a >> 32));
+  const uint64_t as = (uint64_t(hi) << 32) | uint64_t(lo);
+  int v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(as) : "memory");
+  return v;
+}
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier after this wave's LDS accesses have completed (the direct-to-LDS loads in
+// flight are left alone; a fence would wait for them).
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Staged steps are double buffered (loaders write buffer (n + 1) % 2 in step n).
 struct alignas(16) Smem8 {
-  uint8_t lat8[2][kStep][kDC];      // staged codes, chunk c of row t at c ^ swz32(t); also
-                                    // the output rows at the end (64 x 1 KB of bf16)
-  uint16_t rope[2][kStep][kDR];     // staged RoPE rows, chunk c of row t at c ^ rope_swz(t)
-  uint8_t p8[2][kRows][kStep];      // rounded probabilities [row][tok], p_swz
-  int32_t psc[2][kRows][2];         // E8M0 scale of each row's two 32-token halves
-  float ts[2][kStep];               // per-token scales
-  float alpha[2][kRows];            // rescale of the accumulators before the step
-  float lsum[kRows];
+  uint8_t lat8[kStages][kStep][kDC];   // staged codes, chunk c of row t at c ^ swz32(t); also
+                                       // the output rows at the end (64 x 1 KB of bf16)
+  uint16_t rope[kStages][kStep][kDR];  // staged RoPE rows, chunk c of row t at c ^ rope_swz(t)
+  float ts[kStages][kStep];            // per-token scales
+  uint8_t p8[2][kRows][kStep];         // rounded probabilities [row][tok], p_swz
+  int32_t psc[2][kRows][2];            // E8M0 byte of each (row, half) against its stream's reference
+  float mref[2][kRows][2];             // each half-stream's reference after the step
+  float fin_m[kRows][2], fin_l[kRows][2];
   int64_t prefix[kMaxPrefixBatch + 1];
   int64_t wave_tot[kThreads / 64];
 };
 static_assert(sizeof(Smem8::lat8) >= kRows * kDC * 2, "output staging does not fit");
-
-// A loader wave's registers for its 32 tokens of one step.
-struct Load8 {
-  u32x4 lat[16];  // load k: token 2 k + lane / 32, 16-byte chunk lane % 32
-  u32x4 rope[4];  // load j: token 8 j + lane / 8, 16-byte chunk lane % 8
-  float ts;       // scale of token lane % 32
-};
 
 template <int PK>
 __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, int b, int rb, int t_lo, int t_hi,
                                               int L, bool final_out, int64_t out_base) {
   int tid;
   asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(int(threadIdx.x)));
-  Ctx c;
-  c.b = b;
-  c.lane = tid & 63;
-  c.n = c.lane & 31;
-  c.h = c.lane >> 5;
-  c.w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  c.table = a.block_table;
-  c.max_blocks = a.max_blocks;
-  c.bs = a.block_size;
-  c.T = a.T;
-  c.t_hi = t_hi;
+  const int lane = tid & 63, cn = lane & 31, ch = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rows = a.sq * a.H;
   const int r0 = rb * kRows;
   const int nsteps = t_hi > t_lo ? (t_hi - t_lo + kStep - 1) / kStep : 0;
 
-  if (c.w == 4 || c.w == 5) {
-    // ================================ loader waves ===================================
-    const int l = c.w - 4;
-    auto lload = [&](Load8& r, int t0) {
-      const int th = t0 + kHalf * l;
-      if constexpr (PK == kPagedAny) {
-        const char* lat = static_cast<const char*>(a.c_kv);
-        const char* rope = static_cast<const char*>(a.k_rope);
-#pragma unroll
-        for (int k = 0; k < 16; ++k) r.lat[k] = ld16(lat + any_row(c, th + 2 * k + c.h) * kDC + 16 * c.n);
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          r.rope[j] = ld16(rope + any_row(c, th + 8 * j + (c.lane >> 3)) * (kDR * 2) + 16 * (c.lane & 7));
-        r.ts = a.kv_scale[any_row(c, th + c.n)];
-        return;
-      }
-      const char* lat_base;
-      const char* rope_base;
-      const char* sc_base;
-      uint32_t nrows, row0;
-      if constexpr (PK == kContig) {
-        const int64_t seq_row = int64_t(c.b) * c.T;
-        lat_base = static_cast<const char*>(a.c_kv) + seq_row * kDC;
-        rope_base = static_cast<const char*>(a.k_rope) + seq_row * (kDR * 2);
-        sc_base = reinterpret_cast<const char*>(a.kv_scale + seq_row);
-        nrows = uint32_t(c.t_hi);
-        row0 = uint32_t(th);
-      } else {
-        // The half lies inside one block (block_size a multiple of 32, th a multiple of 32).
-        const int blk = min(th, c.t_hi - 1) / c.bs;
-        const int blk_t0 = blk * c.bs;
-        const int64_t pool_row = int64_t(c.table[int64_t(c.b) * c.max_blocks + blk]) * c.bs;
-        lat_base = static_cast<const char*>(a.c_kv) + pool_row * kDC;
-        rope_base = static_cast<const char*>(a.k_rope) + pool_row * (kDR * 2);
-        sc_base = reinterpret_cast<const char*>(a.kv_scale + pool_row);
-        nrows = uint32_t(min(c.bs, c.t_hi - blk_t0));
-        row0 = uint32_t(th - blk_t0);
-      }
-      // Ranges end at the last valid row: rows past it read zeros.
-      const __amdgpu_buffer_rsrc_t rl = make_rsrc(lat_base, nrows * kDC);
-      const __amdgpu_buffer_rsrc_t rr = make_rsrc(rope_base, nrows * (kDR * 2));
-#pragma unroll
-      for (int k = 0; k < 16; ++k) r.lat[k] = buf_ld16(rl, (row0 + uint32_t(2 * k + c.h)) * kDC + 16 * c.n);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        r.rope[j] = buf_ld16(rr, (row0 + uint32_t(8 * j + (c.lane >> 3))) * (kDR * 2) + 16 * (c.lane & 7));
-      r.ts = buf_ld4f(make_rsrc(sc_base, nrows * 4), (row0 + uint32_t(c.n)) * 4);
-    };
-    auto lstage = [&](const Load8& r, int buf) {
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int row = kHalf * l + 2 * k + c.h;
-        *reinterpret_cast<u32x4*>(&sm.lat8[buf][row][16 * (c.n ^ swz32(row))]) = r.lat[k];
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = kHalf * l + 8 * j + (c.lane >> 3);
-        *reinterpret_cast<u32x4*>(&sm.rope[buf][row][8 * ((c.lane & 7) ^ rope_swz(row))]) = r.rope[j];
-      }
-      if (c.h == 0) sm.ts[buf][kHalf * l + c.n] = r.ts;
-    };
-    if (nsteps > 0) {
-      Load8 rx, ry;  // rx holds the even steps, ry the odd ones
-      lload(rx, t_lo);
-      lload(ry, t_lo + kStep);
-      lstage(rx, 0);
-      lload(rx, t_lo + 2 * kStep);
-      __syncthreads();
-      // Step n stages step n + 1 and loads step n + 3 in its place.
-      auto lstep = [&](Load8& r, int n) {
-        if (n + 1 < nsteps) lstage(r, (n + 1) % 2);
-        lload(r, t_lo + (n + 3) * kStep);
-        __syncthreads();
-      };
-      int n = 0;
-      for (; n + 1 < nsteps; n += 2) {
-        lstep(ry, n);
-        lstep(rx, n + 1);
-      }
-      if (n < nsteps) lstep(ry, n);
-    }
-    __syncthreads();  // row sums published
-  } else if (c.w < 2) {
+  if (w < 4) {
     // ================================ score waves ====================================
-    const int row = 32 * c.w + c.n;  // this lane's row of the workgroup
+    const int hf = w >> 1;             // this wave's half of every step
+    const int row = 32 * (w & 1) + cn;  // this lane's row of the workgroup
     // Query operands: q8[m] = the e4m3 codes of columns 64 m + 32 h .. + 31, rounded with the
     // scale qs[m / 2] of their 128-column slice (the partner lane holds the slice's other
     // half); qr[s] = RoPE dims 16 s + 8 h .. + 7 (bf16).
@@ -233,7 +167,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     {
       const int64_t qrow = int64_t(b) * rows + r0 + row;
       const uint16_t* ql = static_cast<const uint16_t*>(a.q_lat) + qrow * kDC;
-      const uint16_t* qp = static_cast<const uint16_t*>(a.q_rope) + qrow * kDR + 8 * c.h;
+      const uint16_t* qp = static_cast<const uint16_t*>(a.q_rope) + qrow * kDR + 8 * ch;
 #pragma unroll
       for (int s = 0; s < 4; ++s) qr[s] = __builtin_bit_cast(bf16x8, ld16(qp + 16 * s));
 #pragma unroll
@@ -241,7 +175,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
         bf16x8 x[8];  // x[4 mm + i]: columns 128 j + 64 mm + 32 h + 8 i .. + 7
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          x[i] = __builtin_bit_cast(bf16x8, ld16(ql + 128 * j + 64 * (i >> 2) + 32 * c.h + 8 * (i & 3)));
+          x[i] = __builtin_bit_cast(bf16x8, ld16(ql + 128 * j + 64 * (i >> 2) + 32 * ch + 8 * (i & 3)));
         float amax = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
@@ -265,26 +199,24 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     }
     const int iq = (r0 + row) / a.H;
     const int lim = min(min(max(L - a.sq + iq + 1, 0), L), t_hi);
-    const int iq_w = (r0 + 32 * c.w) / a.H;
+    const int iq_w = (r0 + 32 * (w & 1)) / a.H;
     const int lim_w = min(min(max(L - a.sq + iq_w + 1, 0), L), t_hi);
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;  // this half-stream's reference and sum
     const float scale_log2 = a.scale_log2;
 
-    // Operand offsets within a half (token n of the half is row 32 hf + n of the step; the
+    // Operand offsets within the half (token n of the half is row 32 hf + n of the step; the
     // swizzles depend on the low 4 row bits only): code product m reads chunks
     // 4 m + 2 h, 4 m + 2 h + 1 of token n; RoPE k-step s chunk (2 s + h) ^ rope_swz(n).
     int boff[8];  // [2 (m % 4) + e]: chunk 4 (m % 4) + 2 h + e, plus 256 bytes per 4 products
 #pragma unroll
-    for (int t = 0; t < 8; ++t) boff[t] = c.n * kDC + 16 * ((4 * (t >> 1) + 2 * c.h + (t & 1)) ^ swz32(c.n));
+    for (int t = 0; t < 8; ++t) boff[t] = cn * kDC + 16 * ((4 * (t >> 1) + 2 * ch + (t & 1)) ^ swz32(cn));
     int roff[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) roff[t] = c.n * kDR + 8 * ((2 * t + c.h) ^ rope_swz(c.n));
-    const int prow_off = 4 * c.h;  // byte of this lane's 4 tokens within an 8-token group
+    for (int t = 0; t < 4; ++t) roff[t] = cn * kDR + 8 * ((2 * t + ch) ^ rope_swz(cn));
+    const int g = p_swz(row);
 
-    // Scores, softmax and rounded probabilities of half hf of step n.  Returns the half's
-    // E8M0 block scale (before any later rescale) and sets alpha to the accumulator rescale.
-    auto half = [&](int n, int hf, float& alpha) -> int {
-      const int buf = n % 2;
+    auto score = [&](int n) {
+      const int buf = n % kStages;
       const uint8_t* l8 = &sm.lat8[buf][kHalf * hf][0];
       const uint16_t* rt = &sm.rope[buf][kHalf * hf][0];
       f32x16 accr, accq[4];
@@ -323,7 +255,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       // Lane (n, h) holds tokens 8 i + 4 h + r (e = 4 i + r) of row `row` in this half.
       f32x4 tsv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tsv[i] = *reinterpret_cast<const f32x4*>(&sm.ts[buf][kHalf * hf + 8 * i + 4 * c.h]);
+      for (int i = 0; i < 4; ++i) tsv[i] = *reinterpret_cast<const f32x4*>(&sm.ts[buf][kHalf * hf + 8 * i + 4 * ch]);
       float sv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -334,7 +266,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       if (t0 + kHalf > lim_w) {
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (t0 + 8 * (e >> 2) + 4 * c.h + (e & 3) >= lim) sv[e] = -INFINITY;
+          if (t0 + 8 * (e >> 2) + 4 * ch + (e & 3) >= lim) sv[e] = -INFINITY;
       }
       float tmax = sv[0];
 #pragma unroll
@@ -345,7 +277,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
         tmax = fmaxf(x0, x1);
       }
       tmax *= scale_log2;
-      alpha = 1.f;
+      float alpha = 1.f;
       if (tmax > m_run + kTau) {
         const float m_new = ceilf(tmax);
         alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, int(m_run - m_new));
@@ -371,58 +303,120 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       const int sbyte = max(int((__float_as_uint(pmax) >> 23) & 0xFF) - 7, 0);
       const float mul = __uint_as_float(uint32_t(254 - sbyte) << 23);
       const int pbuf = n & 1;
-      const int g = p_swz(row);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i] * mul, pw[4 * i + 1] * mul, 0, false);
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i + 2] * mul, pw[4 * i + 3] * mul, wd, true);
         const int chunk = 2 * hf + (i >> 1);
-        *reinterpret_cast<int*>(&sm.p8[pbuf][row][16 * (chunk ^ g) + 8 * (i & 1) + prow_off]) = wd;
+        *reinterpret_cast<int*>(&sm.p8[pbuf][row][16 * (chunk ^ g) + 8 * (i & 1) + 4 * ch]) = wd;
       }
-      return sbyte;
-    };
-
-    auto step = [&](int n) {
-      float a0, a1;
-      const int s0 = half(n, 0, a0);
-      const float m_mid = m_run;
-      const int s1 = half(n, 1, a1);
-      // Half 0 was rounded against the reference after half 0; when half 1 moved it, the
-      // exact power-of-two rescale goes into half 0's block scale (a scale below 2^-127
-      // stays at 2^-127: such weights are negligible against the new reference).
-      int s0f = s0;
-      if (a1 != 1.f) s0f = m_mid == -INFINITY ? 0 : max(s0 + int(m_mid - m_run), 0);
-      if (c.h == 0) {
-        const int pbuf = n & 1;
-        sm.psc[pbuf][row][0] = s0f;
-        sm.psc[pbuf][row][1] = s1;
-        sm.alpha[pbuf][row] = a0 * a1;
+      if (ch == 0) {
+        sm.psc[pbuf][row][hf] = sbyte;
+        sm.mref[pbuf][row][hf] = m_run;
       }
     };
     if (nsteps > 0) {
-      __syncthreads();  // step 0 staged
+      barrier_lds();  // step 0 staged
       for (int n = 0; n < nsteps; ++n) {
-        step(n);
-        __syncthreads();
+        score(n);
+        barrier_lds();
       }
     }
-    // Row sum over both lane halves, log-sum-exp.
+    // This stream's sum over both lane halves; the two streams of a row meet after the barrier.
     float x0 = l_run, x1 = l_run;
     permlane32_swap(x0, x1);
-    const float l_tot = x0 + x1;
-    if (c.h == 0) {
-      sm.lsum[row] = l_tot;
-      const float lse2 = l_tot > 0.f ? m_run + log2f(l_tot) : -INFINITY;
+    if (ch == 0) {
+      sm.fin_m[row][hf] = m_run;
+      sm.fin_l[row][hf] = x0 + x1;
+    }
+    __syncthreads();  // row sums published
+    if (hf == 0 && ch == 0) {
+      const float m0 = sm.fin_m[row][0], m1 = sm.fin_m[row][1];
+      const float M = fmaxf(m0, m1);
+      float lt = 0.f;
+      if (M != -INFINITY) {
+        if (m0 != -INFINITY) lt += sm.fin_l[row][0] * __builtin_amdgcn_ldexpf(1.f, int(m0 - M));
+        if (m1 != -INFINITY) lt += sm.fin_l[row][1] * __builtin_amdgcn_ldexpf(1.f, int(m1 - M));
+      }
+      const float lse2 = lt > 0.f ? M + log2f(lt) : -INFINITY;
       if (final_out) {
         if (a.lse) a.lse[out_base + r0 + row] = lse2 * kLn2;
       } else {
         a.part_lse[out_base + r0 + row] = lse2;
       }
     }
-    __syncthreads();  // row sums published
   } else {
     // ================================ output waves ===================================
-    const int q = (c.w & 1) + 2 * (c.w >> 2);
+    const int q = w - 4;  // column quarter and share of the staged rows
+    // ---------------------------------------------------------------- staging
+    // Wave q stages rows 16 q .. 16 q + 15 of every step (tokens past the piece's last one
+    // are clamped to it; the softmax masks them): latent rows two per load (lane i: row
+    // 16 q + 2 k + i / 32, 16-byte chunk i % 32 fetched from chunk (i % 32) ^ swz32(row)), RoPE
+    // rows eight per load (lane i: row 16 q + 8 k + i / 8, chunk (i % 8) ^ rope_swz(row)) and
+    // the 16 scales (lanes 0 .. 15).
+    const char* lat_g = static_cast<const char*>(a.c_kv);
+    const char* rope_g = static_cast<const char*>(a.k_rope);
+    const char* ts_g = reinterpret_cast<const char*>(a.kv_scale);
+    const int32_t* tab = a.block_table + int64_t(b) * a.max_blocks;
+    auto stage = [&](int n) {
+      const int tq = t_lo + n * kStep + 16 * q;  // token of this wave's first row
+      const int tl = t_hi - 1;
+      const int buf = n % kStages;
+      if constexpr (PK == kPagedAny) {
+        // Rows looked up lane by lane.
+        auto crow = [&](int j) -> int64_t {
+          const int t = min(tq + j, tl);
+          return int64_t(tab[t / a.block_size]) * a.block_size + t % a.block_size;
+        };
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int j = 2 * k + ch;
+          dma16(lat_g + crow(j) * kDC + 16 * (cn ^ swz32(16 * q + j)), lds_addr(&sm.lat8[buf][16 * q + 2 * k][0]));
+        }
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int j = 8 * k + (lane >> 3);
+          dma16(rope_g + crow(j) * (kDR * 2) + 16 * ((lane & 7) ^ rope_swz(16 * q + j)),
+                lds_addr(&sm.rope[buf][16 * q + 8 * k][0]));
+        }
+        const int64_t cts = crow(lane & 15);
+        if (lane < 16) dma4(ts_g + cts * 4, lds_addr(&sm.ts[buf][16 * q]));
+        return;
+      }
+      // One base per wave and step (the sequence, or the block holding the wave's 16 rows
+      // and the clamp target: block_size a multiple of 32, halves 32-aligned), 32-bit offsets
+      // from it (a sequence's rows span less than 2 GiB).
+      int64_t base_row;
+      int t_base;
+      if constexpr (PK == kContig) {
+        base_row = int64_t(b) * a.T;
+        t_base = 0;
+      } else {
+        const int blk = min(tq, tl) / a.block_size;
+        base_row = int64_t(sload_i32(tab + blk)) * a.block_size;
+        t_base = blk * a.block_size;
+      }
+      auto roff = [&](int j) { return uint32_t(min(tq + j, tl) - t_base); };
+      const char* lat_b = lat_g + base_row * kDC;
+      const char* rope_b = rope_g + base_row * (kDR * 2);
+      const char* ts_b = ts_g + base_row * 4;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = 2 * k + ch;
+        dma16_s(lat_b, roff(j) * kDC + uint32_t(16 * (cn ^ swz32(16 * q + j))),
+                lds_addr(&sm.lat8[buf][16 * q + 2 * k][0]));
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = 8 * k + (lane >> 3);
+        dma16_s(rope_b, roff(j) * (kDR * 2) + uint32_t(16 * ((lane & 7) ^ rope_swz(16 * q + j))),
+                lds_addr(&sm.rope[buf][16 * q + 8 * k][0]));
+      }
+      const uint32_t ots = roff(lane & 15) * 4;
+      if (lane < 16) dma4_s(ts_b, ots, lds_addr(&sm.ts[buf][16 * q]));
+    };
+
+    // ---------------------------------------------------------------- value product
     f32x16 oacc[4][2];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
@@ -435,29 +429,30 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     // the step in bytes 0 .. 15 and tokens 32 + 16 h .. 32 + 16 h + 15 in bytes 16 .. 31.
     // Read j (bytes 8 j .. 8 j + 7): the 16-lane group G reads columns 16 (G & 1) + (0..15) of
     // tokens 16 (G >> 1) + 8 (j & 1) + 32 (j >> 1) + (0..7).
-    const int G = c.lane >> 4, gi = c.lane & 15;
-    const int tr_row = 16 * (G >> 1) + (gi >> 1);
-    int voff[4][4];
+    const int G = lane >> 4, gi = lane & 15;
+    // Token 16 (G >> 1) + (gi >> 1) + 8 (j & 1) + 32 (j >> 1): its swizzle depends on j & 1 only
+    // (the low 4 bits) and the 32 (j >> 1) rows are an immediate offset.  Column block cb's
+    // chunk is u + 2 cb with u = 8 q + (G & 1) (bits 1 and 2 clear), so its swizzled byte
+    // offset is 16 ((u ^ swz) ^ 2 cb): one base per j & 1, XORed with 32 cb.
+    const int tok0 = 16 * (G >> 1) + (gi >> 1);
+    const int u = 8 * q + (G & 1);
+    int vb[2];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int tok = tr_row + 8 * (j & 1) + 32 * (j >> 1);
-        const int col = kCols * q + 32 * cb + 16 * (G & 1) + 8 * (gi & 1);
-        voff[cb][j] = tok * kDC + 16 * ((col >> 4) ^ swz32(tok)) + (col & 15);
-      }
+    for (int jo = 0; jo < 2; ++jo)
+      vb[jo] = (tok0 + 8 * jo) * kDC + 8 * (gi & 1) + 16 * (u ^ swz32(tok0 + 8 * jo));
     v8i vop[4];
     auto read_v = [&](int n) {
-      const uint8_t* vt = &sm.lat8[n % 2][0][0];
+      const uint8_t* vt = &sm.lat8[n % kStages][0][0];
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x2 v = lds_read_tr8(vt + voff[cb][j]);
+          const u32x2 v = lds_read_tr8(vt + (vb[j & 1] ^ (32 * cb)) + 32 * (j >> 1) * kDC);
           vop[cb][2 * j] = int(v[0]);
           vop[cb][2 * j + 1] = int(v[1]);
         }
     };
+    float m_acc[2] = {-INFINITY, -INFINITY};  // the accumulator's reference of rows 32 rb2 + n
     auto pv = [&](int n) {
       const int buf = n & 1;
       float al[2];
@@ -465,14 +460,22 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       v8i pb[2];
 #pragma unroll
       for (int rb2 = 0; rb2 < 2; ++rb2) {
-        const int prow = 32 * rb2 + c.n;
-        al[rb2] = sm.alpha[buf][prow];
-        sc[rb2] = sm.psc[buf][prow][c.h];
-        const uint8_t* pr = &sm.p8[buf][prow][0];
+        const int prow = 32 * rb2 + cn;
+        const float m0 = sm.mref[buf][prow][0], m1 = sm.mref[buf][prow][1];
+        const float mn = fmaxf(m0, m1);
+        al[rb2] = mn == m_acc[rb2] ? 1.f
+                  : m_acc[rb2] == -INFINITY ? 0.f
+                                            : __builtin_amdgcn_ldexpf(1.f, int(m_acc[rb2] - mn));
+        m_acc[rb2] = mn;
+        // This lane's half: its block scale, lowered by the stream's distance to the
+        // accumulator's reference (exact: integers in base 2).
+        const float mh = ch ? m1 : m0;
+        sc[rb2] = mh == -INFINITY ? 0 : max(sm.psc[buf][prow][ch] + int(mh - mn), 0);
         // B operand (P^T): row prow, tokens 16 h .. + 15 (chunk h) and 32 + 16 h .. + 15
         // (chunk 2 + h), in the instruction's K order; the lane's scale is that of half h.
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(pr + 16 * (c.h ^ p_swz(prow)));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(pr + 16 * ((2 + c.h) ^ p_swz(prow)));
+        const uint8_t* pr = &sm.p8[buf][prow][0];
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(pr + 16 * (ch ^ p_swz(prow)));
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(pr + 16 * ((2 + ch) ^ p_swz(prow)));
         pb[rb2] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
       }
       if (__any((al[0] != 1.f) | (al[1] != 1.f))) {
@@ -489,23 +492,44 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
               __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[cb], pb[rb2], oacc[cb][rb2], 0, 0, 0, 127, 0, sc[rb2]);
     };
     if (nsteps > 0) {
-      __syncthreads();  // step 0 staged
-      read_v(0);
-      __syncthreads();  // step 0 scored
-      for (int n = 1; n < nsteps; ++n) {
-        pv(n - 1);
+      // Loads run two steps ahead: step k goes to buffer k % 3 in step k - 2 (the prologue
+      // issues steps 0 and 1), and each step ends by waiting for the next one's loads.
+      stage(0);
+      if (nsteps > 1) {
+        stage(1);
+        wait_vm<kLoadsPerStep>();
+      } else {
+        wait_vm<0>();
+      }
+      barrier_lds();  // step 0 staged
+      for (int n = 0; n < nsteps; ++n) {
+        const bool more = n + 2 < nsteps;
+        if (more) stage(n + 2);
+        if (n > 0) pv(n - 1);
         read_v(n);
-        __syncthreads();
+        if (more) wait_vm<kLoadsPerStep>();
+        else wait_vm<0>();
+        barrier_lds();  // step n scored, step n + 1 staged
       }
       pv(nsteps - 1);
     }
     __syncthreads();  // row sums published
+    float lt[2];
+#pragma unroll
+    for (int rb2 = 0; rb2 < 2; ++rb2) {
+      const int prow = 32 * rb2 + cn;
+      const float m0 = sm.fin_m[prow][0], m1 = sm.fin_m[prow][1];
+      lt[rb2] = 0.f;
+      if (m_acc[rb2] != -INFINITY) {
+        if (m0 != -INFINITY) lt[rb2] += sm.fin_l[prow][0] * __builtin_amdgcn_ldexpf(1.f, int(m0 - m_acc[rb2]));
+        if (m1 != -INFINITY) lt[rb2] += sm.fin_l[prow][1] * __builtin_amdgcn_ldexpf(1.f, int(m1 - m_acc[rb2]));
+      }
+    }
     uint16_t* os = reinterpret_cast<uint16_t*>(&sm.lat8[0][0][0]);
 #pragma unroll
     for (int rb2 = 0; rb2 < 2; ++rb2) {
-      const float lt = sm.lsum[32 * rb2 + c.n];
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      const int lrow = 32 * rb2 + c.n;
+      const float inv = lt[rb2] > 0.f ? 1.f / lt[rb2] : 0.f;
+      const int lrow = 32 * rb2 + cn;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -513,7 +537,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
           const int chunk = 16 * q + 4 * cb + i;
           const f32x4 v = f32x4{oacc[cb][rb2][4 * i], oacc[cb][rb2][4 * i + 1], oacc[cb][rb2][4 * i + 2],
                                 oacc[cb][rb2][4 * i + 3]} * inv;
-          *reinterpret_cast<u32x2*>(os + lrow * kDC + 8 * (chunk ^ (lrow & 15)) + 4 * c.h) =
+          *reinterpret_cast<u32x2*>(os + lrow * kDC + 8 * (chunk ^ (lrow & 15)) + 4 * ch) =
               u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         }
     }
@@ -524,9 +548,9 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     uint16_t* dst = static_cast<uint16_t*>(final_out ? a.o_lat : a.part_o);
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const int lrow = 8 * c.w + k;
-      const u32x4 v = *reinterpret_cast<const u32x4*>(os + lrow * kDC + 8 * (c.lane ^ (lrow & 15)));
-      *reinterpret_cast<u32x4*>(dst + (out_base + r0 + lrow) * kDC + 8 * c.lane) = v;
+      const int lrow = 8 * w + k;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(os + lrow * kDC + 8 * (lane ^ (lrow & 15)));
+      *reinterpret_cast<u32x4*>(dst + (out_base + r0 + lrow) * kDC + 8 * lane) = v;
     }
   }
   __syncthreads();  // the next piece stages into these buffers
