@@ -14,7 +14,8 @@ Prints one JSON line:
   roofline     the decode call (its kernels) against the 8 TB/s HBM peak, timed with HIP
                events around each call inside the timed loop
   configs      the decode call alone on the other full-size workloads (paged variable-length,
-               long context, speculative fp8), each with its own roofline, plus the headline's
+               long context, speculative fp8), each with its own roofline (the fp8 one also
+               with both products on the fp8 matrix instruction, labelled), plus the headline's
                decode call with its cache left warm in the last-level cache (labelled)
   cpu_baseline the CPU oracle (fp64 numpy, absorbed form) on a bounded sample of the
                same workload, on this host's cores, and on one core
@@ -36,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 flop / clk / CU
+FP8_MFMA_PEAK_TFS = 5033.2   # twice the bf16 rate (dense fp8)
 
 
 def bytes_of(dtype: str) -> int:
@@ -150,6 +152,25 @@ def side_workload(cfg, calls: int, warmup: int) -> dict:
     del w
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+    if cfg.kv_dtype == "fp8":
+        # The opt-in approximation with both products on the fp8 matrix instruction
+        # (dims.fp8_scores = 2): same inputs, its own rounding of the query and of P.
+        w8 = DeviceWorkload(inp, replicas=1, fp8_scores=2)
+        w8.absorb_q()
+        ms8 = time_decode_calls(w8, calls, warmup)
+        avg8 = float(np.mean(ms8))
+        tf8 = wc["attn_flops"] / (avg8 * 1e-3) / 1e12
+        roof8 = decode_roofline(cfg, wc, avg8)
+        roof8["fp8_peak_frac"] = round(tf8 / FP8_MFMA_PEAK_TFS, 4)
+        out["fp8_products"] = {
+            "note": "dims.fp8_scores = 2: query and probabilities rounded to e4m3, both products on the fp8 "
+                    "matrix instruction (an approximation, not the exact path above)",
+            "decode_call_us": round(avg8 * 1e3, 2), "tflops": round(tf8, 2),
+            "decode_tokens_per_s": round(cfg.batch * cfg.q_len / (avg8 * 1e-3), 1), "roofline": roof8}
+        print(f"[bench] {cfg.name} fp8 products: decode call {avg8 * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del w8
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     return out
 
 
