@@ -36,6 +36,8 @@
 // One barrier per step: in step n the output waves issue the loads of step n + 2, multiply
 // step n - 1 and read the V^T operands of step n, and wait for step n + 1's loads; the score
 // waves score step n.
+#include <type_traits>
+
 #include "device_common.h"
 #include "mfma_common.h"
 #include "mla_internal.h"
@@ -134,16 +136,31 @@ struct alignas(16) Smem8 {
                                        // the output rows at the end (64 x 1 KB of bf16)
   uint16_t rope[kStages][kStep][kDR];  // staged RoPE rows, chunk c of row t at c ^ rope_swz(t)
   float ts[kStages][kStep];            // per-token scales
-  uint8_t p8[2][kRows][kStep];         // rounded probabilities [row][tok], p_swz
-  int32_t psc[2][kRows][2];            // E8M0 byte of each (row, half) against its stream's reference
-  float mref[2][kRows][2];             // each half-stream's reference after the step
+  // Probabilities of the step, double buffered: bf16 [row][tok] (8-token chunk c of row r at
+  // c ^ p16_swz(r)) for a bf16 value product, or e4m3 codes [row][tok] (16-byte chunk c of row
+  // r at c ^ p_swz(r)) in the first 4 KB of each buffer for the fp8 one.
+  uint16_t p[2][kRows][kStep];
+  int32_t psc[2][kRows][2];            // fp8 values: E8M0 byte of each (row, half) against its stream's reference
+  float mref[2][kRows][2];             // reference each half-stream used in the step
   float fin_m[kRows][2], fin_l[kRows][2];
   int64_t prefix[kMaxPrefixBatch + 1];
   int64_t wave_tot[kThreads / 64];
 };
 static_assert(sizeof(Smem8::lat8) >= kRows * kDC * 2, "output staging does not fit");
 
-template <int PK>
+__device__ __forceinline__ int p16_swz(int r) { return (r >> 1) & 7; }
+
+__device__ __forceinline__ bf16x8 scale_bf16x8(bf16x8 v, float f) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = __bf16(float(v[e]) * f);
+  return r;
+}
+
+// The latent score term is an fp8 product (query rounded per 128-column slice).  PV8: the
+// value product in fp8 as well (P rounded with block scales), else in bf16 on the codes
+// converted exactly (P times the token scale rounded to bf16).
+template <int PK, bool PV8>
 __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, int b, int rb, int t_lo, int t_hi,
                                               int L, bool final_out, int64_t out_base) {
   int tid;
@@ -153,6 +170,9 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
   const int rows = a.sq * a.H;
   const int r0 = rb * kRows;
   const int nsteps = t_hi > t_lo ? (t_hi - t_lo + kStep - 1) / kStep : 0;
+  uint8_t(*p8)[kRows][kStep] = reinterpret_cast<uint8_t(*)[kRows][kStep]>(&sm.p[0][0][0]);
+  auto p8buf = [&](int buf) { return reinterpret_cast<uint8_t(*)[kStep]>(reinterpret_cast<uint8_t*>(&sm.p[buf][0][0])); };
+  (void)p8;
 
   if (w < 4) {
     // ================================ score waves ====================================
@@ -170,53 +190,66 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       const uint16_t* qp = static_cast<const uint16_t*>(a.q_rope) + qrow * kDR + 8 * ch;
 #pragma unroll
       for (int s = 0; s < 4; ++s) qr[s] = __builtin_bit_cast(bf16x8, ld16(qp + 16 * s));
+      {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        bf16x8 x[8];  // x[4 mm + i]: columns 128 j + 64 mm + 32 h + 8 i .. + 7
+        for (int j = 0; j < 4; ++j) {
+          bf16x8 x[8];  // x[4 mm + i]: columns 128 j + 64 mm + 32 h + 8 i .. + 7
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-          x[i] = __builtin_bit_cast(bf16x8, ld16(ql + 128 * j + 64 * (i >> 2) + 32 * ch + 8 * (i & 3)));
-        float amax = 0.f;
+          for (int i = 0; i < 8; ++i)
+            x[i] = __builtin_bit_cast(bf16x8, ld16(ql + 128 * j + 64 * (i >> 2) + 32 * ch + 8 * (i & 3)));
+          float amax = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+          for (int i = 0; i < 8; ++i)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(float(x[i][e])));
-        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-        qs[j] = amax > 0.f ? amax * (1.f / 448.f) : 1.f;
-        const float inv = amax > 0.f ? 448.f / amax : 1.f;
+            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(float(x[i][e])));
+          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+          qs[j] = amax > 0.f ? amax * (1.f / 448.f) : 1.f;
+          const float inv = amax > 0.f ? 448.f / amax : 1.f;
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
+          for (int mm = 0; mm < 2; ++mm)
 #pragma unroll
-          for (int d = 0; d < 8; ++d) {  // dword d: columns 64 m + 32 h + 4 d .. + 3
-            const bf16x8 src = x[4 * mm + d / 2];
-            const int o = 4 * (d % 2);
-            auto qf = [&](int e) { return fminf(fmaxf(float(src[o + e]) * inv, -448.f), 448.f); };
-            int wd = __builtin_amdgcn_cvt_pk_fp8_f32(qf(0), qf(1), 0, false);
-            wd = __builtin_amdgcn_cvt_pk_fp8_f32(qf(2), qf(3), wd, true);
-            q8[2 * j + mm][d] = wd;
-          }
+            for (int d = 0; d < 8; ++d) {  // dword d: columns 64 m + 32 h + 4 d .. + 3
+              const bf16x8 src = x[4 * mm + d / 2];
+              const int o = 4 * (d % 2);
+              auto qf = [&](int e) { return fminf(fmaxf(float(src[o + e]) * inv, -448.f), 448.f); };
+              int wd = __builtin_amdgcn_cvt_pk_fp8_f32(qf(0), qf(1), 0, false);
+              wd = __builtin_amdgcn_cvt_pk_fp8_f32(qf(2), qf(3), wd, true);
+              q8[2 * j + mm][d] = wd;
+            }
+        }
       }
     }
     const int iq = (r0 + row) / a.H;
     const int lim = min(min(max(L - a.sq + iq + 1, 0), L), t_hi);
     const int iq_w = (r0 + 32 * (w & 1)) / a.H;
     const int lim_w = min(min(max(L - a.sq + iq_w + 1, 0), L), t_hi);
-    float m_run = -INFINITY, l_run = 0.f;  // this half-stream's reference and sum
+    float ref = -INFINITY, l_run = 0.f;  // this half-stream's reference and sum
     const float scale_log2 = a.scale_log2;
 
     // Operand offsets within the half (token n of the half is row 32 hf + n of the step; the
-    // swizzles depend on the low 4 row bits only): code product m reads chunks
-    // 4 m + 2 h, 4 m + 2 h + 1 of token n; RoPE k-step s chunk (2 s + h) ^ rope_swz(n).
+    // swizzles depend on the low 4 row bits only): code product m reads chunks 4 m + 2 h and
+    // 4 m + 2 h + 1 of token n; RoPE k-step s reads chunk (2 s + h) ^ rope_swz(n).
     int boff[8];  // [2 (m % 4) + e]: chunk 4 (m % 4) + 2 h + e, plus 256 bytes per 4 products
 #pragma unroll
     for (int t = 0; t < 8; ++t) boff[t] = cn * kDC + 16 * ((4 * (t >> 1) + 2 * ch + (t & 1)) ^ swz32(cn));
     int roff[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) roff[t] = cn * kDR + 8 * ((2 * t + ch) ^ rope_swz(cn));
-    const int g = p_swz(row);
 
     auto score = [&](int n) {
       const int buf = n % kStages;
+      const int pbuf = n & 1;
+      // bf16 values: the two half-streams share a reference (the larger of their references
+      // of the last step), so that they differ only in a step where one of them moves its own
+      // and the output waves rarely rescale probabilities.  fp8 values absorb any difference
+      // in the block scales, and each stream keeps its own.
+      if (!PV8 && n > 0) {
+        const float R = fmaxf(sm.mref[pbuf ^ 1][row][0], sm.mref[pbuf ^ 1][row][1]);
+        if (R > ref) {
+          l_run = ref == -INFINITY ? 0.f : l_run * __builtin_amdgcn_ldexpf(1.f, int(ref - R));
+          ref = R;
+        }
+      }
       const uint8_t* l8 = &sm.lat8[buf][kHalf * hf][0];
       const uint16_t* rt = &sm.rope[buf][kHalf * hf][0];
       f32x16 accr, accq[4];
@@ -226,31 +259,33 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
 #pragma unroll
         for (int j = 0; j < 4; ++j) accq[j][e] = 0.f;
       }
-      auto codes = [&](int m) {
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(l8 + 256 * (m >> 2) + boff[2 * (m & 3)]);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(l8 + 256 * (m >> 2) + boff[2 * (m & 3) + 1]);
-        return v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-      };
-      // Eight fp8 products (one accumulator per 128-column slice), codes read two products
-      // ahead, then the four bf16 RoPE products.
-      v8i ring8[2] = {codes(0), codes(1)};
+      {
+        auto codes = [&](int m) {
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(l8 + 256 * (m >> 2) + boff[2 * (m & 3)]);
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(l8 + 256 * (m >> 2) + boff[2 * (m & 3) + 1]);
+          return v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+        };
+        // Eight fp8 products (one accumulator per 128-column slice), codes read two products
+        // ahead, then the four bf16 RoPE products.
+        v8i ring8[2] = {codes(0), codes(1)};
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const v8i av = ring8[m & 1];
-        if (m + 2 < 8) ring8[m & 1] = codes(m + 2);
-        accq[m >> 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, q8[m], accq[m >> 1], 0, 0, 0, 127, 0, 127);
-      }
-      bf16x8 ar[4];
+        for (int m = 0; m < 8; ++m) {
+          const v8i av = ring8[m & 1];
+          if (m + 2 < 8) ring8[m & 1] = codes(m + 2);
+          accq[m >> 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, q8[m], accq[m >> 1], 0, 0, 0, 127, 0, 127);
+        }
+        bf16x8 ar[4];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) ar[s] = *reinterpret_cast<const bf16x8*>(rt + roff[s]);
+        for (int s = 0; s < 4; ++s) ar[s] = *reinterpret_cast<const bf16x8*>(rt + roff[s]);
 #pragma unroll
-      for (int s = 0; s < 4; ++s) accr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[s], qr[s], accr, 0, 0, 0);
+        for (int s = 0; s < 4; ++s) accr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[s], qr[s], accr, 0, 0, 0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int i = 0; i < 2; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        for (int m = 0; m < 8; ++m) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
       }
       // Lane (n, h) holds tokens 8 i + 4 h + r (e = 4 i + r) of row `row` in this half.
       f32x4 tsv[4];
@@ -277,43 +312,49 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
         tmax = fmaxf(x0, x1);
       }
       tmax *= scale_log2;
-      float alpha = 1.f;
-      if (tmax > m_run + kTau) {
-        const float m_new = ceilf(tmax);
-        alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_ldexpf(1.f, int(m_run - m_new));
-        m_run = m_new;
+      if (tmax > ref + kTau) {
+        const float r_new = ceilf(tmax);
+        l_run = ref == -INFINITY ? 0.f : l_run * __builtin_amdgcn_ldexpf(1.f, int(ref - r_new));
+        ref = r_new;
       }
-      const float neg_m = m_run == -INFINITY ? 0.f : -m_run;
+      const float neg_m = ref == -INFINITY ? 0.f : -ref;
       float pw[16], psum = 0.f, pmax = 0.f;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, neg_m));
-        psum += p;
-        pw[e] = p * tsv[e >> 2][e & 3];
-        pmax = fmaxf(pmax, pw[e]);
+        const float pe = __builtin_amdgcn_exp2f(fmaf(sv[e], scale_log2, neg_m));
+        psum += pe;
+        pw[e] = pe * tsv[e >> 2][e & 3];
+        if constexpr (PV8) pmax = fmaxf(pmax, pw[e]);
       }
-      l_run = l_run * alpha + psum;
-      {
-        float x0 = pmax, x1 = pmax;
-        permlane32_swap(x0, x1);
-        pmax = fmaxf(x0, x1);
-      }
-      // Block scale 2^e with e = floor(log2 pmax) - 7: E8M0 byte bexp - 7 (at least 0), and
-      // the values are multiplied by 2^-e before rounding.
-      const int sbyte = max(int((__float_as_uint(pmax) >> 23) & 0xFF) - 7, 0);
-      const float mul = __uint_as_float(uint32_t(254 - sbyte) << 23);
-      const int pbuf = n & 1;
+      l_run += psum;
+      if constexpr (PV8) {
+        {
+          float x0 = pmax, x1 = pmax;
+          permlane32_swap(x0, x1);
+          pmax = fmaxf(x0, x1);
+        }
+        // Block scale 2^e with e = floor(log2 pmax) - 7: E8M0 byte bexp - 7 (at least 0), and
+        // the values are multiplied by 2^-e before rounding.
+        const int sbyte = max(int((__float_as_uint(pmax) >> 23) & 0xFF) - 7, 0);
+        const float mul = __uint_as_float(uint32_t(254 - sbyte) << 23);
+        const int g = p_swz(row);
+        uint8_t(*pp)[kStep] = p8buf(pbuf);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i] * mul, pw[4 * i + 1] * mul, 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i + 2] * mul, pw[4 * i + 3] * mul, wd, true);
-        const int chunk = 2 * hf + (i >> 1);
-        *reinterpret_cast<int*>(&sm.p8[pbuf][row][16 * (chunk ^ g) + 8 * (i & 1) + 4 * ch]) = wd;
+        for (int i = 0; i < 4; ++i) {
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i] * mul, pw[4 * i + 1] * mul, 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(pw[4 * i + 2] * mul, pw[4 * i + 3] * mul, wd, true);
+          const int chunk = 2 * hf + (i >> 1);
+          *reinterpret_cast<int*>(&pp[row][16 * (chunk ^ g) + 8 * (i & 1) + 4 * ch]) = wd;
+        }
+        if (ch == 0) sm.psc[pbuf][row][hf] = sbyte;
+      } else {
+        const int g = p16_swz(row);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<u32x2*>(&sm.p[pbuf][row][8 * ((4 * hf + i) ^ g) + 4 * ch]) =
+              u32x2{pack_bf16x2(pw[4 * i], pw[4 * i + 1]), pack_bf16x2(pw[4 * i + 2], pw[4 * i + 3])};
       }
-      if (ch == 0) {
-        sm.psc[pbuf][row][hf] = sbyte;
-        sm.mref[pbuf][row][hf] = m_run;
-      }
+      if (ch == 0) sm.mref[pbuf][row][hf] = ref;
     };
     if (nsteps > 0) {
       barrier_lds();  // step 0 staged
@@ -326,7 +367,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     float x0 = l_run, x1 = l_run;
     permlane32_swap(x0, x1);
     if (ch == 0) {
-      sm.fin_m[row][hf] = m_run;
+      sm.fin_m[row][hf] = ref;
       sm.fin_l[row][hf] = x0 + x1;
     }
     __syncthreads();  // row sums published
@@ -424,22 +465,26 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       for (int rb2 = 0; rb2 < 2; ++rb2)
 #pragma unroll
         for (int e = 0; e < 16; ++e) oacc[cb][rb2][e] = 0.f;
-    // V^T operand of column block cb (A of the 32 x 32 x 64 product): lane l holds column
-    // 128 q + 32 cb + l % 32 and, in the instruction's K order, tokens 16 h .. 16 h + 15 of
-    // the step in bytes 0 .. 15 and tokens 32 + 16 h .. 32 + 16 h + 15 in bytes 16 .. 31.
-    // Read j (bytes 8 j .. 8 j + 7): the 16-lane group G reads columns 16 (G & 1) + (0..15) of
-    // tokens 16 (G >> 1) + 8 (j & 1) + 32 (j >> 1) + (0..7).
+    // V^T operands of column block cb, read from the staged codes by 8-bit transposed reads
+    // (the 16-lane group G covers columns 16 (G & 1) + (0..15) of 8 tokens, lane gi receiving
+    // column gi).  fp8 values (A of the 32 x 32 x 64 product): lane l holds column
+    // 128 q + 32 cb + l % 32 and, in the instruction's K order, tokens 16 h .. 16 h + 15 of the
+    // step in bytes 0 .. 15 and 32 + 16 h .. 32 + 16 h + 15 in bytes 16 .. 31; read j covers
+    // tokens 16 (G >> 1) + 8 (j & 1) + 32 (j >> 1) + (0..7).  bf16 values (A of 32 x 32 x 16,
+    // converted before the product): k-step ks takes tokens 16 ks + 8 h + (0..7), read j = ks.
+    // A token's swizzle depends on its low 4 bits only, so the reads differ by immediate
+    // offsets plus, for fp8, one of two bases.  Column block cb's chunk is u + 2 cb with
+    // u = 8 q + (G & 1) (bits 1 and 2 clear), so its swizzled byte offset is 16 ((u ^ swz) ^ 2 cb):
+    // the base XORed with 32 cb.
     const int G = lane >> 4, gi = lane & 15;
-    // Token 16 (G >> 1) + (gi >> 1) + 8 (j & 1) + 32 (j >> 1): its swizzle depends on j & 1 only
-    // (the low 4 bits) and the 32 (j >> 1) rows are an immediate offset.  Column block cb's
-    // chunk is u + 2 cb with u = 8 q + (G & 1) (bits 1 and 2 clear), so its swizzled byte
-    // offset is 16 ((u ^ swz) ^ 2 cb): one base per j & 1, XORed with 32 cb.
-    const int tok0 = 16 * (G >> 1) + (gi >> 1);
+    const int tok0 = (PV8 ? 16 : 8) * (G >> 1) + (gi >> 1);
     const int u = 8 * q + (G & 1);
     int vb[2];
 #pragma unroll
-    for (int jo = 0; jo < 2; ++jo)
-      vb[jo] = (tok0 + 8 * jo) * kDC + 8 * (gi & 1) + 16 * (u ^ swz32(tok0 + 8 * jo));
+    for (int jo = 0; jo < 2; ++jo) {
+      const int tk = tok0 + (PV8 ? 8 * jo : 0);
+      vb[jo] = tk * kDC + 8 * (gi & 1) + 16 * (u ^ swz32(tk));
+    }
     v8i vop[4];
     auto read_v = [&](int n) {
       const uint8_t* vt = &sm.lat8[n % kStages][0][0];
@@ -447,7 +492,8 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x2 v = lds_read_tr8(vt + (vb[j & 1] ^ (32 * cb)) + 32 * (j >> 1) * kDC);
+          const int off = PV8 ? (vb[j & 1] ^ (32 * cb)) + 32 * (j >> 1) * kDC : (vb[0] ^ (32 * cb)) + 16 * j * kDC;
+          const u32x2 v = lds_read_tr8(vt + off);
           vop[cb][2 * j] = int(v[0]);
           vop[cb][2 * j + 1] = int(v[1]);
         }
@@ -455,9 +501,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     float m_acc[2] = {-INFINITY, -INFINITY};  // the accumulator's reference of rows 32 rb2 + n
     auto pv = [&](int n) {
       const int buf = n & 1;
-      float al[2];
-      int sc[2];
-      v8i pb[2];
+      float al[2], f[2][2];
 #pragma unroll
       for (int rb2 = 0; rb2 < 2; ++rb2) {
         const int prow = 32 * rb2 + cn;
@@ -467,16 +511,8 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
                   : m_acc[rb2] == -INFINITY ? 0.f
                                             : __builtin_amdgcn_ldexpf(1.f, int(m_acc[rb2] - mn));
         m_acc[rb2] = mn;
-        // This lane's half: its block scale, lowered by the stream's distance to the
-        // accumulator's reference (exact: integers in base 2).
-        const float mh = ch ? m1 : m0;
-        sc[rb2] = mh == -INFINITY ? 0 : max(sm.psc[buf][prow][ch] + int(mh - mn), 0);
-        // B operand (P^T): row prow, tokens 16 h .. + 15 (chunk h) and 32 + 16 h .. + 15
-        // (chunk 2 + h), in the instruction's K order; the lane's scale is that of half h.
-        const uint8_t* pr = &sm.p8[buf][prow][0];
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(pr + 16 * (ch ^ p_swz(prow)));
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(pr + 16 * ((2 + ch) ^ p_swz(prow)));
-        pb[rb2] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+        f[rb2][0] = (m0 == mn || m0 == -INFINITY) ? 1.f : __builtin_amdgcn_ldexpf(1.f, int(m0 - mn));
+        f[rb2][1] = (m1 == mn || m1 == -INFINITY) ? 1.f : __builtin_amdgcn_ldexpf(1.f, int(m1 - mn));
       }
       if (__any((al[0] != 1.f) | (al[1] != 1.f))) {
 #pragma unroll
@@ -484,12 +520,53 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
 #pragma unroll
           for (int rb2 = 0; rb2 < 2; ++rb2) oacc[cb][rb2] *= al[rb2];
       }
+      if constexpr (PV8) {
+        int sc[2];
+        v8i pb[2];
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
+        for (int rb2 = 0; rb2 < 2; ++rb2) {
+          const int prow = 32 * rb2 + cn;
+          // This lane's half: its block scale, lowered by the stream's distance to the
+          // accumulator's reference (exact: integers in base 2).
+          const float mh = ch ? sm.mref[buf][prow][1] : sm.mref[buf][prow][0];
+          sc[rb2] = mh == -INFINITY ? 0 : max(sm.psc[buf][prow][ch] + int(mh - m_acc[rb2]), 0);
+          // B operand (P^T): row prow, tokens 16 h .. + 15 (chunk h) and 32 + 16 h .. + 15
+          // (chunk 2 + h), in the instruction's K order; the lane's scale is that of half h.
+          const uint8_t* pr = &p8buf(buf)[prow][0];
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(pr + 16 * (ch ^ p_swz(prow)));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(pr + 16 * ((2 + ch) ^ p_swz(prow)));
+          pb[rb2] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
+        }
 #pragma unroll
-        for (int rb2 = 0; rb2 < 2; ++rb2)
-          oacc[cb][rb2] =
-              __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[cb], pb[rb2], oacc[cb][rb2], 0, 0, 0, 127, 0, sc[rb2]);
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int rb2 = 0; rb2 < 2; ++rb2)
+            oacc[cb][rb2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[cb], pb[rb2], oacc[cb][rb2], 0, 0, 0,
+                                                                            127, 0, sc[rb2]);
+      } else {
+        // B operand (P^T) of k-step ks: row prow, tokens 16 ks + 8 h .. + 7 (chunk 2 ks + h);
+        // k-steps 0, 1 belong to half 0, 2, 3 to half 1, scaled by that half's distance to
+        // the accumulator's reference when one moved on its own in this step.
+        const bool scale_p = __any((f[0][0] != 1.f) | (f[0][1] != 1.f) | (f[1][0] != 1.f) | (f[1][1] != 1.f));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          bf16x8 pb[2];
+#pragma unroll
+          for (int rb2 = 0; rb2 < 2; ++rb2) {
+            const int prow = 32 * rb2 + cn;
+            pb[rb2] = *reinterpret_cast<const bf16x8*>(&sm.p[buf][prow][8 * ((2 * ks + ch) ^ p16_swz(prow))]);
+            if (scale_p) pb[rb2] = scale_bf16x8(pb[rb2], f[rb2][ks >> 1]);
+          }
+#pragma unroll
+          for (int cb = 0; cb < 4; ++cb) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(uint32_t(vop[cb][2 * ks]),
+                                                                           uint32_t(vop[cb][2 * ks + 1])));
+#pragma unroll
+            for (int rb2 = 0; rb2 < 2; ++rb2)
+              oacc[cb][rb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[rb2], oacc[cb][rb2], 0, 0, 0);
+          }
+        }
+      }
     };
     if (nsteps > 0) {
       // Loads run two steps ahead: step k goes to buffer k % 3 in step k - 2 (the prologue
@@ -558,24 +635,24 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
 
 // Launch bounds: 512 threads and at least 2 waves per SIMD, i.e. one 8-wave workgroup per
 // compute unit (the kernel's LDS allows one); each wave may then hold up to 256 registers.
-template <int PK>
+template <int PK, bool PV8>
 __global__ __launch_bounds__(kThreads, 2) void decode_fp8_kernel(DecodeArgs a, int num_splits, int chunk,
                                                                  int rblocks, int n_units, int n_xcd) {
   __shared__ Smem8 sm;
   walk_pieces<32, kThreads>(a, num_splits, chunk, rblocks, n_units, n_xcd, sm.prefix, sm.wave_tot,
                             [&](int b, int rb, int t_lo, int t_hi, int L, bool fin, int64_t base)
                                 __attribute__((always_inline)) {
-                                  decode_piece8<PK>(sm, a, b, rb, t_lo, t_hi, L, fin, base);
+                                  decode_piece8<PK, PV8>(sm, a, b, rb, t_lo, t_hi, L, fin, base);
                                 });
 }
 
-template <int PK>
+template <int PK, bool PV8>
 int launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const int rblocks = p.rows / kRows;
   const int n_units = p.balanced ? p.num_splits * rblocks : a.B * p.num_splits * rblocks;
   const int n_xcd = p.n_xcd > 0 ? p.n_xcd : 1;
   const int grid = (n_units + n_xcd - 1) / n_xcd * n_xcd;
-  hipLaunchKernelGGL((decode_fp8_kernel<PK>), dim3(grid), dim3(kThreads), 0, s, a, p.num_splits,
+  hipLaunchKernelGGL((decode_fp8_kernel<PK, PV8>), dim3(grid), dim3(kThreads), 0, s, a, p.num_splits,
                      p.split_tokens, rblocks, n_units, n_xcd);
   return int(hipGetLastError());
 }
@@ -584,8 +661,15 @@ int launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
 
 int launch_decode_fp8(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   if (a.kv_dt != MLA_FP8_E4M3 || p.rows % kRows) return int(hipErrorInvalidValue);
-  if (!a.paged) return launch_t<kContig>(a, p, s);
-  return a.block_size % kHalf == 0 ? launch_t<kPagedTile>(a, p, s) : launch_t<kPagedAny>(a, p, s);
+  const int pk = !a.paged ? kContig : a.block_size % kHalf == 0 ? kPagedTile : kPagedAny;
+  auto by_layout = [&](auto pv8) {
+    constexpr bool V = decltype(pv8)::value;
+    if (pk == kContig) return launch_t<kContig, V>(a, p, s);
+    return pk == kPagedTile ? launch_t<kPagedTile, V>(a, p, s) : launch_t<kPagedAny, V>(a, p, s);
+  };
+  if (a.fp8_scores == 2) return by_layout(std::true_type{});
+  if (a.fp8_scores == 1) return by_layout(std::false_type{});
+  return int(hipErrorInvalidValue);
 }
 
 }  // namespace mla

@@ -14,8 +14,7 @@
 // 32-token tiles, and its eight waves take three roles:
 //   * loader waves 4, 5 (SIMDs 0, 1): wave 4 + l streams tokens 16 l .. 16 l + 15 of every
 //     tile from HBM (whole 1 KB latent rows and 128-byte RoPE rows, 16 bytes per lane, two
-//     tiles ahead in registers; fp8 codes are converted to bf16 here, and also staged as
-//     codes for the fp8 score product) and stages them in LDS;
+//     tiles ahead in registers; fp8 codes are converted to bf16 here) and stages them in LDS;
 //   * score waves 0, 1 (SIMDs 0, 1): wave w owns rows 32 w .. 32 w + 31 over the whole
 //     576-wide key (query operands in registers for the whole split), so a tile's scores
 //     come out of one MFMA accumulator and the online softmax runs on it in registers
@@ -36,9 +35,8 @@
 // reference max that only moves when a tile exceeds it by more than kTau; output waves
 // skip the accumulator rescale whenever no row's reference moved.  fp8 (OCP e4m3fn)
 // caches are converted exactly to bf16; the per-token scale multiplies the latent part of
-// the score and the probability used in the PV product.  With the fp8 score product the
-// query rows are rounded to e4m3 (one scale per 128-column slice, amax / 448) and multiplied
-// with the stored codes by the 32 x 32 x 64 fp8 matrix instruction.
+// the score and the probability used in the PV product.  (The fp8 score and value products
+// run in their own kernel, decode_fp8.hip.)
 #include "device_common.h"
 #include "mfma_common.h"
 #include "mla_internal.h"
@@ -102,12 +100,10 @@ __device__ __forceinline__ int64_t any_row(const Ctx& c, int t) {
 
 // Staged tiles are double buffered: in step n the loaders write buffer (n + 1) % 2 while
 // the score and output waves read buffer n % 2.
-template <bool QK8>
 struct alignas(16) Smem {
   static constexpr int kNB = 2;
   uint16_t lat[kNB][kTile][kDC];        // staged latent rows (bf16), chunk c of row t at c ^ swz32(t)
   uint16_t rope[kNB][kTile][kDR];       // staged RoPE rows, chunk c of row t at c ^ rope_swz(t)
-  uint8_t lat8[QK8 ? kNB : 1][kTile][QK8 ? kDC : 16];  // fp8 score product: the codes, same swizzle
   uint16_t p[2][kRows][kPPitch];        // probabilities (double buffered), [row][tok], p_swz
   float ts[kNB][kTile];                 // fp8 per-token scales
   float alpha[2][kRows];
@@ -145,8 +141,8 @@ struct LoadRegs {
 // any other piece writes its normalised partial output and base-2 log-sum-exp.  Row r of
 // the row block goes to row out_base + 64 rb + r of the target arrays.  Every wave of
 // the workgroup calls it with the same arguments (it contains barriers).
-template <bool FP8, int PK, bool QK8>
-__device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a, int b, int rb, int t_lo,
+template <bool FP8, int PK>
+__device__ __forceinline__ void decode_piece(Smem& sm, const DecodeArgs& a, int b, int rb, int t_lo,
                                               int t_hi, int L, bool final_out, int64_t out_base) {
   int tid;
   asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(int(threadIdx.x)));
@@ -165,7 +161,7 @@ __device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a,
   const int r0 = rb * kRows;
   const int ntiles = t_hi > t_lo ? (t_hi - t_lo + kTile - 1) / kTile : 0;
   const bool single = final_out;
-  constexpr int kNB = Smem<QK8>::kNB;
+  constexpr int kNB = Smem::kNB;
 
   if (c.w == 4 || c.w == 5) {
     // ================================ loader waves ===================================
@@ -235,8 +231,6 @@ __device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a,
         if constexpr (FP8) {
           const int row = 16 * l + 2 * k + c.h;
           const u32x4 w = r.lat[k];
-          if constexpr (QK8)
-            *reinterpret_cast<u32x4*>(&sm.lat8[buf][row][16 * ((c.lane & 31) ^ swz32(row))]) = w;
           const int ch = 2 * (c.lane & 31);
           *reinterpret_cast<u32x4*>(&sm.lat[buf][row][8 * (ch ^ swz32(row))]) = e4m3x8_to_bf16x8(w[0], w[1]);
           *reinterpret_cast<u32x4*>(&sm.lat[buf][row][8 * ((ch + 1) ^ swz32(row))]) = e4m3x8_to_bf16x8(w[2], w[3]);
@@ -278,51 +272,16 @@ __device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a,
     // ================================ score waves ====================================
     const int row = 32 * c.w + c.n;  // this lane's row of the workgroup
     // Query operands (B): qb[s] = columns 16 s + 8 h .. + 7 of the row for latent k-step s < 32,
-    // RoPE dims 16 (s - 32) + 8 h .. + 7 for s = 32 .. 35.  With the fp8 score product the
-    // latent part is q8[m] instead: the e4m3 codes of columns 64 m + 32 h .. + 31, rounded
-    // with the scale qs[m / 2] of their 128-column slice (amax / 448, the partner lane holds
-    // the slice's other half).
+    // RoPE dims 16 (s - 32) + 8 h .. + 7 for s = 32 .. 35.
     bf16x8 qb[36];
-    v8i q8[8];
-    float qs[4];
     {
       const int64_t qrow = int64_t(b) * rows + r0 + row;
       const uint16_t* ql = static_cast<const uint16_t*>(a.q_lat) + qrow * kDC;
       const uint16_t* qr = static_cast<const uint16_t*>(a.q_rope) + qrow * kDR + 8 * c.h;
-      if constexpr (!QK8) {
 #pragma unroll
-        for (int s = 0; s < 32; ++s) qb[s] = __builtin_bit_cast(bf16x8, ld16(ql + 16 * s + 8 * c.h));
-      }
+      for (int s = 0; s < 32; ++s) qb[s] = __builtin_bit_cast(bf16x8, ld16(ql + 16 * s + 8 * c.h));
 #pragma unroll
       for (int s = 0; s < 4; ++s) qb[32 + s] = __builtin_bit_cast(bf16x8, ld16(qr + 16 * s));
-      if constexpr (QK8) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          bf16x8 x[8];  // x[4 mm + i]: columns 128 j + 64 mm + 32 h + 8 i .. + 7
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            x[i] = __builtin_bit_cast(bf16x8, ld16(ql + 128 * j + 64 * (i >> 2) + 32 * c.h + 8 * (i & 3)));
-          float amax = 0.f;
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(float(x[i][e])));
-          amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-          qs[j] = amax > 0.f ? amax * (1.f / 448.f) : 1.f;
-          const float inv = amax > 0.f ? 448.f / amax : 1.f;
-#pragma unroll
-          for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-            for (int d = 0; d < 8; ++d) {  // dword d: columns 64 m + 32 h + 4 d .. + 3
-              const bf16x8 src = x[4 * mm + d / 2];
-              const int o = 4 * (d % 2);
-              auto qf = [&](int e) { return fminf(fmaxf(float(src[o + e]) * inv, -448.f), 448.f); };
-              int wd = __builtin_amdgcn_cvt_pk_fp8_f32(qf(0), qf(1), 0, false);
-              wd = __builtin_amdgcn_cvt_pk_fp8_f32(qf(2), qf(3), wd, true);
-              q8[2 * j + mm][d] = wd;
-            }
-        }
-      }
     }
     const int iq = (r0 + row) / a.H;
     const int lim = min(min(max(L - a.sq + iq + 1, 0), L), t_hi);
@@ -341,12 +300,6 @@ __device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a,
 #pragma unroll
     for (int t = 0; t < 4; ++t) roff[t] = c.n * kDR + 8 * ((2 * t + c.h) ^ rope_swz(c.n));
 
-    // fp8 score product: product m reads the codes of columns 64 m + 32 h .. + 31 of token n,
-    // chunks 4 m + 2 h and 4 m + 2 h + 1 of its 512-byte row (same swizzle).
-    int boff[8];  // [2 (m % 4) + e]: chunk 4 (m % 4) + 2 h + e, plus 256 bytes per 4 products
-#pragma unroll
-    for (int t = 0; t < 8; ++t) boff[t] = c.n * kDC + 16 * ((4 * (t >> 1) + 2 * c.h + (t & 1)) ^ swz32(c.n));
-
     auto tile = [&](int n) {
       const int buf = n % kNB;
       const uint16_t* lt = &sm.lat[buf][0][0];
@@ -355,43 +308,13 @@ __device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a,
         return s < 32 ? *reinterpret_cast<const bf16x8*>(lt + 128 * (s >> 3) + loff[s & 7])
                       : *reinterpret_cast<const bf16x8*>(rt + roff[s - 32]);
       };
-      f32x16 acc, accr, accq[4];
+      f32x16 acc, accr;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         acc[e] = 0.f;
         accr[e] = 0.f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) accq[j][e] = 0.f;
       }
-      if constexpr (QK8) {
-        // Eight fp8 products (one accumulator per 128-column slice), codes read two products
-        // ahead, then the four bf16 RoPE products.
-        const uint8_t* l8 = &sm.lat8[buf][0][0];
-        auto codes = [&](int m) {
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(l8 + 256 * (m >> 2) + boff[2 * (m & 3)]);
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(l8 + 256 * (m >> 2) + boff[2 * (m & 3) + 1]);
-          return v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
-        };
-        v8i ring8[2] = {codes(0), codes(1)};
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          const v8i av = ring8[m & 1];
-          if (m + 2 < 8) ring8[m & 1] = codes(m + 2);
-          accq[m >> 1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, q8[m], accq[m >> 1], 0, 0, 0, 127, 0, 127);
-        }
-        bf16x8 ar[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) ar[s] = operand(32 + s);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) accr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ar[s], qb[32 + s], accr, 0, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-        }
-      } else {
+      {
         // Products s in order (one accumulator; RoPE products apart for fp8), each operand
         // read kPre products ahead.
         constexpr int kSteps = 36, kPre = 4;
@@ -423,11 +346,6 @@ __device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a,
       if constexpr (FP8) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) tsv[i] = *reinterpret_cast<const f32x4*>(&sm.ts[buf][8 * i + 4 * c.h]);
-        if constexpr (QK8) {
-#pragma unroll
-          for (int e = 0; e < 16; ++e)
-            acc[e] = qs[0] * accq[0][e] + qs[1] * accq[1][e] + qs[2] * accq[2][e] + qs[3] * accq[3][e];
-        }
 #pragma unroll
         for (int e = 0; e < 16; ++e) sv[e] = fmaf(acc[e], tsv[e >> 2][e & 3], accr[e]);
       } else {
@@ -582,24 +500,24 @@ __device__ __forceinline__ void decode_piece(Smem<QK8>& sm, const DecodeArgs& a,
 
 // Launch bounds: 512 threads and at least 2 waves per SIMD (HIP's second argument counts
 // waves per SIMD), i.e. one 8-wave workgroup per compute unit, which is what the kernel's
-// 124 KB of LDS allows; each wave may then hold up to 256 registers.
-template <bool FP8, int PK, bool QK8>
+// 91 KB of LDS allows; each wave may then hold up to 256 registers.
+template <bool FP8, int PK>
 __global__ __launch_bounds__(kThreads, 2) void decode_mfma_kernel(DecodeArgs a, int num_splits,
                                                                   int chunk, int rblocks, int n_units, int n_xcd) {
-  __shared__ Smem<QK8> sm;
+  __shared__ Smem sm;
   walk_pieces<kTile, kThreads>(a, num_splits, chunk, rblocks, n_units, n_xcd, sm.prefix, sm.wave_tot,
                                [&](int b, int rb, int t_lo, int t_hi, int L, bool fin, int64_t base) __attribute__((always_inline)) {
-                                 decode_piece<FP8, PK, QK8>(sm, a, b, rb, t_lo, t_hi, L, fin, base);
+                                 decode_piece<FP8, PK>(sm, a, b, rb, t_lo, t_hi, L, fin, base);
                                });
 }
 
-template <bool FP8, int PK, bool QK8 = false>
+template <bool FP8, int PK>
 int launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const int rblocks = p.rows / kRows;
   const int n_units = p.balanced ? p.num_splits * rblocks : a.B * p.num_splits * rblocks;
   const int n_xcd = p.n_xcd > 0 ? p.n_xcd : 1;
   const int grid = (n_units + n_xcd - 1) / n_xcd * n_xcd;
-  hipLaunchKernelGGL((decode_mfma_kernel<FP8, PK, QK8>), dim3(grid), dim3(kThreads), 0, s, a,
+  hipLaunchKernelGGL((decode_mfma_kernel<FP8, PK>), dim3(grid), dim3(kThreads), 0, s, a,
                      p.num_splits, p.split_tokens, rblocks, n_units, n_xcd);
   return int(hipGetLastError());
 }
@@ -607,10 +525,7 @@ int launch_t(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
 }  // namespace
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const int pk = !a.paged ? kContig : (a.block_size % kTile == 0 ? kPagedTile : kPagedAny);
-  if (a.kv_dt == MLA_FP8_E4M3 && a.fp8_scores == 1) {
-    if (pk == kContig) return launch_t<true, kContig, true>(a, p, s);
-    return pk == kPagedTile ? launch_t<true, kPagedTile, true>(a, p, s) : launch_t<true, kPagedAny, true>(a, p, s);
-  }
+  if (a.fp8_scores) return int(hipErrorInvalidValue);  // the fp8 products run in decode_fp8.hip
   if (a.kv_dt == MLA_FP8_E4M3) {
     if (pk == kContig) return launch_t<true, kContig>(a, p, s);
     return pk == kPagedTile ? launch_t<true, kPagedTile>(a, p, s) : launch_t<true, kPagedAny>(a, p, s);

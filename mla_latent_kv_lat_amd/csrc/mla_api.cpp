@@ -126,8 +126,8 @@ mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s, b
     if (err) return hip_status(err);
   }
   int err = p.kernel == DecodeKernel::kLatent ? launch_decode_latent(a, p, s)
-            : p.kernel == DecodeKernel::kMfma ? (a.fp8_scores == 2 ? launch_decode_fp8(a, p, s)
-                                                                   : launch_decode_mfma(a, p, s))
+            : p.kernel == DecodeKernel::kMfma ? (a.fp8_scores ? launch_decode_fp8(a, p, s)
+                                                              : launch_decode_mfma(a, p, s))
                                               : launch_decode_general(a, p, s);
   if (err) return hip_status(err);
   if (combine && (p.balanced || p.num_splits > 1)) return hip_status(launch_combine(a, p, s));
