@@ -65,6 +65,13 @@ enum : int { kContig = 0, kPagedTile = 1, kPagedAny = 2 };
 
 __device__ __forceinline__ int rope_swz(int row) { return (row >> 1) & 7; }
 
+// Staged code rows are 512 bytes (32 chunks of 16 bytes, every row starting on bank 0); chunk c
+// of row t sits at c ^ lat_swz(t), which permutes the low 4 chunk bits.  It is bijective on each
+// aligned group of 16 rows (a score read takes one chunk of 16 rows per pass) and, on each
+// aligned group of 8 rows, keeps bit 0 and permutes bits 1 .. 3 (a transposed read takes 8 rows
+// at chunks c and c ^ 1 per pass: 16 distinct bank groups).
+__device__ __forceinline__ int lat_swz(int t) { return ((t & 7) << 1) | ((t >> 3) & 1); }
+
 // Probability rows hold 64 codes (4 chunks of 16 bytes); chunk c of row r sits at
 // c ^ p_swz(r): the output waves' 16-byte operand reads (16 rows per pass) hit distinct banks.
 __device__ __forceinline__ int p_swz(int row) { return (row >> 2) & 3; }
@@ -132,7 +139,7 @@ __device__ __forceinline__ void wait_vm() {
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 struct alignas(16) Smem8 {
-  uint8_t lat8[kStages][kStep][kDC];   // staged codes, chunk c of row t at c ^ swz32(t); also
+  uint8_t lat8[kStages][kStep][kDC];   // staged codes, chunk c of row t at c ^ lat_swz(t); also
                                        // the output rows at the end (64 x 1 KB of bf16)
   uint16_t rope[kStages][kStep][kDR];  // staged RoPE rows, chunk c of row t at c ^ rope_swz(t)
   float ts[kStages][kStep];            // per-token scales
@@ -231,7 +238,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     // 4 m + 2 h + 1 of token n; RoPE k-step s reads chunk (2 s + h) ^ rope_swz(n).
     int boff[8];  // [2 (m % 4) + e]: chunk 4 (m % 4) + 2 h + e, plus 256 bytes per 4 products
 #pragma unroll
-    for (int t = 0; t < 8; ++t) boff[t] = cn * kDC + 16 * ((4 * (t >> 1) + 2 * ch + (t & 1)) ^ swz32(cn));
+    for (int t = 0; t < 8; ++t) boff[t] = cn * kDC + 16 * ((4 * (t >> 1) + 2 * ch + (t & 1)) ^ lat_swz(cn));
     int roff[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) roff[t] = cn * kDR + 8 * ((2 * t + ch) ^ rope_swz(cn));
@@ -392,7 +399,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     // ---------------------------------------------------------------- staging
     // Wave q stages rows 16 q .. 16 q + 15 of every step (tokens past the piece's last one
     // are clamped to it; the softmax masks them): latent rows two per load (lane i: row
-    // 16 q + 2 k + i / 32, 16-byte chunk i % 32 fetched from chunk (i % 32) ^ swz32(row)), RoPE
+    // 16 q + 2 k + i / 32, 16-byte chunk i % 32 fetched from chunk (i % 32) ^ lat_swz(row)), RoPE
     // rows eight per load (lane i: row 16 q + 8 k + i / 8, chunk (i % 8) ^ rope_swz(row)) and
     // the 16 scales (lanes 0 .. 15).
     const char* lat_g = static_cast<const char*>(a.c_kv);
@@ -412,7 +419,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int j = 2 * k + ch;
-          dma16(lat_g + crow(j) * kDC + 16 * (cn ^ swz32(16 * q + j)), lds_addr(&sm.lat8[buf][16 * q + 2 * k][0]));
+          dma16(lat_g + crow(j) * kDC + 16 * (cn ^ lat_swz(16 * q + j)), lds_addr(&sm.lat8[buf][16 * q + 2 * k][0]));
         }
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
@@ -444,7 +451,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int j = 2 * k + ch;
-        dma16_s(lat_b, roff(j) * kDC + uint32_t(16 * (cn ^ swz32(16 * q + j))),
+        dma16_s(lat_b, roff(j) * kDC + uint32_t(16 * (cn ^ lat_swz(16 * q + j))),
                 lds_addr(&sm.lat8[buf][16 * q + 2 * k][0]));
       }
 #pragma unroll
@@ -483,7 +490,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
 #pragma unroll
     for (int jo = 0; jo < 2; ++jo) {
       const int tk = tok0 + (PV8 ? 8 * jo : 0);
-      vb[jo] = tk * kDC + 8 * (gi & 1) + 16 * (u ^ swz32(tk));
+      vb[jo] = tk * kDC + 8 * (gi & 1) + 16 * (u ^ lat_swz(tk));
     }
     v8i vop[4];
     auto read_v = [&](int n) {
