@@ -84,8 +84,8 @@ typedef struct {
                             cache codes as stored; the RoPE term, the softmax and the product
                             with V are unchanged.  Twice the matrix rate for the score, at
                             the cost of the query rounding.  Needs an MLA_FP8_E4M3 cache on
-                            the matrix-core kernel (else MLA_ERR_UNSUPPORTED); mla_decode /
-                            mla_decode_paged only.
+                            the matrix-core kernel (else MLA_ERR_UNSUPPORTED); taken by every
+                            decode call (prefill requires 0).
                             Accuracy: the result is attention with that rounded query (to the
                             fp8 kernel bar of 2e-2), which is an approximation of the exact
                             result, outside its 6e-2 parity bar in general: each logit moves by

@@ -221,3 +221,28 @@ def test_full_size_sampled_fp8_values():
     check(o[batches], l[batches], o_ref, l_ref, flip_allowance(sub, q_bits[batches], d), "full size")
     measure_vs_exact(o[batches], l[batches], sub, q_bits[batches], d)
     del w
+
+
+@pytest.mark.parametrize("fp8_scores", [1, 2])
+def test_fused_absorb_out_equals_separate_calls(fp8_scores):
+    """mla_decode_absorb_out with an fp8 product mode: o_lat, lse and out bit for bit those of
+    mla_decode followed by mla_absorb_out (the same decode kernel; the range merge inside the
+    absorption does the separate merge's arithmetic)."""
+    cfg = configs.SPEC_FP8.with_(batch=6, seq_len=900, cfg_id=44)
+    lengths = [900, 0, 3, 517, 64, 899]
+    say("fused decode + absorb_out, fp8_scores", fp8_scores, lengths, cfg)
+    inp = synth.make_inputs(cfg, 2, lengths=np.array(lengths, np.int32), poison_tail=True)
+    w = DeviceWorkload(inp, fp8_scores=fp8_scores)
+    w.absorb_q()
+    w.decode()
+    w.absorb_out()
+    torch.cuda.synchronize()
+    sep = {k: to_host_f64(t).copy() for k, t in (("o_lat", w.o_lat), ("lse", w.lse), ("out", w.out))}
+    for t in (w.o_lat, w.lse, w.out):
+        t.fill_(float("nan"))
+    w.decode_absorb_out()
+    torch.cuda.synchronize()
+    for k, t in (("o_lat", w.o_lat), ("lse", w.lse), ("out", w.out)):
+        assert np.array_equal(sep[k], to_host_f64(t), equal_nan=True), k
+    assert np.all(np.isfinite(sep["out"]))
+    del w
