@@ -33,9 +33,9 @@
 //     the two, and each half's block scale is lowered by its distance to it (powers of two).
 //     They also stage the cache: each wave copies 16 rows of every step straight from memory
 //     into LDS (direct-to-LDS loads, two steps ahead, three buffers).
-// One barrier per step: in step n the output waves issue the loads of step n + 2, multiply
-// step n - 1 and read the V^T operands of step n, and wait for step n + 1's loads; the score
-// waves score step n.
+// One barrier per step: in step n the output waves issue the loads of step n + 2 (between the
+// products, with fp8 value products), multiply step n - 1 and read the V^T operands of step n,
+// and wait for step n + 1's loads; the score waves score step n.
 #include <type_traits>
 
 #include "device_common.h"
@@ -142,7 +142,9 @@ struct alignas(16) Smem8 {
   uint8_t lat8[kStages][kStep][kDC];   // staged codes, chunk c of row t at c ^ lat_swz(t); also
                                        // the output rows at the end (64 x 1 KB of bf16)
   uint16_t rope[kStages][kStep][kDR];  // staged RoPE rows, chunk c of row t at c ^ rope_swz(t)
-  float ts[kStages][kStep];            // per-token scales
+  // per-token scales: row 16 q + j of a step at [q][j]; each output wave loads 64 lanes (lanes
+  // 16 .. 63 repeat lane & 15's row into [q][16 ..]), so that no branch splits its loads
+  float ts[kStages][kStep / 16][64];
   // Probabilities of the step, double buffered: bf16 [row][tok] (8-token chunk c of row r at
   // c ^ p16_swz(r)) for a bf16 value product, or e4m3 codes [row][tok] (16-byte chunk c of row
   // r at c ^ p_swz(r)) in the first 4 KB of each buffer for the fp8 one.
@@ -297,7 +299,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       // Lane (n, h) holds tokens 8 i + 4 h + r (e = 4 i + r) of row `row` in this half.
       f32x4 tsv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tsv[i] = *reinterpret_cast<const f32x4*>(&sm.ts[buf][kHalf * hf + 8 * i + 4 * ch]);
+      for (int i = 0; i < 4; ++i) tsv[i] = *reinterpret_cast<const f32x4*>(&sm.ts[buf][2 * hf + (i >> 1)][8 * (i & 1) + 4 * ch]);
       float sv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -406,62 +408,79 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
     const char* rope_g = static_cast<const char*>(a.k_rope);
     const char* ts_g = reinterpret_cast<const char*>(a.kv_scale);
     const int32_t* tab = a.block_table + int64_t(b) * a.max_blocks;
-    auto stage = [&](int n) {
-      const int tq = t_lo + n * kStep + 16 * q;  // token of this wave's first row
+    // A step's 11 loads per output wave: stage_prep once, then stage_part(k), k = 0 .. 10 (8
+    // latent loads, 2 RoPE loads, the scales); stage issues all 11 at once.  With fp8 value
+    // products they are spread between the products instead: a burst of 44 per compute unit
+    // queues every output wave on the address unit (about one 64-byte line per clock).
+    struct StageCtx {
+      const char* lat_b;
+      const char* rope_b;
+      const char* ts_b;
+      int tq, t_base, buf;
+    };
+    auto stage_prep = [&](int n) {
+      StageCtx sc;
+      sc.tq = t_lo + n * kStep + 16 * q;  // token of this wave's first row
+      sc.buf = n % kStages;
+      sc.lat_b = lat_g;
+      sc.rope_b = rope_g;
+      sc.ts_b = ts_g;
+      sc.t_base = 0;
+      if constexpr (PK != kPagedAny) {
+        // One base per wave and step (the sequence, or the block holding the wave's 16 rows
+        // and the clamp target: block_size a multiple of 32, halves 32-aligned), 32-bit
+        // offsets from it (a sequence's rows span less than 2 GiB).
+        int64_t base_row;
+        if constexpr (PK == kContig) {
+          base_row = int64_t(b) * a.T;
+        } else {
+          const int blk = min(sc.tq, t_hi - 1) / a.block_size;
+          base_row = int64_t(sload_i32(tab + blk)) * a.block_size;
+          sc.t_base = blk * a.block_size;
+        }
+        sc.lat_b = lat_g + base_row * kDC;
+        sc.rope_b = rope_g + base_row * (kDR * 2);
+        sc.ts_b = ts_g + base_row * 4;
+      }
+      return sc;
+    };
+    auto stage_part = [&](const StageCtx& sc, int k) {
       const int tl = t_hi - 1;
-      const int buf = n % kStages;
-      if constexpr (PK == kPagedAny) {
-        // Rows looked up lane by lane.
-        auto crow = [&](int j) -> int64_t {
-          const int t = min(tq + j, tl);
-          return int64_t(tab[t / a.block_size]) * a.block_size + t % a.block_size;
-        };
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const int j = 2 * k + ch;
-          dma16(lat_g + crow(j) * kDC + 16 * (cn ^ lat_swz(16 * q + j)), lds_addr(&sm.lat8[buf][16 * q + 2 * k][0]));
-        }
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int j = 8 * k + (lane >> 3);
-          dma16(rope_g + crow(j) * (kDR * 2) + 16 * ((lane & 7) ^ rope_swz(16 * q + j)),
-                lds_addr(&sm.rope[buf][16 * q + 8 * k][0]));
-        }
-        const int64_t cts = crow(lane & 15);
-        if (lane < 16) dma4(ts_g + cts * 4, lds_addr(&sm.ts[buf][16 * q]));
-        return;
-      }
-      // One base per wave and step (the sequence, or the block holding the wave's 16 rows
-      // and the clamp target: block_size a multiple of 32, halves 32-aligned), 32-bit offsets
-      // from it (a sequence's rows span less than 2 GiB).
-      int64_t base_row;
-      int t_base;
-      if constexpr (PK == kContig) {
-        base_row = int64_t(b) * a.T;
-        t_base = 0;
-      } else {
-        const int blk = min(tq, tl) / a.block_size;
-        base_row = int64_t(sload_i32(tab + blk)) * a.block_size;
-        t_base = blk * a.block_size;
-      }
-      auto roff = [&](int j) { return uint32_t(min(tq + j, tl) - t_base); };
-      const char* lat_b = lat_g + base_row * kDC;
-      const char* rope_b = rope_g + base_row * (kDR * 2);
-      const char* ts_b = ts_g + base_row * 4;
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      // row 16 q + j of the step: its cache row (general paged layout, looked up lane by
+      // lane) or its offset from the step's base
+      auto crow = [&](int j) -> int64_t {
+        const int t = min(sc.tq + j, tl);
+        return int64_t(tab[t / a.block_size]) * a.block_size + t % a.block_size;
+      };
+      auto roff = [&](int j) { return uint32_t(min(sc.tq + j, tl) - sc.t_base); };
+      if (k < 8) {
         const int j = 2 * k + ch;
-        dma16_s(lat_b, roff(j) * kDC + uint32_t(16 * (cn ^ lat_swz(16 * q + j))),
-                lds_addr(&sm.lat8[buf][16 * q + 2 * k][0]));
+        const uint32_t dst = lds_addr(&sm.lat8[sc.buf][16 * q + 2 * k][0]);
+        const int chunk = cn ^ lat_swz(16 * q + j);
+        if constexpr (PK == kPagedAny)
+          dma16(lat_g + crow(j) * kDC + 16 * chunk, dst);
+        else
+          dma16_s(sc.lat_b, roff(j) * kDC + uint32_t(16 * chunk), dst);
+      } else if (k < 10) {
+        const int j = 8 * (k - 8) + (lane >> 3);
+        const uint32_t dst = lds_addr(&sm.rope[sc.buf][16 * q + 8 * (k - 8)][0]);
+        const int chunk = (lane & 7) ^ rope_swz(16 * q + j);
+        if constexpr (PK == kPagedAny)
+          dma16(rope_g + crow(j) * (kDR * 2) + 16 * chunk, dst);
+        else
+          dma16_s(sc.rope_b, roff(j) * (kDR * 2) + uint32_t(16 * chunk), dst);
+      } else {
+        const uint32_t dst = lds_addr(&sm.ts[sc.buf][q][0]);
+        if constexpr (PK == kPagedAny)
+          dma4(ts_g + crow(lane & 15) * 4, dst);
+        else
+          dma4_s(sc.ts_b, roff(lane & 15) * 4, dst);
       }
+    };
+    auto stage = [&](int n) {
+      const StageCtx sc = stage_prep(n);
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int j = 8 * k + (lane >> 3);
-        dma16_s(rope_b, roff(j) * (kDR * 2) + uint32_t(16 * ((lane & 7) ^ rope_swz(16 * q + j))),
-                lds_addr(&sm.rope[buf][16 * q + 8 * k][0]));
-      }
-      const uint32_t ots = roff(lane & 15) * 4;
-      if (lane < 16) dma4_s(ts_b, ots, lds_addr(&sm.ts[buf][16 * q]));
+      for (int k = 0; k < kLoadsPerStep; ++k) stage_part(sc, k);
     };
 
     // ---------------------------------------------------------------- value product
@@ -506,7 +525,10 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
         }
     };
     float m_acc[2] = {-INFINITY, -INFINITY};  // the accumulator's reference of rows 32 rb2 + n
-    auto pv = [&](int n) {
+    // issue_c: std::true_type to spread the loads of sc_next's step over the fp8 value products
+    // (a compile-time choice, so that no branch splits the products from the loads)
+    auto pv = [&](int n, auto issue_c, const StageCtx& sc_next) {
+      constexpr bool issue = decltype(issue_c)::value;
       const int buf = n & 1;
       float al[2], f[2][2];
 #pragma unroll
@@ -544,12 +566,21 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
           const u32x4 hi = *reinterpret_cast<const u32x4*>(pr + 16 * ((2 + ch) ^ p_swz(prow)));
           pb[rb2] = v8i{int(lo[0]), int(lo[1]), int(lo[2]), int(lo[3]), int(hi[0]), int(hi[1]), int(hi[2]), int(hi[3])};
         }
+        // One load of the step two ahead after each product (the last three after the last).
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-          for (int rb2 = 0; rb2 < 2; ++rb2)
+          for (int rb2 = 0; rb2 < 2; ++rb2) {
+            const int i = 2 * cb + rb2;
             oacc[cb][rb2] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vop[cb], pb[rb2], oacc[cb][rb2], 0, 0, 0,
                                                                             127, 0, sc[rb2]);
+            if constexpr (issue) {
+              stage_part(sc_next, i);
+              if (i == 7)
+                for (int k = 8; k < kLoadsPerStep; ++k) stage_part(sc_next, k);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
       } else {
         // B operand (P^T) of k-step ks: row prow, tokens 16 ks + 8 h .. + 7 (chunk 2 ks + h);
         // k-steps 0, 1 belong to half 0, 2, 3 to half 1, scaled by that half's distance to
@@ -586,16 +617,41 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
         wait_vm<0>();
       }
       barrier_lds();  // step 0 staged
-      for (int n = 0; n < nsteps; ++n) {
-        const bool more = n + 2 < nsteps;
-        if (more) stage(n + 2);
-        if (n > 0) pv(n - 1);
+      // Step n: the products of step n - 1 (with the loads of step n + 2 while there is one),
+      // then step n's values read, then wait for step n + 1's loads.
+      auto step_end = [&](int n) {
+        __builtin_amdgcn_sched_barrier(0);
         read_v(n);
-        if (more) wait_vm<kLoadsPerStep>();
+        if (n + 2 < nsteps) wait_vm<kLoadsPerStep>();
         else wait_vm<0>();
         barrier_lds();  // step n scored, step n + 1 staged
+      };
+      const StageCtx none{};
+      // The loads are spread over the fp8 value products (8 short products, each followed by
+      // one or more loads).  The bf16 value product keeps the burst: spread over its 32
+      // products it measured slower (946 against 885 us on the speculative fp8 workload).
+      // The general paged layout looks its rows up lane by lane (vector loads the compiler
+      // waits for), so it keeps the burst too.
+      constexpr bool kSpread = PV8 && PK != kPagedAny;
+      if (nsteps > 2) stage(2);
+      step_end(0);
+      int n = 1;
+      if constexpr (kSpread) {
+        for (; n + 2 < nsteps; ++n) {
+          pv(n - 1, std::true_type{}, stage_prep(n + 2));
+          __builtin_amdgcn_sched_barrier(0);
+          read_v(n);
+          wait_vm<kLoadsPerStep>();
+          barrier_lds();
+        }
       }
-      pv(nsteps - 1);
+      // Otherwise a step's loads go out in one burst, and so do the last two steps'.
+      for (; n < nsteps; ++n) {
+        if (n + 2 < nsteps) stage(n + 2);
+        pv(n - 1, std::false_type{}, none);
+        step_end(n);
+      }
+      pv(nsteps - 1, std::false_type{}, none);
     }
     __syncthreads();  // row sums published
     float lt[2];

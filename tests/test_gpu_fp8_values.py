@@ -141,11 +141,13 @@ def check(o, l, o_ref, l_ref, allow, what):
 
 # Ragged lengths with an empty sequence, one shorter than s_q = 4 (some queries see nothing)
 # and lengths that end inside a 32-token half; balanced ranges, static splits of 64 and 192
-# tokens (many partial pieces), and 4x larger logits (peaked attention).
-CASES = [(0, 1.0), (64, 1.0), (192, 1.0), (0, 4.0)]
+# tokens (many partial pieces), a split of 1024 (one piece per sequence: the 700-token one
+# runs 11 steps, so the loads of a step are issued during the products of the step three
+# before it, the steady state of long sequences), and 4x larger logits (peaked attention).
+CASES = [(0, 1.0), (64, 1.0), (192, 1.0), (1024, 1.0), (0, 4.0)]
 
 
-@pytest.mark.parametrize("split_tokens,q_gain", CASES, ids=["balanced", "split64", "split192", "peaked"])
+@pytest.mark.parametrize("split_tokens,q_gain", CASES, ids=["balanced", "split64", "split192", "whole", "peaked"])
 def test_decode_fp8_values(split_tokens, q_gain):
     cfg = configs.SPEC_FP8.with_(batch=5, seq_len=700, cfg_id=41)
     lengths = [700, 0, 2, 333, 97]

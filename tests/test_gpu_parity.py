@@ -485,8 +485,10 @@ def test_decode_balanced_ranges(case, kern, monkeypatch):
 # measurement: the e4m3 query rounding moves each logit by about 2^-4 of its size, so on a
 # sequence of a few tokens the log-sum-exp moves by several 1e-2, and at 4x larger logits
 # (peaked attention) the output by several percent.
-@pytest.mark.parametrize("split_tokens,q_gain", [(0, 1.0), (128, 1.0), (0, 4.0)],
-                         ids=["balanced", "split128", "peaked"])
+# A split of 1024 keeps each sequence in one piece (11 steps for 700 tokens: the steady state
+# of long sequences, where a step's loads are issued among earlier products).
+@pytest.mark.parametrize("split_tokens,q_gain", [(0, 1.0), (128, 1.0), (1024, 1.0), (0, 4.0)],
+                         ids=["balanced", "split128", "whole", "peaked"])
 def test_decode_fp8_scores(split_tokens, q_gain):
     cfg = configs.SPEC_FP8.with_(batch=3, seq_len=700, cfg_id=31)
     say("decode fp8 scores", split_tokens, q_gain, cfg)
