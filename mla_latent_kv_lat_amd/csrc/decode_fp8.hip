@@ -104,18 +104,26 @@ __device__ __forceinline__ void dma16_s(const void* base, uint32_t voff, uint32_
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(ps), "s"(m0)
                : "memory");
 }
-__device__ __forceinline__ void dma4_s(const void* base, uint32_t voff, uint32_t lds) {
+// Loads of 4 bytes per lane issued by lanes 0 .. 15 only (called with every lane active): the
+// exec mask is narrowed and restored inside the statement, so that no branch splits the
+// caller's code and no lane repeats another's address.
+__device__ __forceinline__ void dma4_s_16(const void* base, uint32_t voff, uint32_t lds) {
   const uint64_t p = reinterpret_cast<uint64_t>(base);
   const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
   const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
   const uint64_t ps = (uint64_t(hi) << 32) | uint64_t(lo);
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 3\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(ps), "s"(m0)
-               : "memory");
+  uint64_t saved;
+  asm volatile("s_mov_b32 m0, %3\n\ts_mov_b64 %0, exec\n\ts_mov_b64 exec, 0xffff\n\ts_nop 3\n\t"
+               "global_load_lds_dword %1, %2\n\ts_mov_b64 exec, %0"
+               : "=&s"(saved) : "v"(voff), "s"(ps), "s"(m0) : "memory");
 }
-__device__ __forceinline__ void dma4(const void* addr, uint32_t lds) {
+__device__ __forceinline__ void dma4_16(const void* addr, uint32_t lds) {
   const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds);
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 3\n\tglobal_load_lds_dword %0, off" ::"v"(addr), "s"(m0) : "memory");
+  uint64_t saved;
+  asm volatile("s_mov_b32 m0, %2\n\ts_mov_b64 %0, exec\n\ts_mov_b64 exec, 0xffff\n\ts_nop 3\n\t"
+               "global_load_lds_dword %1, off\n\ts_mov_b64 exec, %0"
+               : "=&s"(saved) : "v"(addr), "s"(m0) : "memory");
 }
 // Scalar load of one int (a wave-uniform address) and its wait, in one block: a vector load
 // would make the compiler wait for every outstanding vector-memory operation, the staged loads
@@ -142,9 +150,7 @@ struct alignas(16) Smem8 {
   uint8_t lat8[kStages][kStep][kDC];   // staged codes, chunk c of row t at c ^ lat_swz(t); also
                                        // the output rows at the end (64 x 1 KB of bf16)
   uint16_t rope[kStages][kStep][kDR];  // staged RoPE rows, chunk c of row t at c ^ rope_swz(t)
-  // per-token scales: row 16 q + j of a step at [q][j]; each output wave loads 64 lanes (lanes
-  // 16 .. 63 repeat lane & 15's row into [q][16 ..]), so that no branch splits its loads
-  float ts[kStages][kStep / 16][64];
+  float ts[kStages][kStep];            // per-token scales
   // Probabilities of the step, double buffered: bf16 [row][tok] (8-token chunk c of row r at
   // c ^ p16_swz(r)) for a bf16 value product, or e4m3 codes [row][tok] (16-byte chunk c of row
   // r at c ^ p_swz(r)) in the first 4 KB of each buffer for the fp8 one.
@@ -299,7 +305,7 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
       // Lane (n, h) holds tokens 8 i + 4 h + r (e = 4 i + r) of row `row` in this half.
       f32x4 tsv[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tsv[i] = *reinterpret_cast<const f32x4*>(&sm.ts[buf][2 * hf + (i >> 1)][8 * (i & 1) + 4 * ch]);
+      for (int i = 0; i < 4; ++i) tsv[i] = *reinterpret_cast<const f32x4*>(&sm.ts[buf][kHalf * hf + 8 * i + 4 * ch]);
       float sv[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -470,11 +476,11 @@ __device__ __forceinline__ void decode_piece8(Smem8& sm, const DecodeArgs& a, in
         else
           dma16_s(sc.rope_b, roff(j) * (kDR * 2) + uint32_t(16 * chunk), dst);
       } else {
-        const uint32_t dst = lds_addr(&sm.ts[sc.buf][q][0]);
+        const uint32_t dst = lds_addr(&sm.ts[sc.buf][16 * q]);
         if constexpr (PK == kPagedAny)
-          dma4(ts_g + crow(lane & 15) * 4, dst);
+          dma4_16(ts_g + crow(lane & 15) * 4, dst);
         else
-          dma4_s(sc.ts_b, roff(lane & 15) * 4, dst);
+          dma4_s_16(sc.ts_b, roff(lane & 15) * 4, dst);
       }
     };
     auto stage = [&](int n) {
