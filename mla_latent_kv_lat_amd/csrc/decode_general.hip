@@ -814,8 +814,9 @@ int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s) {
   const bool vec = a.dc % 8 == 0;
   if (p.balanced) {
     if (!a.part_bf16 || a.q_dt != MLA_BF16 || !vec) return int(hipErrorInvalidValue);
-    // Four waves per row when the ranges cut the average sequence into 8 or more pieces.
-    if (p.num_splits >= 8 * a.B)
+    // Four waves per row when the ranges cut the average sequence into 16 or more pieces (one
+    // wave loads up to 8 pieces in one batch).
+    if (p.num_splits >= 16 * a.B)
       hipLaunchKernelGGL(combine_ranges_kernel<kCombWaves>, dim3(p.rows, a.B), dim3(64 * kCombWaves), 0, s, a,
                          p.num_splits);
     else
