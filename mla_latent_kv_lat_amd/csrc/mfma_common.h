@@ -76,6 +76,20 @@ __device__ __forceinline__ bf16x8 lds_operand_tr(const uint16_t* tile, int k0, i
   return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
+// A 32 x 16 (m = 32 columns, k = 16 rows) bf16 A operand of v_mfma_f32_32x32x16_bf16, read
+// transposed from a staged tile (1 KB rows, swz32): rows k0 .. k0 + 15, columns c0 .. c0 + 31
+// (c0 a multiple of 32).  Lane l receives column c0 + l % 32 and rows k0 + 8h .. k0 + 8h + 7
+// (h = l / 32): 16-lane group G reads columns c0 + 16 (G & 1) + (0..15) of rows
+// k0 + 8 (G >> 1) + (0..7).
+__device__ __forceinline__ bf16x8 lds_operand_tr512(const uint16_t* tile, int k0, int c0, int lane) {
+  const int G = lane >> 4, r = (lane >> 2) & 3, q = lane & 3;
+  const int col = c0 + 16 * (G & 1) + 4 * q;
+  const int k_lo = k0 + 8 * (G >> 1) + r, k_hi = k_lo + 4;
+  const u32x2 lo = lds_read_tr4(tile + k_lo * 512 + 8 * ((col >> 3) ^ swz32(k_lo)) + (col & 7));
+  const u32x2 hi = lds_read_tr4(tile + k_hi * 512 + 8 * ((col >> 3) ^ swz32(k_hi)) + (col & 7));
+  return __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
 // Two e4m3fn codes (low or high half-word of `w`) -> two bf16, exactly.
 template <bool HI>
 __device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t w) {

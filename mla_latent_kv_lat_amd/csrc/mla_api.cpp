@@ -126,9 +126,10 @@ mla_status run_decode(const DecodeArgs& a, const DecodePlan& p, hipStream_t s, b
     if (err) return hip_status(err);
   }
   int err = p.kernel == DecodeKernel::kLatent ? launch_decode_latent(a, p, s)
-            : p.kernel == DecodeKernel::kMfma ? (a.fp8_scores ? launch_decode_fp8(a, p, s)
-                                                              : launch_decode_mfma(a, p, s))
-                                              : launch_decode_general(a, p, s);
+            : p.kernel == DecodeKernel::kPair   ? launch_decode_pair(a, p, s)
+            : p.kernel == DecodeKernel::kMfma   ? (a.fp8_scores ? launch_decode_fp8(a, p, s)
+                                                                : launch_decode_mfma(a, p, s))
+                                                : launch_decode_general(a, p, s);
   if (err) return hip_status(err);
   if (combine && (p.balanced || p.num_splits > 1)) return hip_status(launch_combine(a, p, s));
   return MLA_OK;
@@ -180,6 +181,13 @@ bool mfma_decode_eligible(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, in
          d->d_rope == 64 && (d->q_len * d->n_heads) % 64 == 0 && seq_bytes < (int64_t(1) << 31);
 }
 
+// The 64-row bf16 decode runs on the paired-score-wave kernel unless the environment
+// variable MLA_DECODE_PAIR is "0" (then on the kernel with loader, score and output roles).
+static bool pair_enabled() {
+  const char* env = std::getenv("MLA_DECODE_PAIR");
+  return !(env && env[0] == '0' && env[1] == 0);
+}
+
 mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32_t max_seq_len,
                        DecodePlan* plan) {
   mla_status st = check_dims(d);
@@ -203,6 +211,14 @@ mla_status plan_decode(const mla_dims* d, mla_dtype q_dt, mla_dtype kv_dt, int32
   if (want_latent && latent_decode_eligible(d, q_dt, kv_dt, max_seq_len)) {
     p.kernel = DecodeKernel::kLatent;
     p.row_block = 128;
+    p.max_prefix_here = 64;
+    tile = 64;
+    min_chunk = 512;
+  } else if (old_ok && kv_dt == MLA_BF16 && d->fp8_scores == 0 && pair_enabled()) {
+    // bf16 caches: the 64-row kernel with two score waves per row block (it computes the
+    // tile prefix itself for up to 64 sequences).
+    p.kernel = DecodeKernel::kPair;
+    p.row_block = 64;
     p.max_prefix_here = 64;
     tile = 64;
     min_chunk = 512;

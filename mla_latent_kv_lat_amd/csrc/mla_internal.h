@@ -16,6 +16,7 @@ enum class DecodeKernel : int {
   kGeneral = 0,  // VALU kernel for any supported shape (one workgroup per 4 query rows)
   kMfma = 1,     // matrix-core kernel (64 query rows per workgroup): fp8 caches
   kLatent = 2,   // matrix-core kernel (128 query rows per workgroup): bf16 caches
+  kPair = 3,     // matrix-core kernel (64 query rows, two score waves per row block): bf16 caches
 };
 
 // Split-K plan of one decode call.
@@ -130,6 +131,7 @@ int launch_decode_general(const DecodeArgs& a, const DecodePlan& p, hipStream_t 
 int launch_decode_mfma(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_decode_fp8(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_decode_latent(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
+int launch_decode_pair(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 int launch_combine(const DecodeArgs& a, const DecodePlan& p, hipStream_t s);
 // The balanced ranges' merge inside the output absorption (decode_general.hip).
 bool merge_absorb_fits(const DecodeArgs& a, const DecodePlan& p, int32_t d_h);

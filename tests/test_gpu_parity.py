@@ -35,19 +35,25 @@ def say(*a):
     print("[case]", *a, flush=True)
 
 
-# The bf16 decode has two matrix-core kernels (row blocks of 128 and of 64 query rows) and a
-# general one (any head count); the plan picks by sequence length, and the environment
-# variable MLA_DECODE_ROW_BLOCK forces one of the first two, so every small case below runs
-# on each of them.
-KERNELS = {"rows128": (128, "128"), "rows64": (128, "64"), "general": (8, None)}
+# The bf16 decode has three matrix-core kernels (row blocks of 128 query rows; of 64 rows
+# with two score waves per row block; of 64 rows with loader, score and output roles) and a
+# general one (any head count).  The plan picks by sequence length; the environment
+# variables MLA_DECODE_ROW_BLOCK (128 or 64) and MLA_DECODE_PAIR ("0": the role kernel for
+# 64-row blocks) force one of the first three, so every small case below runs on each.
+KERNELS = {"rows128": (128, "128", None), "pair": (128, "64", None), "rows64": (128, "64", "0"),
+           "general": (8, None, None)}
 
 
 def use_kernel(kern, monkeypatch):
-    n_heads, env = KERNELS[kern]
+    n_heads, env, pair = KERNELS[kern]
     if env is None:
         monkeypatch.delenv("MLA_DECODE_ROW_BLOCK", raising=False)
     else:
         monkeypatch.setenv("MLA_DECODE_ROW_BLOCK", env)
+    if pair is None:
+        monkeypatch.delenv("MLA_DECODE_PAIR", raising=False)
+    else:
+        monkeypatch.setenv("MLA_DECODE_PAIR", pair)
     return n_heads
 
 
@@ -191,7 +197,7 @@ def test_decode_stage_bf16_ragged(split_tokens, kern, monkeypatch):
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+@pytest.mark.parametrize("kern", ["rows128", "pair", "rows64"])
 def test_decode_stage_peaked_scores(kern, monkeypatch):
     use_kernel(kern, monkeypatch)
     cfg = configs.V2_DECODE.with_(batch=2, seq_len=700, cfg_id=23)
@@ -272,7 +278,7 @@ def test_causal_equals_independent_single_query_decodes():
 
 # -------------------------------------------------------------- paged cache ----
 
-@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+@pytest.mark.parametrize("kern", ["rows128", "pair", "rows64"])
 def test_paged_equals_contiguous_bitwise(kern, monkeypatch):
     use_kernel(kern, monkeypatch)
     cfg = configs.PAGED_VARLEN.with_(batch=6, seq_len=1500, len_min=1, cfg_id=26)
@@ -304,7 +310,7 @@ PAGED_LAYOUT_CASES = [(kv, bs, 0) for kv in ("bf16", "fp8") for bs in (64, 48, 1
 
 @pytest.mark.parametrize("kv,block_size,fp8_scores", PAGED_LAYOUT_CASES,
                          ids=[f"{k}-{b}" + ("-fp8s" if f else "") for k, b, f in PAGED_LAYOUT_CASES])
-@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+@pytest.mark.parametrize("kern", ["rows128", "pair", "rows64"])
 def test_paged_layouts_equal_contiguous_bitwise(kv, block_size, fp8_scores, kern, monkeypatch):
     if kv != "bf16" and kern == "rows128":
         pytest.skip("the 128-row kernel reads bf16 caches only")
@@ -337,8 +343,9 @@ SAMPLE = {configs.V2_DECODE.name: [0, 17, 31], configs.PAGED_VARLEN.name: [0, 33
 
 
 # Each workload at full size with the plan's own kernel choice, plus the bf16 decode and the
-# paged workload forced onto the other matrix-core kernel.
-FULL_CASES = [(c, None) for c in FULL] + [(configs.V2_DECODE, "rows128"), (configs.PAGED_VARLEN, "rows64")]
+# paged workload forced onto the other matrix-core kernels.
+FULL_CASES = [(c, None) for c in FULL] + [(configs.V2_DECODE, "rows128"), (configs.V2_DECODE, "rows64"),
+                                          (configs.PAGED_VARLEN, "pair"), (configs.PAGED_VARLEN, "rows64")]
 
 
 @pytest.mark.parametrize("cfg,kern", FULL_CASES, ids=[c.name + (f"-{k}" if k else "") for c, k in FULL_CASES])
@@ -398,7 +405,7 @@ def decoded_batches(inp, batches):
     return decoded(sub)
 
 
-@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+@pytest.mark.parametrize("kern", ["rows128", "pair", "rows64"])
 def test_run_to_run_bitwise_deterministic(kern, monkeypatch):
     use_kernel(kern, monkeypatch)
     cfg = configs.V2_DECODE.with_(batch=4, seq_len=2048, cfg_id=27)
@@ -457,7 +464,7 @@ BALANCED_CASES = {
 }
 
 
-@pytest.mark.parametrize("kern", ["rows128", "rows64"])
+@pytest.mark.parametrize("kern", ["rows128", "pair", "rows64"])
 @pytest.mark.parametrize("case", list(BALANCED_CASES))
 def test_decode_balanced_ranges(case, kern, monkeypatch):
     use_kernel(kern, monkeypatch)
