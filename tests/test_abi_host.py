@@ -406,6 +406,22 @@ def test_noalloc_scratch_holds_every_full_size_plan(rows, monkeypatch):
         assert 0 < ws <= L.NOALLOC_SCRATCH_BYTES, (cfg.name, rows, ws)
 
 
+@pytest.mark.parametrize("pair", ["0", "1"])
+def test_bf16_64_row_kernels_share_the_plan(pair, monkeypatch):
+    """Both bf16 kernels with 64-row blocks (paired score waves, or loader/score/output
+    roles: MLA_DECODE_PAIR=0) take the same balanced ranges and the same workspace, so the
+    combine and the fused output absorption read their partials alike."""
+    monkeypatch.setenv("MLA_DECODE_ROW_BLOCK", "64")
+    monkeypatch.setenv("MLA_DECODE_PAIR", pair)
+    d = L.dims_from_config(configs.V2_DECODE)
+    plan = L.mla_decode_plan(d, "bf16", configs.V2_DECODE.seq_len)
+    ws = L.mla_decode_workspace_bytes(d, "bf16", configs.V2_DECODE.seq_len)
+    monkeypatch.delenv("MLA_DECODE_PAIR")
+    assert plan == L.mla_decode_plan(d, "bf16", configs.V2_DECODE.seq_len)
+    assert ws == L.mla_decode_workspace_bytes(d, "bf16", configs.V2_DECODE.seq_len)
+    assert plan[0] == 256 // 2  # ranges: compute units / row blocks of the 128 heads
+
+
 def test_fold_output_weights_validates_before_any_hip_call():
     """mla_fold_output_weights rejects unsupported shapes and dtypes, null and misaligned
     pointers without touching the device."""
