@@ -181,8 +181,11 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, mla_dtype kv_dt, int32_t
  * block and 0 tokens.  A bf16 cache takes row blocks of 128 query rows when max_seq_len is
  * at least 8192 (or when the rows are a multiple of 32 but not of 64), else of 64; the
  * environment variable MLA_DECODE_ROW_BLOCK=64 or =128, read on every plan, overrides the
- * length rule where that kernel applies.  An fp8 cache takes 64.  The device's compute
- * unit count (256 when no device is present) sets the ranges.  No kernel launch. */
+ * length rule where that kernel applies.  bf16 row blocks of 64 run on the kernel with two
+ * score waves per row block, or, with the environment variable MLA_DECODE_PAIR=0, on the
+ * kernel with loader, score and output waves; both take the same plan.  An fp8 cache
+ * takes 64.  The device's compute unit count (256 when no device is present) sets the
+ * ranges.  No kernel launch. */
 mla_status mla_decode_plan(const mla_dims* dims, mla_dtype kv_dt, int32_t max_seq_len,
                            int32_t* num_splits, int32_t* split_tokens);
 
