@@ -239,6 +239,24 @@ def test_decode_rising_scores(gain, split_tokens, kern, monkeypatch):
     assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
 
 
+@pytest.mark.parametrize("kern", list(KERNELS))
+@pytest.mark.parametrize("split_tokens", [0, 128])
+def test_decode_stage_bf16_causal(split_tokens, kern, monkeypatch):
+    """Four query tokens per sequence, causal among them, on a bf16 cache, on every bf16
+    kernel: query i of a sequence of L rows sees rows t <= L - 4 + i.  A sequence of 3 rows
+    leaves its query 0 with no visible key: o_lat 0 and lse -inf."""
+    n_heads = use_kernel(kern, monkeypatch)
+    cfg = configs.V2_DECODE.with_(batch=3, q_len=4, seq_len=700, cfg_id=36, n_heads=n_heads)
+    say("decode bf16 causal", split_tokens, cfg)
+    o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [700, 130, 3], split_tokens)
+    e_o, e_l = max_rel_err(o, o_ref), max_abs_err(l, l_ref)
+    print(f"  o_lat {e_o:.2e} lse {e_l:.2e}")
+    assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
+    none = ~np.isfinite(l_ref)
+    assert none.sum() == n_heads  # query 0 of the 3-row sequence, every head
+    assert np.all(l[none] == -np.inf) and np.all(o[none] == 0)
+
+
 @pytest.mark.parametrize("n_heads", [128, 8], ids=["mfma", "general"])
 @pytest.mark.parametrize("split_tokens", [0, 128])
 def test_decode_stage_fp8_causal(split_tokens, n_heads):
