@@ -257,6 +257,19 @@ def test_decode_stage_bf16_causal(split_tokens, kern, monkeypatch):
     assert np.all(l[none] == -np.inf) and np.all(o[none] == 0)
 
 
+@pytest.mark.parametrize("kern", ["rows128", "pair", "rows64"])
+def test_decode_stage_bf16_odd_row_blocks(kern, monkeypatch):
+    """64 heads and 3 query tokens: 192 query rows per sequence, three 64-row blocks (the
+    128-row kernel's second block half empty), causal, ragged lengths."""
+    use_kernel(kern, monkeypatch)
+    cfg = configs.V2_DECODE.with_(batch=3, q_len=3, n_heads=64, seq_len=900, cfg_id=37)
+    say("decode bf16 192 rows", cfg)
+    o, l, o_ref, l_ref, *_ = decode_stage_case(cfg, 0, [900, 250, 33], 0)
+    e_o, e_l = max_rel_err(o, o_ref), max_abs_err(l, l_ref)
+    print(f"  o_lat {e_o:.2e} lse {e_l:.2e}")
+    assert e_o <= TOL["bf16"] and e_l <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("n_heads", [128, 8], ids=["mfma", "general"])
 @pytest.mark.parametrize("split_tokens", [0, 128])
 def test_decode_stage_fp8_causal(split_tokens, n_heads):
