@@ -138,17 +138,21 @@ __device__ __forceinline__ void pair_piece(SmemPair& sm, const DecodeArgs& a, in
   auto issue = [&](int k) {
     const TileRows r = tile_rows(k);
     const int slot = k % kSlots;
+    // The swizzled chunk offsets are formed from an opaque copy of the lane index at every
+    // issue: otherwise the compiler keeps all of them live across the products and spills.
+    int ln;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(ln) : "v"(lane));
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const int trow = 8 * q + j;
       const uint32_t dst = lat0 + uint32_t((slot * kTile + trow) * (kDC * 2));
-      const uint32_t chunk = uint32_t(16 * (lane ^ swz32(trow)));
+      const uint32_t chunk = uint32_t(16 * (ln ^ swz32(trow)));
       if constexpr (PK == kContig)  // one base per sequence; 32-bit offsets (a sequence spans < 2 GiB)
         dma16_s(lat_base + seq_row0 * (kDC * 2), uint32_t(r.row[j] * (kDC * 2)) + chunk, dst);
       else
         dma16_s(lat_base + r.row[j] * (kDC * 2), chunk, dst);
     }
-    const uint32_t rchunk = uint32_t(16 * ((lane & 7) ^ rope_swz(8 * q + (lane >> 3))));
+    const uint32_t rchunk = uint32_t(16 * ((ln & 7) ^ rope_swz(8 * q + (ln >> 3))));
     const uint32_t rdst = rope0 + uint32_t((slot * kTile + 8 * q) * (kDR * 2));
     if constexpr (PK == kContig)
       dma16_s(rope_base + seq_row0 * (kDR * 2), uint32_t(r.rope * (kDR * 2)) + rchunk, rdst);
