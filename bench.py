@@ -92,12 +92,14 @@ def metric_name(cfg) -> str:
 
 def decode_roofline(cfg, wc, call_ms: float) -> dict:
     """The decode call against HBM for the streaming workloads, against the bf16 matrix peak
-    where the arithmetic intensity is past the ridge (speculative multi-token fp8)."""
+    where the arithmetic intensity is past the ridge (speculative multi-token fp8).  `traffic`
+    is the call's measured HBM bytes either way."""
     mfma_bound = wc["attn_flops"] / wc["decode_bytes"] > BF16_MFMA_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)
     if mfma_bound:
         achieved = wc["attn_flops"] / (call_ms * 1e-3) / 1e12
         return {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_MFMA_PEAK_TFS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFS, 4),
+                "traffic": measured_traffic(cfg.name)}
     achieved = wc["decode_bytes"] / (call_ms * 1e-3) / 1e9
     return {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(cfg.name)}
@@ -161,6 +163,7 @@ def side_workload(cfg, calls: int, warmup: int) -> dict:
         avg8 = float(np.mean(ms8))
         tf8 = wc["attn_flops"] / (avg8 * 1e-3) / 1e12
         roof8 = decode_roofline(cfg, wc, avg8)
+        roof8["traffic"] = measured_traffic(cfg.name + "_fp8products")
         roof8["fp8_peak_frac"] = round(tf8 / FP8_MFMA_PEAK_TFS, 4)
         out["fp8_products"] = {
             "note": "dims.fp8_scores = 2: query and probabilities rounded to e4m3, both products on the fp8 "
